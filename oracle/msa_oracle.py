@@ -1,0 +1,268 @@
+"""Plain fp64 CPU oracle for the forward path of MiniMax Sparse Attention (MSA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and its
+Python binding) imports, calls or links this module; only the tests, the smoke
+check and the CPU-baseline leg of the benchmark do.  It shares no code, table or
+helper with the GPU path.
+
+What the pages say the method computes, and where (pages are cited by site and
+section; they carry no equation numbers):
+
+* GQA base: query heads are split into consecutive groups, each group sharing one
+  K/V head (Notion notes "Minimax-sparse-Attention", section "what is MHA, MQA,
+  GQA?"; yhxrc.cn article, section "第二步：稀疏分支", where heads Q1-Q3 use I1 and
+  Q4-Q6 use I2).  Head h belongs to group h // (Hq / Hkv).
+* Index branch (yhxrc.cn article, section "第一步：索引分支"): one index query per
+  GQA group and token, one index key per token shared by all heads; the token
+  score is the plain dot product q_idx . k_idx over every causal token; the token
+  scores are max-pooled per KV block; a top-k keeps the best blocks.
+* The selection is per query and per GQA group, independently (hamidun.com news,
+  "Como o MSA funciona"; lumi-systems news summary).
+* The top-k is exponential-free (lumi-systems news summary): selection works on
+  the raw pooled scores, no softmax.
+* k = 16 blocks of 128 tokens per query, a fixed 2,048-token budget, and the
+  query's own (local) block is always part of the selection (lefilia.fr article).
+* Main branch: exact softmax attention on the real, uncompressed K/V of only the
+  selected blocks (hamidun.com "Como o MSA funciona"; yhxrc.cn "第二步：稀疏分支";
+  lefilia.fr article).
+
+Readings where the pages are silent (each also listed in the design notes):
+  r1  index score has no scale, activation or per-head weight;
+  r2  k counts the local block: local + (k-1) best earlier blocks;
+  r3  ties in the pooled score go to the lower block index;
+  r4  when the query has at most k causal blocks, all of them are selected and
+      the row is padded with -1;
+  r5  selected block indices are written in ascending order;
+  r6  causality is per token, s <= p, in both branches;
+  r7  softmax scale 1/sqrt(d) unless the caller gives one;
+  r8  a decode query sits at p = n_kv - 1 (its own K/V are already cached);
+  r9  block j covers tokens [j*B, min((j+1)*B, n_kv)).
+
+Array conventions (all numpy, float64 inside):
+  q_idx [batch][n_q][Hkv][d_idx]     k_idx [batch][n_kv][d_idx]
+  q     [batch][n_q][Hq][d]          k, v  [batch][n_kv][Hkv][d]
+  query i of a call sits at absolute position p = pos0 + i.
+
+Every function is pinned by tests/test_oracle_*.py against brute force, closed
+forms, invariants and a textbook attention routine.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+# ----------------------------------------------------------------------------
+# Index branch, one (query, group) row at a time
+# ----------------------------------------------------------------------------
+
+def token_scores(q_idx_row: np.ndarray, k_idx_seq: np.ndarray, p: int) -> np.ndarray:
+    """Index score of one query against every causal token s <= p.
+
+    yhxrc.cn article, "第一步：索引分支": the score is the dot product of the
+    group's index query with the index key shared by all heads (reading r1: no
+    scale).  Returns float64 [p + 1].
+    """
+    q = np.asarray(q_idx_row, dtype=np.float64)
+    keys = np.asarray(k_idx_seq[: p + 1], dtype=np.float64)
+    return keys @ q
+
+
+def block_max_pool(scores: np.ndarray, p: int, block: int) -> np.ndarray:
+    """Max-pool token scores per KV block over the causal tokens.
+
+    yhxrc.cn article, "第一步：索引分支" (block max-pooling turns token scores into
+    block scores).  Block j covers tokens [j*block, (j+1)*block) clipped to
+    s <= p (reading r6).  Returns float64 [p // block + 1]; the last entry is the
+    query's own block, pooled over its causal part only.
+    """
+    jl = p // block
+    pooled = np.empty(jl + 1, dtype=np.float64)
+    for j in range(jl + 1):
+        lo = j * block
+        hi = min((j + 1) * block, p + 1)
+        pooled[j] = np.max(scores[lo:hi])
+    return pooled
+
+
+def select_blocks(pooled: np.ndarray, jl: int, topk: int) -> np.ndarray:
+    """Exponential-free top-k over the pooled block scores, local block forced.
+
+    lumi-systems summary (exponential-free top-k), lefilia.fr article (k blocks,
+    local block always included), yhxrc.cn "第一步" (TopK decides which blocks are
+    kept).  Readings r2-r5: the local block jl plus the (topk - 1) best earlier
+    blocks j < jl, best meaning larger pooled score, ties to the lower index;
+    ascending order; -1 padding when fewer than topk blocks exist.
+
+    The top-(topk-1) is taken by repeated first-occurrence argmax, the plainest
+    exact statement of "largest score, lower index on ties".
+    """
+    out = np.full(topk, -1, dtype=np.int64)
+    if jl + 1 <= topk:
+        out[: jl + 1] = np.arange(jl + 1)
+        return out
+    cand = np.array(pooled[:jl], dtype=np.float64)
+    chosen = []
+    for _ in range(topk - 1):
+        j = int(np.argmax(cand))          # first maximal index: ties -> lower j
+        chosen.append(j)
+        cand[j] = NEG_INF                 # pooled scores are finite, so a chosen
+                                          # block never wins a later round
+    chosen.append(jl)
+    out[:] = np.sort(np.array(chosen, dtype=np.int64))
+    return out
+
+
+def index_topk_row(q_idx_row: np.ndarray, k_idx_seq: np.ndarray, p: int,
+                   block: int, topk: int):
+    """Whole index branch for one (query, group): scores -> pool -> select.
+
+    Returns (pooled [jl + 1] float64, selection [topk] int64).
+    """
+    sc = token_scores(q_idx_row, k_idx_seq, p)
+    pooled = block_max_pool(sc, p, block)
+    sel = select_blocks(pooled, p // block, topk)
+    return pooled, sel
+
+
+# ----------------------------------------------------------------------------
+# Main branch, one (query, group) row at a time
+# ----------------------------------------------------------------------------
+
+def visible_positions(sel: np.ndarray, p: int, block: int, n_kv: int) -> np.ndarray:
+    """Token positions the main branch attends to for one (query, group).
+
+    Every token of every selected block, clipped to s <= p (reading r6) and to
+    the cache length (reading r9).  Sorted ascending.
+    """
+    pos = []
+    for j in sel:
+        if j < 0:
+            continue
+        lo = int(j) * block
+        hi = min((int(j) + 1) * block, p + 1, n_kv)
+        pos.extend(range(lo, hi))
+    return np.array(sorted(pos), dtype=np.int64)
+
+
+def softmax_attention(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray,
+                      scale: float):
+    """Exact softmax attention of several query heads over the given K/V rows.
+
+    hamidun.com "Como o MSA funciona" and yhxrc.cn "第二步：稀疏分支": the attention
+    formula runs unchanged, on real K/V.  q_heads [G][d], keys/values [n][d].
+    Returns (out [G][d], lse [G]) in float64, where lse is the natural log of the
+    softmax normaliser of the scaled logits.
+    """
+    q = np.asarray(q_heads, dtype=np.float64)
+    kk = np.asarray(keys, dtype=np.float64)
+    vv = np.asarray(values, dtype=np.float64)
+    z = scale * (q @ kk.T)                     # [G][n]
+    m = np.max(z, axis=1, keepdims=True)
+    e = np.exp(z - m)
+    s = np.sum(e, axis=1, keepdims=True)
+    out = (e @ vv) / s
+    lse = (m + np.log(s))[:, 0]
+    return out, lse
+
+
+def default_scale(d: int) -> float:
+    """Reading r7: the usual 1/sqrt(d) softmax scale."""
+    return 1.0 / math.sqrt(d)
+
+
+# ----------------------------------------------------------------------------
+# Whole-tensor drivers (loops over rows; for small and medium shapes)
+# ----------------------------------------------------------------------------
+
+def msa_index_topk(q_idx: np.ndarray, k_idx: np.ndarray, pos0: int, block: int,
+                   topk: int):
+    """Index branch for every (batch, query, group).
+
+    Returns (bscore [b][n_q][Hkv][nblk] float64 with -inf where j > p // block,
+             blk_idx [b][n_q][Hkv][topk] int64).
+    """
+    b, n_q, h_kv, _ = q_idx.shape
+    n_kv = k_idx.shape[1]
+    nblk = -(-n_kv // block)
+    bscore = np.full((b, n_q, h_kv, nblk), NEG_INF, dtype=np.float64)
+    blk = np.full((b, n_q, h_kv, topk), -1, dtype=np.int64)
+    for bi in range(b):
+        kseq = np.asarray(k_idx[bi], dtype=np.float64)
+        for i in range(n_q):
+            p = pos0 + i
+            for g in range(h_kv):
+                pooled, sel = index_topk_row(q_idx[bi, i, g], kseq, p, block, topk)
+                bscore[bi, i, g, : pooled.shape[0]] = pooled
+                blk[bi, i, g] = sel
+    return bscore, blk
+
+
+def msa_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                         blk_idx: np.ndarray, pos0: int, block: int,
+                         scale: float | None = None):
+    """Main branch: every head of group g attends to the group's selected blocks.
+
+    yhxrc.cn "第二步：稀疏分支" (all heads of a group share one selection) and
+    lefilia.fr (exact softmax only on the selected blocks).
+    Returns (out [b][n_q][Hq][d], lse [b][n_q][Hq]) in float64.
+    """
+    b, n_q, h_q, d = q.shape
+    n_kv, h_kv = k.shape[1], k.shape[2]
+    group = h_q // h_kv
+    if scale is None:
+        scale = default_scale(d)
+    out = np.zeros((b, n_q, h_q, d), dtype=np.float64)
+    lse = np.zeros((b, n_q, h_q), dtype=np.float64)
+    for bi in range(b):
+        for i in range(n_q):
+            p = pos0 + i
+            for g in range(h_kv):
+                pos = visible_positions(blk_idx[bi, i, g], p, block, n_kv)
+                hs = slice(g * group, (g + 1) * group)
+                o, l = softmax_attention(q[bi, i, hs], k[bi, pos, g], v[bi, pos, g], scale)
+                out[bi, i, hs] = o
+                lse[bi, i, hs] = l
+    return out, lse
+
+
+def dense_gqa(q: np.ndarray, k: np.ndarray, v: np.ndarray, pos0: int,
+              scale: float | None = None):
+    """Dense causal GQA, the comparator: every head attends to all s <= p.
+
+    Notion notes, "what is MHA, MQA, GQA?" (grouped K/V heads) and hamidun.com
+    "Como o MSA funciona" (the all-to-all baseline MSA is measured against).
+    Written separately from msa_sparse_attention on purpose.
+    """
+    b, n_q, h_q, d = q.shape
+    h_kv = k.shape[2]
+    group = h_q // h_kv
+    if scale is None:
+        scale = default_scale(d)
+    out = np.zeros((b, n_q, h_q, d), dtype=np.float64)
+    lse = np.zeros((b, n_q, h_q), dtype=np.float64)
+    for bi in range(b):
+        for i in range(n_q):
+            p = pos0 + i
+            for h in range(h_q):
+                g = h // group
+                o, l = softmax_attention(q[bi, i, h][None, :], k[bi, : p + 1, g],
+                                         v[bi, : p + 1, g], scale)
+                out[bi, i, h] = o[0]
+                lse[bi, i, h] = l[0]
+    return out, lse
+
+
+def msa_forward(q_idx, k_idx, q, k, v, pos0: int, block: int, topk: int,
+                scale: float | None = None):
+    """Index branch then main branch, in the pages' order.
+
+    Returns (out, lse, blk_idx, bscore).
+    """
+    bscore, blk = msa_index_topk(q_idx, k_idx, pos0, block, topk)
+    out, lse = msa_sparse_attention(q, k, v, blk, pos0, block, scale)
+    return out, lse, blk, bscore

@@ -1,0 +1,126 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each test swaps one oracle function for a plausible wrong version (a flipped
+tie-break, a dropped term, an off-by-one mask, a wrong head->group map, a
+missing scale) on the CPU and checks that at least one of the pins in
+test_oracle_index.py / test_oracle_attention.py fails.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import msa_oracle as O
+from tests import test_oracle_attention as TA
+from tests import test_oracle_index as TI
+
+
+def fails(fn, *a):
+    try:
+        fn(*a)
+    except AssertionError:
+        return True
+    return False
+
+
+def mut_select_high_tie(pooled, jl, topk):
+    out = np.full(topk, -1, dtype=np.int64)
+    if jl + 1 <= topk:
+        out[: jl + 1] = np.arange(jl + 1)
+        return out
+    cand = np.array(pooled[:jl])
+    order = np.lexsort((-np.arange(jl), -cand))     # ties -> HIGHER index
+    out[:] = np.sort(list(order[: topk - 1]) + [jl])
+    return out
+
+
+def mut_select_no_local(pooled, jl, topk):
+    out = np.full(topk, -1, dtype=np.int64)
+    n = min(topk, jl + 1)
+    order = np.lexsort((np.arange(jl + 1), -np.asarray(pooled[: jl + 1])))
+    out[:n] = np.sort(order[:n])
+    return out
+
+
+def mut_pool_excludes_p(scores, p, block):
+    jl = p // block
+    pooled = np.empty(jl + 1)
+    for j in range(jl + 1):
+        lo, hi = j * block, min((j + 1) * block, p + 1)
+        seg = scores[lo:hi - 1] if hi - 1 > lo else scores[lo:hi]
+        pooled[j] = np.max(seg)
+    return pooled
+
+
+def mut_scores_drop_term(q, k_idx, p):
+    return np.asarray(k_idx[: p + 1, :-1], dtype=np.float64) @ np.asarray(q[:-1], dtype=np.float64)
+
+
+def mut_visible_leaks_future(sel, p, block, n_kv):
+    pos = []
+    for j in sel:
+        if j >= 0:
+            pos.extend(range(j * block, min((j + 1) * block, p + 2, n_kv)))
+    return np.array(sorted(pos), dtype=np.int64)
+
+
+def mut_dense_wrong_group(q, k, v, pos0, scale=None):
+    b, n_q, h_q, d = q.shape
+    h_kv = k.shape[2]
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    out = np.zeros((b, n_q, h_q, d))
+    lse = np.zeros((b, n_q, h_q))
+    for bi in range(b):
+        for i in range(n_q):
+            p = pos0 + i
+            for h in range(h_q):
+                g = h % h_kv                                # interleaved, wrong
+                o, l = O.softmax_attention(q[bi, i, h][None], k[bi, : p + 1, g], v[bi, : p + 1, g], scale)
+                out[bi, i, h], lse[bi, i, h] = o[0], l[0]
+    return out, lse
+
+
+def mut_attention_no_scale(q_heads, keys, values, scale):
+    return ORIG_SOFTMAX(q_heads, keys, values, 1.0)
+
+
+ORIG_SOFTMAX = O.softmax_attention
+
+
+def test_flipped_tie_break_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "select_blocks", mut_select_high_tie)
+    assert fails(TI.test_selection_all_ties_takes_lowest_indices)
+    assert fails(TI.test_selection_matches_full_sort_with_heavy_ties, 16)
+
+
+def test_missing_local_block_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "select_blocks", mut_select_no_local)
+    assert fails(TI.test_selection_structure_invariants)
+
+
+def test_pool_off_by_one_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "block_max_pool", mut_pool_excludes_p)
+    assert fails(TI.test_block_max_pool_matches_loop_brute_force)
+
+
+def test_dropped_score_term_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "token_scores", mut_scores_drop_term)
+    assert fails(TI.test_token_scores_match_integer_brute_force)
+
+
+def test_future_leak_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "visible_positions", mut_visible_leaks_future)
+    assert fails(TA.test_no_future_token_changes_anything) or \
+        fails(TA.test_sparse_matches_torch_sdpa_on_selection_mask, 4, 1)
+    assert fails(TA.test_block_probe_shows_exactly_the_selected_blocks)
+
+
+def test_wrong_head_group_map_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "dense_gqa", mut_dense_wrong_group)
+    assert fails(TA.test_dense_matches_torch_sdpa, 8, 2)
+
+
+def test_missing_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "softmax_attention", mut_attention_no_scale)
+    assert fails(TA.test_dense_matches_torch_sdpa, 4, 1)

@@ -1,0 +1,188 @@
+// C ABI of the MSA forward path: argument validation on the host, workspace
+// sizing, and the kernel launch sequence of each entry point.  Declared and
+// documented in include/msa.h.
+#include "msa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "launch.h"
+
+namespace {
+
+using msa::Dims;
+
+enum : unsigned {
+  kNeedD = 1u,      // attention head dimension is used
+  kNeedDIdx = 2u,   // index dimension is used
+  kDecode = 4u,     // n_q must be 1
+  kCsr = 8u,        // per-(b, g, block) lists must fit int32
+};
+
+constexpr int64_t kMaxKv = 1 << 20;
+
+msa_status check_dims(const msa_dims* p, unsigned need) {
+  if (!p) return MSA_ERR_NULL;
+  const msa_dims& d = *p;
+  if (d.batch < 0 || d.n_q < 0 || d.n_kv < 1 || d.pos0 < 0 || d.h_q < 1 || d.h_kv < 1 || d.block < 1 ||
+      d.topk < 1 || d.d < 1 || d.d_idx < 1)
+    return MSA_ERR_SHAPE;
+  if (d.h_q % d.h_kv != 0) return MSA_ERR_SHAPE;
+  if ((int64_t)d.pos0 + d.n_q > d.n_kv) return MSA_ERR_SHAPE;
+  if ((need & kDecode) && d.n_q != 1) return MSA_ERR_SHAPE;
+  if (d.block != 128 || d.topk > 32) return MSA_ERR_UNSUPPORTED;
+  const int g = d.h_q / d.h_kv;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return MSA_ERR_UNSUPPORTED;
+  if ((need & kNeedD) && d.d != 64 && d.d != 128) return MSA_ERR_UNSUPPORTED;
+  if ((need & kNeedDIdx) && d.d_idx != 64 && d.d_idx != 128) return MSA_ERR_UNSUPPORTED;
+  if (d.n_kv > kMaxKv) return MSA_ERR_UNSUPPORTED;
+  if (d.batch > 65535) return MSA_ERR_UNSUPPORTED;
+  if ((int64_t)d.batch * d.n_q * d.h_kv * d.topk >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
+  if ((int64_t)d.n_q * d.h_kv > (int64_t(1) << 25)) return MSA_ERR_UNSUPPORTED;
+  const int64_t nblk = (d.n_kv + d.block - 1) / d.block;
+  if ((need & kCsr) && (int64_t)d.batch * d.h_kv * nblk >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+Dims to_dims(const msa_dims& d) {
+  return Dims{d.batch, d.n_q, d.n_kv, d.pos0, d.h_q, d.h_kv, d.d, d.d_idx, d.block, d.topk};
+}
+
+bool empty(const msa_dims& d) { return d.batch == 0 || d.n_q == 0; }
+
+size_t index_ws_bytes(const Dims& d) {
+  return msa::align_up((size_t)d.batch * d.n_q * d.h_kv * d.nblk() * sizeof(float), 256);
+}
+
+unsigned op_needs(msa_op op) {
+  switch (op) {
+    case MSA_OP_INDEX_TOPK: return kNeedDIdx;
+    case MSA_OP_BLOCK_TOPK: return 0u;
+    case MSA_OP_SPARSE_PREFILL: return kNeedD | kCsr;
+    case MSA_OP_SPARSE_DECODE: return kNeedD | kDecode;
+    case MSA_OP_DENSE_GQA: return kNeedD;
+  }
+  return 0u;
+}
+
+msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
+
+}  // namespace
+
+extern "C" {
+
+size_t msa_workspace_size(msa_op op, const msa_dims* dims) {
+  if (op < MSA_OP_INDEX_TOPK || op > MSA_OP_BLOCK_TOPK) return 0;
+  if (check_dims(dims, op_needs(op)) != MSA_OK) return 0;
+  const Dims d = to_dims(*dims);
+  switch (op) {
+    case MSA_OP_INDEX_TOPK: return index_ws_bytes(d);
+    case MSA_OP_BLOCK_TOPK: return 0;
+    case MSA_OP_SPARSE_PREFILL: return msa::prefill_ws_layout(d).total;
+    case MSA_OP_SPARSE_DECODE: return msa::sparse_decode_ws_layout(d).total;
+    case MSA_OP_DENSE_GQA: return d.n_q == 1 ? msa::dense_decode_ws_layout(d).total : 0;
+  }
+  return 0;
+}
+
+const char* msa_status_str(msa_status s) {
+  switch (s) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_NULL: return "MSA_ERR_NULL: a required pointer is NULL";
+    case MSA_ERR_SHAPE: return "MSA_ERR_SHAPE: inconsistent sizes";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: sizes outside what this build implements";
+    case MSA_ERR_ALIGN: return "MSA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE: workspace missing or too small";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP: a kernel launch failed";
+  }
+  return "unknown msa_status";
+}
+
+msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx, int32_t* blk_idx,
+                          void* workspace, size_t workspace_bytes, msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_INDEX_TOPK));
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  if (!q_idx || !k_idx || !blk_idx) return MSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(k_idx) || misaligned(blk_idx)) return MSA_ERR_ALIGN;
+  const Dims d = to_dims(*dims);
+  if (!workspace || workspace_bytes < index_ws_bytes(d)) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* bscore = static_cast<float*>(workspace);
+  st = hip_status(msa::launch_index_scores(d, q_idx, k_idx, bscore, s));
+  if (st != MSA_OK) return st;
+  return hip_status(msa::launch_block_topk(d, bscore, blk_idx, s));
+}
+
+msa_status msa_block_topk(const msa_dims* dims, const float* bscore, int32_t* blk_idx, msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_BLOCK_TOPK));
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  if (!bscore || !blk_idx) return MSA_ERR_NULL;
+  if (misaligned(bscore) || misaligned(blk_idx)) return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_block_topk(to_dims(*dims), bscore, blk_idx, static_cast<hipStream_t>(stream)));
+}
+
+msa_status msa_sparse_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
+                              size_t workspace_bytes, msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_PREFILL));
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  if (!q || !k || !v || !blk_idx || !out) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(blk_idx) || misaligned(out) ||
+      (lse && misaligned(lse)))
+    return MSA_ERR_ALIGN;
+  const Dims d = to_dims(*dims);
+  const size_t need = msa::prefill_ws_layout(d).total;
+  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_sparse_prefill(d, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
+                             size_t workspace_bytes, msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_DECODE));
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  if (!q || !k || !v || !blk_idx || !out) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(blk_idx) || misaligned(out) ||
+      (lse && misaligned(lse)))
+    return MSA_ERR_ALIGN;
+  const Dims d = to_dims(*dims);
+  const size_t need = msa::sparse_decode_ws_layout(d).total;
+  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_sparse_decode(d, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+msa_status msa_dense_gqa(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v, float scale,
+                         uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_DENSE_GQA));
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  if (!q || !k || !v || !out) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || (lse && misaligned(lse)))
+    return MSA_ERR_ALIGN;
+  const Dims d = to_dims(*dims);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float sc = resolve_scale(scale, d.d);
+  if (d.n_q == 1) {
+    const size_t need = msa::dense_decode_ws_layout(d).total;
+    if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return MSA_ERR_ALIGN;
+    return hip_status(msa::launch_dense_decode(d, q, k, v, sc, out, lse, workspace, s));
+  }
+  return hip_status(msa::launch_dense_prefill(d, q, k, v, sc, out, lse, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+// Index branch, step 3: exponential-free top-k over the pooled block scores with
+// the query's own block always kept (lumi-systems summary: exponential-free
+// top-k; lefilia.fr article: k blocks per query, local block always included).
+//
+// Per (query, group) row with local block jl = (pos0 + t) / 128:
+//   * jl + 1 <= k: all blocks 0..jl, then -1 padding;
+//   * otherwise jl plus the k-1 best blocks among 0..jl-1, best meaning larger
+//     pooled score, ties to the lower block index; written in ascending order.
+//
+// One wave per row; the row's scores live in registers (element e = 64*i + lane
+// sits in slot i of lane `lane`, so slot-major / lane-minor order is block
+// order).  Scores are mapped to order-preserving unsigned keys.  No exponential,
+// no sort:
+//   1. T0 = (k-1)-th largest of the 64 per-lane maxima.  At least k-1 elements
+//      are >= T0, so the true threshold T is >= T0 and every selected block has
+//      key >= T0.
+//   2. If fewer than k-1 keys are > T0, then T = T0: keep all keys > T0 and the
+//      lowest-index keys == T0 (two ballots per slot).
+//   3. Else, if at most 64 keys are > T0, compact them into LDS in block order,
+//      one per lane, and select exactly among them (bitwise threshold search
+//      over one key per lane, ties by lane order = block order).
+//   4. Else (adversarial rows only) bitwise threshold search over all keys.
+// Each bitwise search finds the largest T with count(key >= T) >= k-1 by
+// fixing bits from the top, counting with wave ballots.
+#include "launch.h"
+#include "msa_device.h"
+
+namespace msa {
+namespace {
+
+constexpr int kRowsPerWg = 4;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;                       // -0 ties with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // finite keys are >= 0x007fffff
+}
+
+// Largest T with #{lanes : x >= T} >= kk  (= the kk-th largest x).
+__device__ __forceinline__ uint32_t kth_largest_wave(uint32_t x, int kk) {
+  uint32_t T = 0u;
+#pragma unroll 4
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = T | (1u << bit);
+    if (__popcll(ballot(x >= c)) >= kk) T = c;
+  }
+  return T;
+}
+
+template <int V>
+__device__ __forceinline__ uint32_t kth_largest_all(const uint32_t (&key)[V], int kk) {
+  uint32_t T = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = T | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) cnt += __popcll(ballot(key[i] >= c));
+    if (cnt >= kk) T = c;
+  }
+  return T;
+}
+
+// Write every key > T and the first `need` keys == T (block order) to out[0..).
+template <int V>
+__device__ __forceinline__ void emit_threshold(const uint32_t (&key)[V], uint32_t T, int need, int32_t* out) {
+  const int lane = lane_id();
+  int base = 0, eqbase = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const bool gt = key[i] > T, eq = key[i] == T;
+    const uint64_t eqm = ballot(eq);
+    const int er = eqbase + lanes_below(eqm);
+    eqbase += __popcll(eqm);
+    const bool sel = gt || (eq && er < need);
+    const uint64_t sm = ballot(sel);
+    if (sel) out[base + lanes_below(sm)] = i * 64 + lane;
+    base += __popcll(sm);
+  }
+}
+
+template <int V>
+__global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* __restrict__ bscore,
+                                                                   int32_t* __restrict__ blk, int n_q, int pos0,
+                                                                   int h_kv, int nblk, int topk, int64_t nrows) {
+  __shared__ uint32_t ck[kRowsPerWg][64];
+  __shared__ int32_t ci[kRowsPerWg][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + wave;
+  if (row >= nrows) return;
+  const int t = (int)((row / h_kv) % n_q);
+  const int jl = (pos0 + t) / kBlock;
+  int32_t* out = blk + row * topk;
+  if (jl + 1 <= topk) {
+    for (int i = lane; i < topk; i += 64) out[i] = (i <= jl) ? i : -1;
+    return;
+  }
+  const int kk = topk - 1;
+  if (lane == 0) out[kk] = jl;                         // the local block is the largest index
+  if (kk == 0) return;
+
+  const float* sc = bscore + row * nblk;
+  const int n = jl;                                    // candidates 0..jl-1, n > kk
+  uint32_t key[V];
+  uint32_t lm = 0u;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = i * 64 + lane;
+    key[i] = (e < n) ? order_key(sc[e]) : 0u;          // 0 is below every finite key
+    lm = max(lm, key[i]);
+  }
+  const uint32_t T0 = kth_largest_wave(lm, kk);
+  int c_gt = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) c_gt += __popcll(ballot(key[i] > T0));
+
+  if (c_gt < kk) {                                     // case 2: threshold is T0
+    emit_threshold<V>(key, T0, kk - c_gt, out);
+    return;
+  }
+  if (c_gt <= 64) {                                    // case 3: compact the keys > T0
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const bool gt = key[i] > T0;
+      const uint64_t m = ballot(gt);
+      if (gt) {
+        const int pos = base + lanes_below(m);
+        ck[wave][pos] = key[i];
+        ci[wave][pos] = i * 64 + lane;
+      }
+      base += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t my = lane < c_gt ? ck[wave][lane] : 0u;
+    const int32_t myi = lane < c_gt ? ci[wave][lane] : 0;
+    const uint32_t T = kth_largest_wave(my, kk);
+    const int n_gt = __popcll(ballot(my > T));
+    const uint64_t eqm = ballot(my == T);
+    const bool sel = my > T || (my == T && lanes_below(eqm) < kk - n_gt);
+    const uint64_t sm = ballot(sel);
+    if (sel) out[lanes_below(sm)] = myi;
+    return;
+  }
+  // case 4
+  const uint32_t T = kth_largest_all<V>(key, kk);
+  int n_gt = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) n_gt += __popcll(ballot(key[i] > T));
+  emit_threshold<V>(key, T, kk - n_gt, out);
+}
+
+template <int V>
+hipError_t launch_v(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
+  const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
+  const int64_t wgs = (nrows + kRowsPerWg - 1) / kRowsPerWg;
+  hipLaunchKernelGGL(block_topk_rows<V>, dim3((unsigned)wgs), dim3(kRowsPerWg * 64), 0, stream, bscore, blk,
+                     d.n_q, d.pos0, d.h_kv, d.nblk(), d.topk, nrows);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
+  const int jl_max = (d.pos0 + d.n_q - 1) / kBlock;      // most candidates any row has
+  const int per_lane = (jl_max + 63) / 64;
+  if (per_lane <= 1) return launch_v<1>(d, bscore, blk, stream);
+  if (per_lane <= 2) return launch_v<2>(d, bscore, blk, stream);
+  if (per_lane <= 4) return launch_v<4>(d, bscore, blk, stream);
+  if (per_lane <= 8) return launch_v<8>(d, bscore, blk, stream);
+  if (per_lane <= 16) return launch_v<16>(d, bscore, blk, stream);
+  if (per_lane <= 32) return launch_v<32>(d, bscore, blk, stream);
+  if (per_lane <= 64) return launch_v<64>(d, bscore, blk, stream);
+  return launch_v<128>(d, bscore, blk, stream);         // the C-ABI caps nblk at 8192
+}
+
+}  // namespace msa

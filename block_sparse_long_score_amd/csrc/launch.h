@@ -1,0 +1,51 @@
+// Internal host-side interface between the C-ABI layer and the kernel files.
+// Every launcher assumes its arguments were validated by the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct Dims {
+  int batch, n_q, n_kv, pos0, h_q, h_kv, d, d_idx, block, topk;
+  int nblk() const { return (n_kv + block - 1) / block; }
+  int group() const { return h_q / h_kv; }
+};
+
+// Sparse-prefill workspace: CSR inversion of the block selection plus the
+// per-(query, group, slot) partial softmax results.  Offsets in bytes.
+struct PrefillWs {
+  size_t cnt, off, item_off, cursor, entries, part_o, part_ml, total;
+  int64_t lists, entries_max, items_max;
+};
+PrefillWs prefill_ws_layout(const Dims& d);
+
+// Decode / dense-decode partials.
+struct DecodeWs {
+  size_t part_o, part_ml, total;
+  int nslot;
+};
+DecodeWs sparse_decode_ws_layout(const Dims& d);
+DecodeWs dense_decode_ws_layout(const Dims& d);
+
+hipError_t launch_index_scores(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,
+                               hipStream_t stream);
+hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk_idx, hipStream_t stream);
+hipError_t launch_sparse_prefill(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* ws,
+                                 hipStream_t stream);
+hipError_t launch_sparse_decode(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* ws,
+                                hipStream_t stream);
+hipError_t launch_dense_prefill(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                float scale, uint16_t* out, float* lse, hipStream_t stream);
+hipError_t launch_merge(const Dims& d, const uint16_t* part_o, const float* part_ml, const int32_t* blk,
+                        uint16_t* out, float* lse, int nslot, int per, hipStream_t stream);
+hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               float scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace msa

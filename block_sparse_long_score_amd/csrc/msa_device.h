@@ -1,0 +1,407 @@
+// Device-side building blocks shared by the MSA kernels (gfx950 / CDNA4).
+//
+// Conventions used by every kernel in this library:
+//   * bf16 values travel as uint16_t bit patterns; arithmetic is fp32.
+//   * MFMA: v_mfma_f32_16x16x32_bf16.  For one 16x16 output tile D = A * B:
+//       lane l supplies A[row = l % 16][k = 8*(l/16) .. 8*(l/16)+7]
+//       lane l supplies B[k = 8*(l/16) .. +7][col = l % 16]
+//       lane l receives D[row = 4*(l/16) + r][col = l % 16], r = 0..3.
+//     The contraction is a sum, so any assignment of contraction indices to
+//     the 32 (lane-group, element) slots works as long as A and B agree; the
+//     attention kernels use that freedom to feed softmax probabilities straight
+//     from the score accumulators into the P*V product.
+//   * Scores are computed transposed, S^T = K * Q^T: keys are MFMA rows and
+//     query columns are MFMA columns, so a per-query reduction over keys is a
+//     reduction inside a lane plus two cross-lane steps (xor 16, xor 32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBlock = 128;   // KV block size B (tokens); the only size supported
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 pair, packed low|high (hardware convert).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) {
+  return __shfl_xor(v, m, 64);
+}
+
+// Max over the four lane groups (l/16) that share a column.
+__device__ __forceinline__ float colgroup_max(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  v = fmaxf(v, shfl_xor_f(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float colgroup_sum(float v) {
+  v += shfl_xor_f(v, 16);
+  v += shfl_xor_f(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Number of set bits of `mask` in lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ---------------------------------------------------------------------------
+// One KV block of one K/V head staged in LDS.
+//   k  : [128 keys][D + 8]   row-major, padded so 16-byte MFMA operand reads of
+//        16 consecutive rows fall in distinct banks.
+//   vt : [D][128 + 8]        V transposed (d-major), so an MFMA operand that
+//        needs 8 keys at a fixed d is two 8-byte LDS reads.
+// ---------------------------------------------------------------------------
+template <int D>
+struct KVTile {
+  static constexpr int KS = D + 8;
+  static constexpr int VS = kBlock + 8;
+  uint16_t k[kBlock * KS];
+  uint16_t vt[D * VS];
+};
+
+// Stage keys [s0, s0 + 128) of one K/V head into LDS; rows at or past n_kv are
+// zero-filled.  kbase/vbase point at token 0 of the sequence for this head;
+// row_stride is the distance between consecutive tokens in elements (h_kv * D).
+template <int D, int NT>
+__device__ __forceinline__ void stage_kv_block(KVTile<D>& t, const uint16_t* __restrict__ kbase,
+                                               const uint16_t* __restrict__ vbase, int64_t row_stride,
+                                               int s0, int n_kv, int tid) {
+  constexpr int DC = D / 8;                 // 16-byte chunks per row
+  // K: one 16-byte chunk per work item.
+  for (int w = tid; w < kBlock * DC; w += NT) {
+    const int key = w / DC, dc = w % DC;
+    const int s = s0 + key;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (s < n_kv) val = ld16(kbase + (int64_t)s * row_stride + dc * 8);
+    st16(&t.k[key * KVTile<D>::KS + dc * 8], val);
+  }
+  // V: four consecutive keys x 8 dims per work item, transposed into vt.
+  for (int w = tid; w < (kBlock / 4) * DC; w += NT) {
+    const int kq = w / DC, dc = w % DC;
+    u32x4 r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = s0 + kq * 4 + i;
+      r[i] = (s < n_kv) ? ld16(vbase + (int64_t)s * row_stride + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // element e of each of the 4 rows -> one 8-byte write vt[dc*8+e][kq*4 .. +3]
+      const int word = e >> 1, sh = (e & 1) * 16;
+      const uint32_t x0 = (r[0][word] >> sh) & 0xffffu, x1 = (r[1][word] >> sh) & 0xffffu;
+      const uint32_t x2 = (r[2][word] >> sh) & 0xffffu, x3 = (r[3][word] >> sh) & 0xffffu;
+      u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
+      *reinterpret_cast<u32x2*>(&t.vt[(dc * 8 + e) * KVTile<D>::VS + kq * 4]) = pk;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention of up to 32 query columns (two 16-column MFMA tiles) against the
+// staged block, for one wave.
+//
+// qrow[ct]      : pointer to the D-vector of this lane's column in tile ct
+//                 (column = l % 16), or nullptr for an empty column (reads 0).
+// plim[ct]      : last visible absolute key position for this lane's column;
+//                 keys s0 + key > plim are masked.
+// need_mask     : wave-uniform; false when every key of the block is visible
+//                 to every column.
+// block_scores_softmax returns, per lane and tile ct (replicated over the four
+// lane groups of a column): bmax = block max of the scaled logits in log2
+// units, mref = the max the exponentials were taken against (bmax, or for
+// online softmax max(previous mref, bmax)), bsum = sum of exp2(logit2 - mref).
+// block_pv then accumulates the unnormalised P*V.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__device__ __forceinline__ void load_q_operand(u32x4 (&qb)[2][D / 32], const uint16_t* const (&qrow)[2]) {
+  const int q = lane_id() >> 4;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int cc = 0; cc < D / 32; ++cc)
+      qb[ct][cc] = qrow[ct] ? ld16(qrow[ct] + cc * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Computes S^T for the block and its block-local softmax pieces.  Writes the
+// probabilities (bf16, already laid out as the B operand of the P*V MFMA) into
+// pb and returns the block max / sum per column.
+template <int D>
+__device__ __forceinline__ void block_scores_softmax(const KVTile<D>& t, const u32x4 (&qb)[2][D / 32],
+                                                     float sl2, int s0, const int (&plim)[2], bool need_mask,
+                                                     float (&bmax)[2], float (&bsum)[2],
+                                                     u32x4 (&pb)[2][4], float (&mref)[2], bool use_mref) {
+  const int lane = lane_id();
+  const int col = lane & 15, q = lane >> 4;
+  (void)col;
+  f32x4 s[8][2];
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) s[kt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int cc = 0; cc < D / 32; ++cc) {
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&t.k[(kt * 16 + (lane & 15)) * KVTile<D>::KS + cc * 32 + q * 8]);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) s[kt][ct] = mfma_16x16x32(a, qb[ct][cc], s[kt][ct]);
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = s[kt][ct][r] * sl2;
+        if (need_mask) {
+          const int key = s0 + kt * 16 + q * 4 + r;
+          if (key > plim[ct]) v = -INFINITY;
+        }
+        s[kt][ct][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = colgroup_max(mx);
+    bmax[ct] = mx;
+    // Reference max for the exponentials: the block max, or (online softmax)
+    // the caller's running max merged with it.
+    const float mr = use_mref ? fmaxf(mref[ct], mx) : mx;
+    mref[ct] = mr;
+    float sum = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      float p[8];
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(s[2 * kc + hlf][ct][r] - mr);
+          p[hlf * 4 + r] = e;
+          sum += e;
+        }
+      pb[ct][kc] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    }
+    bsum[ct] = colgroup_sum(sum);
+  }
+}
+
+// acc[ct][pp][half] += V^T * P^T for the block.  acc rows are permuted so that
+// lane group q ends up holding d = 32*pp + 8*q + 4*half + r.
+template <int D>
+__device__ __forceinline__ void block_pv(const KVTile<D>& t, const u32x4 (&pb)[2][4],
+                                         f32x4 (&acc)[2][D / 32][2]) {
+  const int lane = lane_id();
+  const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+    for (int pp = 0; pp < D / 32; ++pp)
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const int d = 32 * pp + 8 * (m >> 2) + 4 * hlf + (m & 3);
+        const uint16_t* row = &t.vt[d * KVTile<D>::VS + 32 * kc + 4 * q];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) acc[ct][pp][hlf] = mfma_16x16x32(a, pb[ct][kc], acc[ct][pp][hlf]);
+      }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Decode-shaped attention: the G <= 16 query heads of one (sequence, group)
+// against blocks [j_begin, j_end) of that group's K/V, with online softmax
+// across the blocks.  One wave, no LDS staging of K/V: K streams from HBM
+// straight into MFMA A operands (S^T = K * Q^T, heads are the columns), V
+// streams with 16-byte loads into a VALU accumulation.  pt is this wave's LDS
+// scratch of kBlock * 16 + 16 floats (probabilities and per-head rescales).
+//
+// Writes the normalised partial o (bf16, [G][D]) and (m2, l) per head, where
+// m2 is the running max of the scaled logits in log2 units and l the sum of
+// exp2(logit2 - m2).  Keys past plim (the query position) are masked.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__device__ __forceinline__ void decode_attend(const uint16_t* __restrict__ qheads,
+                                              const uint16_t* __restrict__ kbase,
+                                              const uint16_t* __restrict__ vbase, int64_t row_stride,
+                                              int n_kv, int plim, int j_begin, int j_end, float sl2,
+                                              float* pt, uint16_t* __restrict__ out_o,
+                                              float* __restrict__ out_ml) {
+  constexpr int CC = D / 32;
+  constexpr int LPR = D / 8;          // lanes per V row (16-byte pieces)
+  constexpr int KPI = 64 / LPR;       // keys per V load instruction
+  const int lane = lane_id();
+  const int col = lane & 15, q = lane >> 4;
+  const int kg = lane / LPR, dl = lane % LPR;
+  float* alpha_s = pt + kBlock * 16;
+
+  u32x4 qb[CC];
+#pragma unroll
+  for (int cc = 0; cc < CC; ++cc)
+    qb[cc] = (col < G) ? ld16(qheads + col * D + cc * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+
+  float m_run = -INFINITY, l_run = 0.f;                 // this lane's column
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  for (int j = j_begin; j < j_end; ++j) {
+    const int s0 = j * kBlock;
+    u32x4 a[8][CC];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      const int s = s0 + kt * 16 + col;
+#pragma unroll
+      for (int cc = 0; cc < CC; ++cc)
+        a[kt][cc] = (s < n_kv) ? ld16(kbase + (int64_t)s * row_stride + cc * 32 + q * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x4 sc[8];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < CC; ++cc) sc[kt] = mfma_16x16x32(a[kt][cc], qb[cc], sc[kt]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = sc[kt][r] * sl2;
+        if (s0 + kt * 16 + q * 4 + r > plim) v = -INFINITY;
+        sc[kt][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = colgroup_max(mx);
+    const float m_new = fmaxf(m_run, mx);               // finite: the first block has key s0 <= plim
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(sc[kt][r] - m_new);
+        sum += e;
+        if (col < G) pt[(kt * 16 + q * 4 + r) * 16 + col] = e;
+      }
+    sum = colgroup_sum(sum);
+    l_run = l_run * alpha + sum;
+    m_run = m_new;
+    if (q == 0 && col < G) alpha_s[col] = alpha;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // P * V on the vector ALUs: lane (kg, dl) owns d = 8*dl .. 8*dl+7 for keys
+    // kg, kg + KPI, ...
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float al = alpha_s[h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+    }
+#pragma unroll 4
+    for (int it = 0; it < kBlock / KPI; ++it) {
+      const int key = it * KPI + kg;
+      const int s = s0 + key;
+      u32x4 vv = {0u, 0u, 0u, 0u};
+      if (s < n_kv) vv = ld16(vbase + (int64_t)s * row_stride + dl * 8);
+      float vf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = bf16_to_f32(vv[e] & 0xffffu);
+        vf[2 * e + 1] = bf16_to_f32(vv[e] >> 16);
+      }
+      const float* prow = pt + key * 16;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pr = prow[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // Sum the partial P*V over the key groups; lanes of group kg = 0 write.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+#pragma unroll
+      for (int m = LPR; m < 64; m <<= 1) v += shfl_xor_f(v, m);
+      acc[h][e] = v;
+    }
+  }
+  // (m, l) of head h lives in lanes with col == h; share them through LDS.
+  if (q == 0 && col < G) {
+    alpha_s[col] = l_run;
+    pt[col] = m_run;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (kg == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float inv = 1.f / alpha_s[h];
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[h][2 * e] * inv, acc[h][2 * e + 1] * inv);
+      st16(out_o + h * D + dl * 8, o);
+    }
+  }
+  if (lane < G) {
+    out_ml[2 * lane] = pt[lane];
+    out_ml[2 * lane + 1] = alpha_s[lane];
+  }
+}
+
+}  // namespace msa

@@ -1,0 +1,413 @@
+// Main branch: exact softmax attention of every query head of a GQA group over
+// only the blocks its index branch selected (hamidun.com news, "Como o MSA
+// funciona": exact attention on the selected blocks only; yhxrc.cn article,
+// "第二步：稀疏分支": all heads of a group share the group's selection and the
+// attention formula runs unchanged on the real K/V; lefilia.fr article: k blocks
+// of 128 tokens per query).
+//
+// Prefill is KV-outer (lumi-systems summary names a KV-outer sparse attention
+// kernel): the selection blk_idx[b][t][g][slot] is inverted into per-(b, g,
+// block) lists of (t, slot); one workgroup stages a 128-token K/V block of one
+// K/V head in LDS once and runs every (query token x group head) column that
+// selected it through MFMA, writing one normalised partial (o, m, l) per
+// (t, g, slot, head).  A merge kernel then combines the <= k partials of each
+// (t, head) with log-sum-exp weights.  Every partial is computed from its own
+// column only, so the order of a list never changes a result bit.
+//
+// Decode streams the <= k selected blocks of each (sequence, group) straight
+// from HBM, one wave per block, and merges the same way.
+#include <climits>
+
+#include "launch.h"
+#include "msa_device.h"
+
+namespace msa {
+namespace {
+
+constexpr int kEntriesPerItem = 64;   // list entries (query tokens) per KV-outer workgroup
+constexpr int kAttnThreads = 256;
+
+int64_t prefill_entries_max(const Dims& d) { return (int64_t)d.batch * d.n_q * d.h_kv * d.topk; }
+
+// ---------------------------------------------------------------- CSR --------
+
+__global__ void fill_zero_i32(int* __restrict__ a, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) a[i] = 0;
+}
+
+__global__ void csr_count(const int32_t* __restrict__ blk, int* __restrict__ cnt, int64_t nent, int n_q, int h_kv,
+                          int topk, int nblk, int pos0) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nent) return;
+  const int j = blk[i];
+  const int64_t row = i / topk;                        // (b * n_q + t) * h_kv + g
+  const int t = (int)((row / h_kv) % n_q);
+  if (j < 0 || j > (pos0 + t) / kBlock) return;        // padding, or not a causal block
+  const int g = (int)(row % h_kv);
+  const int b = (int)(row / ((int64_t)h_kv * n_q));
+  atomicAdd(&cnt[((int64_t)b * h_kv + g) * nblk + j], 1);
+}
+
+// One workgroup: exclusive scans of the list sizes and of their item counts.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void csr_scan(const int* __restrict__ cnt, int* __restrict__ off,
+                                                        int* __restrict__ item_off, int lists, int per_item) {
+  __shared__ int s_e[kScanThreads];
+  __shared__ int s_i[kScanThreads];
+  const int tid = threadIdx.x;
+  const int per = (lists + kScanThreads - 1) / kScanThreads;
+  const int lo = min(lists, tid * per), hi = min(lists, lo + per);
+  int se = 0, si = 0;
+  for (int i = lo; i < hi; ++i) {
+    const int c = cnt[i];
+    se += c;
+    si += (c + per_item - 1) / per_item;
+  }
+  s_e[tid] = se;
+  s_i[tid] = si;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {         // inclusive Hillis-Steele scan
+    const int ae = tid >= o ? s_e[tid - o] : 0;
+    const int ai = tid >= o ? s_i[tid - o] : 0;
+    __syncthreads();
+    s_e[tid] += ae;
+    s_i[tid] += ai;
+    __syncthreads();
+  }
+  int re = s_e[tid] - se, ri = s_i[tid] - si;          // exclusive prefix of this thread's range
+  for (int i = lo; i < hi; ++i) {
+    off[i] = re;
+    item_off[i] = ri;
+    const int c = cnt[i];
+    re += c;
+    ri += (c + per_item - 1) / per_item;
+  }
+  if (tid == kScanThreads - 1) {
+    off[lists] = s_e[tid];
+    item_off[lists] = s_i[tid];
+  }
+}
+
+__global__ void csr_fill(const int32_t* __restrict__ blk, const int* __restrict__ off, int* __restrict__ cursor,
+                         int* __restrict__ entries, int64_t nent, int n_q, int h_kv, int topk, int nblk, int pos0) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nent) return;
+  const int j = blk[i];
+  const int64_t row = i / topk;
+  const int slot = (int)(i % topk);
+  const int g = (int)(row % h_kv);
+  const int64_t bt = row / h_kv;
+  const int t = (int)(bt % n_q);
+  if (j < 0 || j > (pos0 + t) / kBlock) return;
+  const int b = (int)(bt / n_q);
+  const int64_t list = ((int64_t)b * h_kv + g) * nblk + j;
+  const int pos = off[list] + atomicAdd(&cursor[list], 1);
+  entries[pos] = (t << 5) | slot;                      // slot < 32, t < 2^26
+}
+
+// --------------------------------------------------------- KV-outer ---------
+
+template <int D, int LOG2G>
+__global__ __launch_bounds__(kAttnThreads) void sparse_kv_outer(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int* __restrict__ cnt, const int* __restrict__ off, const int* __restrict__ item_off,
+    const int* __restrict__ entries, uint16_t* __restrict__ part_o, float* __restrict__ part_ml, int n_q, int n_kv,
+    int pos0, int h_q, int h_kv, int nblk, int topk, int lists, float sl2) {
+  constexpr int G = 1 << LOG2G;
+  __shared__ KVTile<D> tile;
+  __shared__ int ent[kEntriesPerItem];
+  __shared__ int s_list;
+  const int item = blockIdx.x;
+  if (item >= item_off[lists]) return;                 // grid is an upper bound
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid == 0) {
+    int lo = 0, hi = lists - 1;                        // last list with item_off <= item
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (item_off[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    s_list = lo;
+  }
+  __syncthreads();
+  const int list = s_list;
+  const int c = item - item_off[list];
+  const int e0 = off[list] + c * kEntriesPerItem;
+  const int E = min(kEntriesPerItem, cnt[list] - c * kEntriesPerItem);
+  const int j = list % nblk;
+  const int bg = list / nblk;
+  const int g = bg % h_kv, b = bg / h_kv;
+  if (tid < E) ent[tid] = entries[e0 + tid];
+  const int64_t row_stride = (int64_t)h_kv * D;
+  const int64_t head0 = ((int64_t)b * n_kv * h_kv + g) * D;
+  stage_kv_block<D, kAttnThreads>(tile, k + head0, v + head0, row_stride, j * kBlock, n_kv, tid);
+  __syncthreads();
+
+  const int s0 = j * kBlock;
+  const int ncols = E << LOG2G;
+  const int ngroups = (ncols + 31) >> 5;
+  const int q4 = lane >> 4;
+  for (int cg = wave; cg < ngroups; cg += kAttnThreads / 64) {
+    const uint16_t* qrow[2];
+    int plim[2];
+    bool valid[2];
+    int64_t prow[2];
+    bool mask_any = false;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int col = cg * 32 + ct * 16 + (lane & 15);
+      const int e = col >> LOG2G, hh = col & (G - 1);
+      valid[ct] = e < E;
+      const int en = valid[ct] ? ent[e] : 0;
+      const int t = en >> 5, slot = en & 31;
+      const int p = pos0 + t;
+      qrow[ct] = valid[ct] ? q + (((int64_t)b * n_q + t) * h_q + g * G + hh) * D : nullptr;
+      plim[ct] = valid[ct] ? p : INT_MAX;
+      prow[ct] = ((((int64_t)b * n_q + t) * h_kv + g) * topk + slot) * G + hh;
+      mask_any |= valid[ct] && (p < s0 + kBlock - 1);
+    }
+    const bool need_mask = ballot(mask_any) != 0ull;
+    u32x4 qb[2][D / 32];
+    load_q_operand<D>(qb, qrow);
+    float bmax[2], bsum[2], mref[2] = {0.f, 0.f};
+    u32x4 pb[2][4];
+    block_scores_softmax<D>(tile, qb, sl2, s0, plim, need_mask, bmax, bsum, pb, mref, false);
+    f32x4 acc[2][D / 32][2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int pp = 0; pp < D / 32; ++pp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[ct][pp][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    block_pv<D>(tile, pb, acc);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      if (!valid[ct]) continue;
+      const float inv = 1.f / bsum[ct];
+      uint16_t* dst = part_o + prow[ct] * D;
+#pragma unroll
+      for (int pp = 0; pp < D / 32; ++pp) {
+        const f32x4 a0 = acc[ct][pp][0], a1 = acc[ct][pp][1];
+        u32x4 o = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
+                   pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
+        st16(dst + 32 * pp + 8 * q4, o);
+      }
+      if (q4 == 0) {
+        part_ml[2 * prow[ct]] = bmax[ct];
+        part_ml[2 * prow[ct] + 1] = bsum[ct];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ decode -------
+
+template <int D, int G>
+__global__ __launch_bounds__(kAttnThreads) void sparse_decode_blocks(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ blk, uint16_t* __restrict__ part_o, float* __restrict__ part_ml, int n_kv, int pos0,
+    int h_q, int h_kv, int topk, int64_t units, float sl2) {
+  __shared__ float pt[kAttnThreads / 64][kBlock * 16 + 16];
+  const int wave = threadIdx.x >> 6;
+  const int64_t unit = (int64_t)blockIdx.x * (kAttnThreads / 64) + wave;   // (b, g, slot)
+  if (unit >= units) return;
+  const int j = blk[unit];
+  if (j < 0 || j > pos0 / kBlock) return;              // padding, or not a causal block
+  const int64_t bg = unit / topk;
+  const int g = (int)(bg % h_kv), b = (int)(bg / h_kv);
+  const int64_t head0 = ((int64_t)b * n_kv * h_kv + g) * D;
+  decode_attend<D, G>(q + ((int64_t)b * h_q + g * G) * D, k + head0, v + head0, (int64_t)h_kv * D, n_kv, pos0, j,
+                      j + 1, sl2, pt[wave], part_o + unit * G * D, part_ml + unit * G * 2);
+}
+
+// ------------------------------------------------------------- merge --------
+
+// Slot s of a row takes part when it holds a result: for the sparse paths when
+// blk[.., s] is a block index in [0, jl]; for split dense decode (blk == nullptr)
+// when s * per <= jl.
+template <int D>
+__global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      const int32_t* __restrict__ blk, uint16_t* __restrict__ out,
+                                                      float* __restrict__ lse, int64_t nrows, int n_q, int pos0,
+                                                      int h_q, int G, int nslot, int per) {
+  constexpr int TPR = D / 8;                           // threads per (token, head) row
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // (b * n_q + t) * h_q + h
+  if (row >= nrows) return;
+  const int dl = threadIdx.x % TPR;
+  const int h = (int)(row % h_q);
+  const int64_t bt = row / h_q;
+  const int t = (int)(bt % n_q);
+  const int g = h / G, hh = h % G;
+  const int h_kv = h_q / G;
+  const int jl = (pos0 + t) / kBlock;
+  const int64_t unit0 = (bt * h_kv + g) * nslot;
+  auto live = [&](int s) {
+    if (blk) {
+      const int j = blk[unit0 + s];
+      return j >= 0 && j <= jl;
+    }
+    return s * per <= jl;
+  };
+  float M = -INFINITY;
+  for (int s = 0; s < nslot; ++s)
+    if (live(s)) M = fmaxf(M, part_ml[2 * ((unit0 + s) * G + hh)]);
+  float L = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int s = 0; s < nslot; ++s) {
+    if (!live(s)) continue;
+    const int64_t pr = (unit0 + s) * G + hh;
+    const float w = part_ml[2 * pr + 1] * __builtin_amdgcn_exp2f(part_ml[2 * pr] - M);
+    L += w;
+    const u32x4 o = ld16(part_o + pr * D + dl * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(w, bf16_to_f32(o[e] & 0xffffu), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(w, bf16_to_f32(o[e] >> 16), acc[2 * e + 1]);
+    }
+  }
+  const float inv = 1.f / L;
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  st16(out + row * D + dl * 8, r);
+  if (lse && dl == 0) lse[row] = (M + __log2f(L)) * kLn2;
+}
+
+template <int D>
+hipError_t launch_merge_t(const Dims& d, const uint16_t* part_o, const float* part_ml, const int32_t* blk,
+                          uint16_t* out, float* lse, int nslot, int per, hipStream_t stream) {
+  const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_q;
+  const int rows_per_wg = 256 / (D / 8);
+  const int64_t wgs = (nrows + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL(merge_partials<D>, dim3((unsigned)wgs), dim3(256), 0, stream, part_o, part_ml, blk, out, lse,
+                     nrows, d.n_q, d.pos0, d.h_q, d.group(), nslot, per);
+  return hipGetLastError();
+}
+
+template <int D, int LOG2G>
+hipError_t launch_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* blk, float sl2, uint16_t* out, float* lse, void* ws,
+                            hipStream_t stream) {
+  const PrefillWs L = prefill_ws_layout(d);
+  char* base = static_cast<char*>(ws);
+  int* cnt = reinterpret_cast<int*>(base + L.cnt);
+  int* off = reinterpret_cast<int*>(base + L.off);
+  int* item_off = reinterpret_cast<int*>(base + L.item_off);
+  int* cursor = reinterpret_cast<int*>(base + L.cursor);
+  int* entries = reinterpret_cast<int*>(base + L.entries);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
+  float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
+  const int nblk = d.nblk();
+  const int64_t nent = L.entries_max;
+  const int lists = (int)L.lists;
+  hipLaunchKernelGGL(fill_zero_i32, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream, cnt, (int64_t)lists);
+  hipLaunchKernelGGL(fill_zero_i32, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream, cursor,
+                     (int64_t)lists);
+  const unsigned egrid = (unsigned)((nent + 255) / 256);
+  hipLaunchKernelGGL(csr_count, dim3(egrid), dim3(256), 0, stream, blk, cnt, nent, d.n_q, d.h_kv, d.topk, nblk,
+                     d.pos0);
+  hipLaunchKernelGGL(csr_scan, dim3(1), dim3(kScanThreads), 0, stream, cnt, off, item_off, lists, kEntriesPerItem);
+  hipLaunchKernelGGL(csr_fill, dim3(egrid), dim3(256), 0, stream, blk, off, cursor, entries, nent, d.n_q, d.h_kv,
+                     d.topk, nblk, d.pos0);
+  hipLaunchKernelGGL((sparse_kv_outer<D, LOG2G>), dim3((unsigned)L.items_max), dim3(kAttnThreads), 0, stream, q, k,
+                     v, cnt, off, item_off, entries, part_o, part_ml, d.n_q, d.n_kv, d.pos0, d.h_q, d.h_kv, nblk,
+                     d.topk, lists, sl2);
+  return launch_merge_t<D>(d, part_o, part_ml, blk, out, lse, d.topk, 1, stream);
+}
+
+template <int D, int G>
+hipError_t launch_decode_t(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const int32_t* blk, float sl2, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
+  const DecodeWs L = sparse_decode_ws_layout(d);
+  char* base = static_cast<char*>(ws);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
+  float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
+  const int64_t units = (int64_t)d.batch * d.h_kv * d.topk;
+  const int64_t wgs = (units + 3) / 4;
+  hipLaunchKernelGGL((sparse_decode_blocks<D, G>), dim3((unsigned)wgs), dim3(kAttnThreads), 0, stream, q, k, v, blk,
+                     part_o, part_ml, d.n_kv, d.pos0, d.h_q, d.h_kv, d.topk, units, sl2);
+  return launch_merge_t<D>(d, part_o, part_ml, blk, out, lse, d.topk, 1, stream);
+}
+
+template <int D>
+hipError_t prefill_by_group(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* blk, float sl2, uint16_t* out, float* lse, void* ws, hipStream_t s) {
+  switch (d.group()) {
+    case 1: return launch_prefill_t<D, 0>(d, q, k, v, blk, sl2, out, lse, ws, s);
+    case 2: return launch_prefill_t<D, 1>(d, q, k, v, blk, sl2, out, lse, ws, s);
+    case 4: return launch_prefill_t<D, 2>(d, q, k, v, blk, sl2, out, lse, ws, s);
+    case 8: return launch_prefill_t<D, 3>(d, q, k, v, blk, sl2, out, lse, ws, s);
+    default: return launch_prefill_t<D, 4>(d, q, k, v, blk, sl2, out, lse, ws, s);
+  }
+}
+
+template <int D>
+hipError_t decode_by_group(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const int32_t* blk, float sl2, uint16_t* out, float* lse, void* ws, hipStream_t s) {
+  switch (d.group()) {
+    case 1: return launch_decode_t<D, 1>(d, q, k, v, blk, sl2, out, lse, ws, s);
+    case 2: return launch_decode_t<D, 2>(d, q, k, v, blk, sl2, out, lse, ws, s);
+    case 4: return launch_decode_t<D, 4>(d, q, k, v, blk, sl2, out, lse, ws, s);
+    case 8: return launch_decode_t<D, 8>(d, q, k, v, blk, sl2, out, lse, ws, s);
+    default: return launch_decode_t<D, 16>(d, q, k, v, blk, sl2, out, lse, ws, s);
+  }
+}
+
+}  // namespace
+
+PrefillWs prefill_ws_layout(const Dims& d) {
+  PrefillWs L{};
+  L.lists = (int64_t)d.batch * d.h_kv * d.nblk();
+  L.entries_max = prefill_entries_max(d);
+  L.items_max = (L.entries_max + kEntriesPerItem - 1) / kEntriesPerItem + L.lists;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
+  L.cnt = take(sizeof(int) * L.lists);
+  L.off = take(sizeof(int) * (L.lists + 1));
+  L.item_off = take(sizeof(int) * (L.lists + 1));
+  L.cursor = take(sizeof(int) * L.lists);
+  L.entries = take(sizeof(int) * L.entries_max);
+  L.part_o = take((size_t)L.entries_max * d.group() * d.d * 2);
+  L.part_ml = take((size_t)L.entries_max * d.group() * 2 * sizeof(float));
+  L.total = o;
+  return L;
+}
+
+DecodeWs sparse_decode_ws_layout(const Dims& d) {
+  DecodeWs L{};
+  L.nslot = d.topk;
+  const size_t units = (size_t)d.batch * d.h_kv * d.topk * d.group();
+  size_t o = 0;
+  L.part_o = o;
+  o = align_up(o + units * d.d * 2, 256);
+  L.part_ml = o;
+  o = align_up(o + units * 2 * sizeof(float), 256);
+  L.total = o;
+  return L;
+}
+
+hipError_t launch_sparse_prefill(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* blk, float scale, uint16_t* out, float* lse, void* ws,
+                                 hipStream_t stream) {
+  const float sl2 = scale * kLog2e;
+  if (d.d == 128) return prefill_by_group<128>(d, q, k, v, blk, sl2, out, lse, ws, stream);
+  return prefill_by_group<64>(d, q, k, v, blk, sl2, out, lse, ws, stream);
+}
+
+hipError_t launch_sparse_decode(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* blk, float scale, uint16_t* out, float* lse, void* ws,
+                                hipStream_t stream) {
+  const float sl2 = scale * kLog2e;
+  if (d.d == 128) return decode_by_group<128>(d, q, k, v, blk, sl2, out, lse, ws, stream);
+  return decode_by_group<64>(d, q, k, v, blk, sl2, out, lse, ws, stream);
+}
+
+hipError_t launch_merge(const Dims& d, const uint16_t* part_o, const float* part_ml, const int32_t* blk,
+                        uint16_t* out, float* lse, int nslot, int per, hipStream_t stream) {
+  if (d.d == 128) return launch_merge_t<128>(d, part_o, part_ml, blk, out, lse, nslot, per, stream);
+  return launch_merge_t<64>(d, part_o, part_ml, blk, out, lse, nslot, per, stream);
+}
+
+}  // namespace msa

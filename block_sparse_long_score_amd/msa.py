@@ -1,0 +1,197 @@
+"""Thin Python binding of the C ABI in include/msa.h (libmsa.so).
+
+Argument marshalling only: every function checks dtypes, shapes, contiguity and
+device, passes raw device pointers and the current HIP stream to the library
+function of the same name, and turns a non-OK status into MsaError.  All the
+arithmetic runs in the library's HIP kernels; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .inputs import Shape
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_OP_INDEX_TOPK = 0
+MSA_OP_SPARSE_PREFILL = 1
+MSA_OP_SPARSE_DECODE = 2
+MSA_OP_DENSE_GQA = 3
+MSA_OP_BLOCK_TOPK = 4
+
+STATUS = {
+    0: "MSA_OK",
+    1: "MSA_ERR_NULL",
+    2: "MSA_ERR_SHAPE",
+    3: "MSA_ERR_UNSUPPORTED",
+    4: "MSA_ERR_ALIGN",
+    5: "MSA_ERR_WORKSPACE",
+    6: "MSA_ERR_HIP",
+}
+
+EXPORTED = (
+    "msa_workspace_size",
+    "msa_status_str",
+    "msa_index_topk",
+    "msa_block_topk",
+    "msa_sparse_prefill",
+    "msa_sparse_decode",
+    "msa_dense_gqa",
+)
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        super().__init__(f"{where}: {text}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class MsaDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "n_q", "n_kv", "pos0", "h_q", "h_kv", "d", "d_idx", "block", "topk")]
+
+
+def dims_of(s: Shape) -> MsaDims:
+    return MsaDims(s.batch, s.n_q, s.n_kv, s.pos0, s.h_q, s.h_kv, s.d, s.d_idx, s.block, s.topk)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmsa.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_long_score_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, I32, F, VP = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    D = ctypes.POINTER(MsaDims)
+    L.msa_workspace_size.argtypes = [I32, D]
+    L.msa_workspace_size.restype = S
+    L.msa_status_str.argtypes = [I32]
+    L.msa_status_str.restype = ctypes.c_char_p
+    L.msa_index_topk.argtypes = [D, P, P, P, P, S, VP]
+    L.msa_block_topk.argtypes = [D, P, P, VP]
+    L.msa_sparse_prefill.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
+    L.msa_sparse_decode.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
+    L.msa_dense_gqa.argtypes = [D, P, P, P, F, P, P, P, S, VP]
+    for fn in EXPORTED[2:]:
+        getattr(L, fn).restype = I32
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, dtype, shape):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+def _ws(t):
+    if t is None:
+        return None, 0
+    if t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError("workspace: must be a contiguous device tensor")
+    return ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size()
+
+
+def _raise(st, where):
+    if st != 0:
+        raise MsaError(st, where, lib().msa_status_str(st).decode())
+
+
+def msa_workspace_size(op: int, s: Shape) -> int:
+    d = dims_of(s)
+    return int(lib().msa_workspace_size(op, ctypes.byref(d)))
+
+
+def alloc_workspace(op: int, s: Shape, device="cuda") -> torch.Tensor:
+    """A byte buffer of msa_workspace_size(op, s) bytes (at least 256)."""
+    n = max(256, msa_workspace_size(op, s))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def msa_index_topk(s: Shape, q_idx, k_idx, blk_idx, workspace, stream=None) -> None:
+    _check(q_idx, "q_idx", torch.bfloat16, (s.batch, s.n_q, s.h_kv, s.d_idx))
+    _check(k_idx, "k_idx", torch.bfloat16, (s.batch, s.n_kv, s.d_idx))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, s.n_q, s.h_kv, s.topk))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_index_topk(ctypes.byref(d), _ptr(q_idx), _ptr(k_idx), _ptr(blk_idx), wp, wb, _stream(stream))
+    _raise(st, "msa_index_topk")
+
+
+def msa_block_topk(s: Shape, bscore, blk_idx, stream=None) -> None:
+    _check(bscore, "bscore", torch.float32, (s.batch, s.n_q, s.h_kv, s.nblk))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, s.n_q, s.h_kv, s.topk))
+    d = dims_of(s)
+    st = lib().msa_block_topk(ctypes.byref(d), _ptr(bscore), _ptr(blk_idx), _stream(stream))
+    _raise(st, "msa_block_topk")
+
+
+def msa_sparse_prefill(s: Shape, q, k, v, blk_idx, out, lse=None, workspace=None, scale: float = 0.0,
+                       stream=None) -> None:
+    _check(q, "q", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(k, "k", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(v, "v", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, s.n_q, s.h_kv, s.topk))
+    _check(out, "out", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(lse, "lse", torch.float32, (s.batch, s.n_q, s.h_q))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_sparse_prefill(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx), ctypes.c_float(scale),
+                                  _ptr(out), _ptr(lse), wp, wb, _stream(stream))
+    _raise(st, "msa_sparse_prefill")
+
+
+def msa_sparse_decode(s: Shape, q, k, v, blk_idx, out, lse=None, workspace=None, scale: float = 0.0,
+                      stream=None) -> None:
+    _check(q, "q", torch.bfloat16, (s.batch, 1, s.h_q, s.d))
+    _check(k, "k", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(v, "v", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, 1, s.h_kv, s.topk))
+    _check(out, "out", torch.bfloat16, (s.batch, 1, s.h_q, s.d))
+    _check(lse, "lse", torch.float32, (s.batch, 1, s.h_q))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_sparse_decode(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx), ctypes.c_float(scale),
+                                 _ptr(out), _ptr(lse), wp, wb, _stream(stream))
+    _raise(st, "msa_sparse_decode")
+
+
+def msa_dense_gqa(s: Shape, q, k, v, out, lse=None, workspace=None, scale: float = 0.0, stream=None) -> None:
+    _check(q, "q", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(k, "k", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(v, "v", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(out, "out", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(lse, "lse", torch.float32, (s.batch, s.n_q, s.h_q))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_dense_gqa(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), ctypes.c_float(scale), _ptr(out),
+                             _ptr(lse), wp, wb, _stream(stream))
+    _raise(st, "msa_dense_gqa")

@@ -1,0 +1,156 @@
+/*
+ * msa.h - C ABI of the MiniMax Sparse Attention (MSA) forward path for AMD
+ * MI355X (gfx950).
+ *
+ * The method (as described on the pages this library follows):
+ *   - Built on grouped-query attention: h_q query heads in h_kv consecutive
+ *     groups, each group sharing one K/V head (Notion notes
+ *     "Minimax-sparse-Attention", "what is MHA, MQA, GQA?").
+ *   - Index branch: one index query per (token, group), one index key per token
+ *     shared by all heads; token score = dot product; scores max-pooled per
+ *     KV block; top-k blocks kept per (query, group) (yhxrc.cn article, section
+ *     "第一步：索引分支"; hamidun.com news, "Como o MSA funciona"), with no
+ *     exponential in the selection (lumi-systems news summary), k = 16 blocks of
+ *     128 tokens and the query's own block always included (lefilia.fr
+ *     article).
+ *   - Main branch: exact softmax attention, on the real K/V, of every head of a
+ *     group over only that group's selected blocks (yhxrc.cn article,
+ *     "第二步：稀疏分支"; lefilia.fr article).
+ *   - The index branch is a separate upstream step whose only output is the
+ *     block selection (yhxrc.cn article, "三個刻意的減法", third point), hence
+ *     the split between msa_index_topk and msa_sparse_prefill/decode.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, row-major, last dimension
+ *     contiguous, 16-byte aligned.  bf16 tensors are passed as uint16_t bit
+ *     patterns.  The caller owns every buffer (inputs, outputs, workspace); the
+ *     library never allocates, frees or synchronises and keeps no pointer after
+ *     returning.  Work is enqueued on `stream` (a hipStream_t, NULL = the null
+ *     stream); buffers must stay valid until the stream has passed the work.
+ *   - Query i of a call sits at absolute position p = pos0 + i of its
+ *     sequence; keys/values/index keys of positions 0 .. n_kv-1 are cached.
+ *     Causality is per token: a query sees keys s <= p.
+ *   - Block j covers tokens [j*block, min((j+1)*block, n_kv)); the local block
+ *     of a query is p / block.  nblk = ceil(n_kv / block).
+ *   - Every argument check runs on the host before any HIP call and returns a
+ *     status; no exception crosses the ABI.  MSA_ERR_HIP reports a launch
+ *     failure; faults inside kernels surface at the caller's next
+ *     synchronisation.  Inputs are never written.  Same inputs, same outputs,
+ *     bit for bit (no floating-point atomics).  Functions are stateless and
+ *     thread-safe.
+ *   - Supported: block == 128; 1 <= topk <= 32; d, d_idx in {64, 128};
+ *     h_q / h_kv in {1, 2, 4, 8, 16}; n_kv <= 1,048,576; pos0 + n_q <= n_kv;
+ *     batch * n_q * h_kv * topk < 2^31.  batch == 0 or n_q == 0 is a no-op.
+ *   - NaN or infinite inputs give undefined (but memory-safe) results.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct msa_dims {
+  int32_t batch; /* sequences */
+  int32_t n_q;   /* query tokens per sequence in this call */
+  int32_t n_kv;  /* cached tokens per sequence */
+  int32_t pos0;  /* absolute position of query 0 */
+  int32_t h_q;   /* query heads */
+  int32_t h_kv;  /* K/V heads = GQA groups */
+  int32_t d;     /* head dimension of Q, K, V */
+  int32_t d_idx; /* dimension of index queries / keys */
+  int32_t block; /* KV block size in tokens (128) */
+  int32_t topk;  /* blocks selected per (query, group), local block included */
+} msa_dims;
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_NULL = 1,        /* a required pointer (or dims) is NULL */
+  MSA_ERR_SHAPE = 2,       /* inconsistent sizes: negative, h_q % h_kv, pos0 + n_q > n_kv, decode n_q != 1 */
+  MSA_ERR_UNSUPPORTED = 3, /* sizes this build does not implement (see the list above) */
+  MSA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  MSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than msa_workspace_size() */
+  MSA_ERR_HIP = 6          /* a kernel launch failed */
+} msa_status;
+
+typedef enum msa_op {
+  MSA_OP_INDEX_TOPK = 0,
+  MSA_OP_SPARSE_PREFILL = 1,
+  MSA_OP_SPARSE_DECODE = 2,
+  MSA_OP_DENSE_GQA = 3,
+  MSA_OP_BLOCK_TOPK = 4
+} msa_op;
+
+typedef void* msa_stream; /* hipStream_t */
+
+/* Workspace bytes `op` needs for `dims` (0 if it needs none).  Returns 0 for
+ * dims the op rejects as well; call the op to get the status. */
+size_t msa_workspace_size(msa_op op, const msa_dims* dims);
+
+/* Static, human-readable name of a status. */
+const char* msa_status_str(msa_status status);
+
+/* Index branch: scores, block max-pool, top-k with the local block forced.
+ * (yhxrc.cn article, "第一步：索引分支"; lumi-systems summary; lefilia.fr.)
+ *   q_idx   [batch][n_q][h_kv][d_idx]  bf16   one index query per token and group
+ *   k_idx   [batch][n_kv][d_idx]       bf16   one index key per cached token
+ *   blk_idx [batch][n_q][h_kv][topk]   int32  out: selected blocks, ascending;
+ *           all blocks 0..jl when jl + 1 <= topk (then -1 padding), else jl
+ *           plus the topk-1 earlier blocks with the largest pooled score, ties
+ *           to the lower block index.
+ *   workspace >= msa_workspace_size(MSA_OP_INDEX_TOPK).  On return it holds, at
+ *           offset 0, the pooled block scores bscore[batch][n_q][h_kv][nblk]
+ *           (fp32): entry j <= jl is max over tokens s of block j with s <= p of
+ *           q_idx . k_idx[s]; entries j > jl are unspecified.
+ * Scores accumulate in fp32; with integer-valued index inputs of magnitude
+ * <= 3 and d_idx <= 128 they are exact. */
+msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
+                          int32_t* blk_idx, void* workspace, size_t workspace_bytes, msa_stream stream);
+
+/* The top-k step alone, on pooled scores in the layout msa_index_topk leaves in
+ * its workspace (lumi-systems summary: exponential-free top-k).
+ *   bscore  [batch][n_q][h_kv][nblk] fp32 (only entries j < jl are read)
+ *   blk_idx [batch][n_q][h_kv][topk] int32 out, as for msa_index_topk. */
+msa_status msa_block_topk(const msa_dims* dims, const float* bscore, int32_t* blk_idx, msa_stream stream);
+
+/* Main branch, prefill: for every head h of group g = h / (h_q / h_kv),
+ *   out[b][t][h] = softmax over visible keys s of (scale * q[b][t][h] . k[b][s][g]) applied to v[b][s][g],
+ * where s is visible when block(s) is in blk_idx[b][t][g] and s <= p
+ * (yhxrc.cn article, "第二步：稀疏分支"; hamidun.com, "Como o MSA funciona").
+ *   q   [batch][n_q][h_q][d]   bf16
+ *   k,v [batch][n_kv][h_kv][d] bf16
+ *   blk_idx [batch][n_q][h_kv][topk] int32 from msa_index_topk, or any
+ *           selection of distinct blocks j <= jl (entries < 0 or > jl are
+ *           skipped); at least one valid entry per row.
+ *   scale   softmax scale; <= 0 means 1/sqrt(d)
+ *   out [batch][n_q][h_q][d] bf16 (fp32 accumulation, round-to-nearest-even)
+ *   lse [batch][n_q][h_q] fp32 natural-log normaliser of the scaled logits, or NULL
+ *   workspace >= msa_workspace_size(MSA_OP_SPARSE_PREFILL). */
+msa_status msa_sparse_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
+                              size_t workspace_bytes, msa_stream stream);
+
+/* Main branch, decode: msa_sparse_prefill with n_q == 1; each of the batch
+ * sequences has its own cache of n_kv tokens and its query at p = pos0
+ * (normally n_kv - 1).  Streams only the selected blocks (lefilia.fr: a fixed
+ * budget of topk * 128 key-value tokens per query whatever the context).
+ *   q [batch][1][h_q][d], blk_idx [batch][1][h_kv][topk], out [batch][1][h_q][d]. */
+msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
+                             size_t workspace_bytes, msa_stream stream);
+
+/* Dense causal GQA, the comparator: as msa_sparse_prefill with every s <= p
+ * visible (hamidun.com, "Como o MSA funciona": standard GQA attends every
+ * key).  n_q == 1 takes a split-key decode path that needs workspace; n_q > 1
+ * needs none (workspace may then be NULL). */
+msa_status msa_dense_gqa(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v, float scale,
+                         uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, msa_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

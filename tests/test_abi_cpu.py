@@ -1,0 +1,143 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments with the documented
+status before touching the GPU (every check here returns before any HIP call).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_long_score_amd import msa as M
+from block_sparse_long_score_amd.inputs import WORKLOADS, Shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:msa_status|size_t|const char\*)\s+(msa_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = M.lib()
+    names = declared_functions()
+    assert set(names) == set(M.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = M.lib()
+    for code, name in M.STATUS.items():
+        assert lib.msa_status_str(code).decode().startswith(name)
+
+
+def dims(**kw):
+    base = dict(batch=1, n_q=256, n_kv=4096, pos0=3840, h_q=8, h_kv=2, d=128, d_idx=128, block=128, topk=16)
+    base.update(kw)
+    return M.MsaDims(*[base[f] for f, _ in M.MsaDims._fields_])
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: every call below fails validation
+ODD = ctypes.c_void_p(0x10008)
+
+
+def index_call(d, q=FAKE, k=FAKE, blk=FAKE, ws=FAKE, wsb=1 << 40):
+    return M.lib().msa_index_topk(ctypes.byref(d) if d is not None else None, q, k, blk, ws, wsb, None)
+
+
+def prefill_call(d, q=FAKE, k=FAKE, v=FAKE, blk=FAKE, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40):
+    return M.lib().msa_sparse_prefill(ctypes.byref(d) if d is not None else None, q, k, v, blk,
+                                      ctypes.c_float(0.0), out, lse, ws, wsb, None)
+
+
+def decode_call(d, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, blk=FAKE, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return M.lib().msa_sparse_decode(ctypes.byref(d), a["q"], a["k"], a["v"], a["blk"], ctypes.c_float(0.0),
+                                     a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def dense_call(d, ws=FAKE, wsb=0):
+    return M.lib().msa_dense_gqa(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.c_float(0.0), FAKE, None, ws, wsb, None)
+
+
+def test_null_dims_and_pointers():
+    assert index_call(None) == NULL
+    assert prefill_call(None) == NULL
+    assert index_call(dims(), q=None) == NULL
+    assert index_call(dims(), blk=None) == NULL
+    assert prefill_call(dims(), v=None) == NULL
+    assert prefill_call(dims(), out=None) == NULL
+    assert M.lib().msa_block_topk(ctypes.byref(dims()), None, FAKE, None) == NULL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(h_q=6, h_kv=4),            # h_q % h_kv
+    dict(pos0=4000),                # pos0 + n_q > n_kv
+    dict(n_q=-1),
+    dict(batch=-2),
+    dict(n_kv=0),
+    dict(topk=0),
+])
+def test_shape_errors(kw):
+    assert index_call(dims(**kw)) == SHAPE
+    assert prefill_call(dims(**kw)) == SHAPE
+
+
+def test_decode_needs_single_query():
+    assert decode_call(dims(n_q=2, pos0=4094)) == SHAPE
+
+
+@pytest.mark.parametrize("kw,op", [
+    (dict(block=64), "both"),
+    (dict(topk=33), "both"),
+    (dict(d=96), "attn"),
+    (dict(d_idx=32), "index"),
+    (dict(h_q=64, h_kv=2), "both"),          # group of 32
+    (dict(h_q=24, h_kv=8), "both"),          # group of 3
+    (dict(n_kv=(1 << 20) + 128, pos0=(1 << 20) - 128), "both"),
+])
+def test_unsupported(kw, op):
+    if op in ("both", "index"):
+        assert index_call(dims(**kw)) == UNSUP
+    if op in ("both", "attn"):
+        assert prefill_call(dims(**kw)) == UNSUP
+
+
+def test_alignment_and_workspace():
+    assert index_call(dims(), q=ODD) == ALIGN
+    assert prefill_call(dims(), lse=ODD) == ALIGN
+    assert index_call(dims(), ws=None) == WS
+    need = M.lib().msa_workspace_size(M.MSA_OP_INDEX_TOPK, ctypes.byref(dims()))
+    assert need >= 256 * 2 * 32 * 4
+    assert index_call(dims(), wsb=need - 1) == WS
+    need_p = M.lib().msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(dims()))
+    assert prefill_call(dims(), wsb=need_p - 1) == WS
+    d1 = dims(n_q=1, pos0=4095)
+    assert dense_call(d1, ws=None) == WS
+    assert dense_call(d1, wsb=M.lib().msa_workspace_size(M.MSA_OP_DENSE_GQA, ctypes.byref(d1)) - 1) == WS
+
+
+def test_empty_calls_are_noops():
+    assert index_call(dims(n_q=0), q=None, k=None, blk=None, ws=None) == OK
+    assert prefill_call(dims(batch=0), q=None, k=None, v=None, blk=None, out=None, ws=None) == OK
+
+
+def test_workspace_sizes_cover_their_buffers():
+    for name, (_, s) in WORKLOADS.items():
+        n_idx = M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, s)
+        assert n_idx >= s.batch * s.n_q * s.h_kv * s.nblk * 4, name
+        if s.n_q == 1:
+            assert M.msa_workspace_size(M.MSA_OP_SPARSE_DECODE, s) >= s.batch * s.h_kv * s.topk * s.group * (s.d * 2 + 8)
+            assert M.msa_workspace_size(M.MSA_OP_DENSE_GQA, s) > 0
+        else:
+            n_pre = M.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, s)
+            assert n_pre >= s.batch * s.n_q * s.h_kv * s.topk * s.group * (s.d * 2 + 8), name
+            assert M.msa_workspace_size(M.MSA_OP_DENSE_GQA, s) == 0
+    assert M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, Shape(1, 10, 5, 0, 8, 2, 128, 128)) == 0   # rejected dims

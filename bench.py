@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the hot path over one batch of synthetic input:
+index scoring + block max-pool (msa_index_scores), exponential-free top-k
+(msa_block_topk) and block-sparse prefill attention (msa_sparse_prefill) on the
+131,072-token prefill workload (64 query heads on 8 K/V heads, d = d_idx = 128,
+128-token blocks, k = 16).  Inputs are resident in HBM before the timed region.
+`value` is prefill tokens per second.  The same JSON line also carries:
+  * per-stage times measured with HIP events on the stream the library runs on,
+  * `roofline` for the dominant kernel (algorithmic flops or bytes per launch
+    over its measured average duration),
+  * the decode leg (1M-token caches, batch 8: index top-k + sparse decode),
+  * the library's own dense causal GQA on the same inputs (speedup),
+  * the top-k kernel against torch.topk on the same pooled scores,
+  * `cpu_baseline`: the fp64 oracle timed on a bounded sample of the workload.
+All progress goes to stderr; stdout gets exactly one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MSA prefill tok/s & decode tok/s at 128K–1M ctx; % MFMA / HBM roofline"
+PEAK_BF16_FLOPS = 2.5e15        # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_128k")
+    ap.add_argument("--decode-workload", default="decode_1m_b8")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-topk-compare", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ counts --
+
+def causal_positions(s):
+    import numpy as np
+    return s.pos0 + np.arange(s.n_q, dtype=np.int64)
+
+
+def index_flops(s) -> float:
+    """S1: h_kv * d_idx * 2 flops per (query, causal token), all sequences."""
+    p = causal_positions(s)
+    return float(s.batch * s.h_kv * s.d_idx * 2 * (p + 1).sum())
+
+
+def visible_counts(s):
+    """|V_t|: causal tokens of the local block plus (k-1) full earlier blocks,
+    or every causal token when the query has at most k blocks."""
+    import numpy as np
+    p = causal_positions(s)
+    jl = p // s.block
+    local = p - jl * s.block + 1
+    full = np.minimum(jl, s.topk - 1) * s.block
+    return local + full
+
+
+def sparse_flops(s) -> float:
+    """S4: QK^T and PV, 4 * d flops per (query head, visible key)."""
+    return float(s.batch * s.h_q * s.d * 4 * visible_counts(s).sum())
+
+
+def dense_flops(s) -> float:
+    p = causal_positions(s)
+    return float(s.batch * s.h_q * s.d * 4 * (p + 1).sum())
+
+
+def topk_bytes(s) -> float:
+    """S3: read every candidate pooled score (j < jl) once, write the indices."""
+    p = causal_positions(s)
+    cand = (p // s.block).sum()
+    return float(s.batch * s.h_kv * (cand * 4 + s.n_q * s.topk * 4))
+
+
+def decode_bytes(s) -> float:
+    """Decode step: index keys of every cached token, the selected K/V, the
+    queries, pooled scores written and read, indices, outputs."""
+    vis = float(visible_counts(s).sum())
+    nblk = s.nblk
+    b = s.batch
+    kidx = b * s.n_kv * s.d_idx * 2
+    kv = b * vis * s.h_kv * s.d * 2 * 2
+    small = b * (s.h_kv * s.d_idx * 2 + s.h_q * s.d * 2 * 2 + s.h_kv * nblk * 4 * 2 + s.h_kv * s.topk * 4 * 2)
+    return float(kidx + kv + small)
+
+
+# ------------------------------------------------------------------ timing --
+
+def time_calls(torch, fns, steps, warmup):
+    """Run the list of zero-argument launches `fns` as one step; returns the
+    mean per-step wall time (events around the whole timed region) and the mean
+    time of each launch (events between launches) in milliseconds."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        ev[i][0].record()
+        for j, f in enumerate(fns):
+            f()
+            ev[i][j + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end) / steps
+    per = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps for j in range(len(fns))]
+    return total, per
+
+
+# ------------------------------------------------------------ CPU baseline --
+
+def cpu_baseline(s, inp, seconds, seed=99):
+    """The fp64 oracle, as it stands, on a seeded sample of query rows of the
+    same workload: all groups' index scoring, pooling and selection, then all
+    heads' sparse attention, per sampled row."""
+    import numpy as np
+    from oracle import msa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(x.get("num_threads", 1)) for x in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    log("cpu baseline: copying inputs to host")
+    q_idx = inp["q_idx"][0].float().cpu().numpy().astype(np.float64)
+    kseq = inp["k_idx"][0].float().cpu().numpy().astype(np.float64)
+    q = inp["q"][0].float().cpu().numpy().astype(np.float64)
+    k = inp["k"][0].float().cpu().numpy().astype(np.float64)
+    v = inp["v"][0].float().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(s.n_q)
+    scale = O.default_scale(s.d)
+    G = s.group
+    done = 0
+    t0 = time.perf_counter()
+    for t in order:
+        p = s.pos0 + int(t)
+        for g in range(s.h_kv):
+            _, sel = O.index_topk_row(q_idx[t, g], kseq, p, s.block, s.topk)
+            pos = O.visible_positions(sel, p, s.block, s.n_kv)
+            O.softmax_attention(q[t, g * G:(g + 1) * G], k[pos, g], v[pos, g], scale)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} query rows drawn uniformly (seed {seed}) from the {s.n_q}-token prefill, "
+                      f"all {s.h_kv} groups and {s.h_q} heads each, {el:.1f} s on the host"}
+
+
+# -------------------------------------------------------------------- main --
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards by K/V-head group or by sequence with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_score_amd import msa as M
+    from block_sparse_long_score_amd.inputs import WORKLOADS, make_inputs
+
+    M.lib()                                            # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    dev = "cuda"
+    cid, s = WORKLOADS[args.workload]
+    log(f"workload {args.workload}: {s}")
+    inp = make_inputs(s, cid, device=dev)
+    bscore = torch.empty((s.batch, s.n_q, s.h_kv, s.nblk), dtype=torch.float32, device=dev)
+    blk = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.int32, device=dev)
+    out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((s.batch, s.n_q, s.h_q), dtype=torch.float32, device=dev)
+    ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
+    torch.cuda.synchronize()
+
+    stages = [
+        lambda: M.msa_index_scores(s, inp["q_idx"], inp["k_idx"], bscore),
+        lambda: M.msa_block_topk(s, bscore, blk),
+        lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
+    ]
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms_step, (ms_idx, ms_topk, ms_sparse) = time_calls(torch, stages, args.steps, args.warmup)
+    tokens = s.batch * s.n_q
+    value = tokens / (ms_step * 1e-3)
+    f_idx, f_sp = index_flops(s), sparse_flops(s)
+    log(f"step {ms_step:.3f} ms: index {ms_idx:.3f}, top-k {ms_topk:.3f}, sparse {ms_sparse:.3f} -> {value:.4g} tok/s")
+
+    per_stage = {
+        "index_scores": {"ms": ms_idx, "bound": "mfma", "achieved": f_idx / (ms_idx * 1e-3) / 1e12,
+                         "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"},
+        "block_topk": {"ms": ms_topk, "bound": "hbm", "achieved": topk_bytes(s) / (ms_topk * 1e-3) / 1e9,
+                       "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s"},
+        "sparse_prefill": {"ms": ms_sparse, "bound": "mfma", "achieved": f_sp / (ms_sparse * 1e-3) / 1e12,
+                           "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"},
+    }
+    for v in per_stage.values():
+        v["frac"] = v["achieved"] / v["peak"]
+    # The index scoring stage is a single kernel launch, so its event time is
+    # that kernel's duration; it is the roofline reported.
+    dom = per_stage["index_scores"]
+    roofline = {"kernel": "index_scores_tiled", "bound": "mfma", "achieved": dom["achieved"], "peak": dom["peak"],
+                "unit": "TFLOP/s", "frac": dom["frac"], "traffic": None,
+                "algorithmic_per_launch": f_idx, "avg_launch_ms": ms_idx}
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": s.batch, "n_q": s.n_q, "n_kv": s.n_kv, "pos0": s.pos0,
+                   "h_q": s.h_q, "h_kv": s.h_kv, "d": s.d, "d_idx": s.d_idx, "block": s.block, "topk": s.topk},
+        "roofline": roofline,
+        "stages": per_stage,
+        "end_to_end_mfma_frac": (f_idx + f_sp) / (ms_step * 1e-3) / PEAK_BF16_FLOPS,
+    }
+
+    if not args.no_topk_compare:
+        vals = bscore[..., : s.nblk]
+        ms_torch, _ = time_calls(torch, [lambda: torch.topk(vals, s.topk - 1, dim=-1)], 3, 1)
+        result["topk_vs_torch"] = {"msa_block_topk_ms": ms_topk, "torch_topk_ms": ms_torch,
+                                   "speedup": ms_torch / ms_topk,
+                                   "note": "torch.topk over the full pooled rows, k-1 per row; timing only"}
+        log(f"top-k: msa {ms_topk:.3f} ms vs torch.topk {ms_torch:.3f} ms")
+
+    if not args.no_dense:
+        dout = torch.empty_like(out)
+        dlse = torch.empty_like(lse)
+        ms_dense, _ = time_calls(torch, [lambda: M.msa_dense_gqa(s, inp["q"], inp["k"], inp["v"], dout, dlse)], 2, 1)
+        fd = dense_flops(s)
+        result["dense_gqa"] = {"ms": ms_dense, "tok_s": tokens / (ms_dense * 1e-3),
+                               "mfma_frac": fd / (ms_dense * 1e-3) / PEAK_BF16_FLOPS,
+                               "msa_speedup": ms_dense / ms_step}
+        log(f"dense GQA {ms_dense:.2f} ms -> MSA speedup {ms_dense / ms_step:.2f}x")
+        del dout, dlse
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(s, inp, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+    result["cpu_baseline"] = cpu
+
+    del ws, out, lse, bscore, blk, inp
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        did, ds = WORKLOADS[args.decode_workload]
+        log(f"decode workload {args.decode_workload}: {ds}")
+        dinp = make_inputs(ds, did, device=dev)
+        dws_i = M.alloc_workspace(M.MSA_OP_INDEX_TOPK, ds)
+        dws_s = M.alloc_workspace(M.MSA_OP_SPARSE_DECODE, ds)
+        dblk = torch.empty((ds.batch, 1, ds.h_kv, ds.topk), dtype=torch.int32, device=dev)
+        dout = torch.empty((ds.batch, 1, ds.h_q, ds.d), dtype=torch.bfloat16, device=dev)
+        dlse = torch.empty((ds.batch, 1, ds.h_q), dtype=torch.float32, device=dev)
+        dsteps = max(args.steps, 20)
+        ms_dec, (ms_di, ms_ds) = time_calls(torch, [
+            lambda: M.msa_index_topk(ds, dinp["q_idx"], dinp["k_idx"], dblk, dws_i),
+            lambda: M.msa_sparse_decode(ds, dinp["q"], dinp["k"], dinp["v"], dblk, dout, dlse, dws_s),
+        ], dsteps, args.warmup)
+        by = decode_bytes(ds)
+        dec = {"workload": args.decode_workload, "batch": ds.batch, "n_kv": ds.n_kv, "steps": dsteps,
+               "ms_per_step": ms_dec, "tok_s": ds.batch / (ms_dec * 1e-3),
+               "index_topk_ms": ms_di, "sparse_decode_ms": ms_ds,
+               "algorithmic_bytes": by, "hbm_gbs": by / (ms_dec * 1e-3) / 1e9,
+               "hbm_frac": by / (ms_dec * 1e-3) / PEAK_HBM_BYTES}
+        log(f"decode step {ms_dec:.3f} ms ({ms_di:.3f} index top-k + {ms_ds:.3f} sparse) -> "
+            f"{dec['tok_s']:.4g} tok/s, {dec['hbm_frac'] * 100:.1f}% of HBM peak")
+        if not args.no_dense:
+            ddws = M.alloc_workspace(M.MSA_OP_DENSE_GQA, ds)
+            ms_dd, _ = time_calls(torch, [lambda: M.msa_dense_gqa(ds, dinp["q"], dinp["k"], dinp["v"], dout, dlse,
+                                                                ddws)], 3, 1)
+            dec["dense_gqa_ms"] = ms_dd
+            dec["msa_speedup"] = ms_dd / ms_dec
+            log(f"dense decode {ms_dd:.3f} ms -> MSA decode speedup {ms_dd / ms_dec:.2f}x")
+        result["decode"] = dec
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -120,6 +120,16 @@ msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uin
   return hip_status(msa::launch_block_topk(d, bscore, blk_idx, s));
 }
 
+msa_status msa_index_scores(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,
+                            msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_INDEX_TOPK));
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  if (!q_idx || !k_idx || !bscore) return MSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(k_idx) || misaligned(bscore)) return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_index_scores(to_dims(*dims), q_idx, k_idx, bscore, static_cast<hipStream_t>(stream)));
+}
+
 msa_status msa_block_topk(const msa_dims* dims, const float* bscore, int32_t* blk_idx, msa_stream stream) {
   msa_status st = check_dims(dims, op_needs(MSA_OP_BLOCK_TOPK));
   if (st != MSA_OK) return st;

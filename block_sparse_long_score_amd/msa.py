@@ -38,6 +38,7 @@ EXPORTED = (
     "msa_workspace_size",
     "msa_status_str",
     "msa_index_topk",
+    "msa_index_scores",
     "msa_block_topk",
     "msa_sparse_prefill",
     "msa_sparse_decode",
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
     L.msa_status_str.argtypes = [I32]
     L.msa_status_str.restype = ctypes.c_char_p
     L.msa_index_topk.argtypes = [D, P, P, P, P, S, VP]
+    L.msa_index_scores.argtypes = [D, P, P, P, VP]
     L.msa_block_topk.argtypes = [D, P, P, VP]
     L.msa_sparse_prefill.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
     L.msa_sparse_decode.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
@@ -144,6 +146,15 @@ def msa_index_topk(s: Shape, q_idx, k_idx, blk_idx, workspace, stream=None) -> N
     wp, wb = _ws(workspace)
     st = lib().msa_index_topk(ctypes.byref(d), _ptr(q_idx), _ptr(k_idx), _ptr(blk_idx), wp, wb, _stream(stream))
     _raise(st, "msa_index_topk")
+
+
+def msa_index_scores(s: Shape, q_idx, k_idx, bscore, stream=None) -> None:
+    _check(q_idx, "q_idx", torch.bfloat16, (s.batch, s.n_q, s.h_kv, s.d_idx))
+    _check(k_idx, "k_idx", torch.bfloat16, (s.batch, s.n_kv, s.d_idx))
+    _check(bscore, "bscore", torch.float32, (s.batch, s.n_q, s.h_kv, s.nblk))
+    d = dims_of(s)
+    st = lib().msa_index_scores(ctypes.byref(d), _ptr(q_idx), _ptr(k_idx), _ptr(bscore), _stream(stream))
+    _raise(st, "msa_index_scores")
 
 
 def msa_block_topk(s: Shape, bscore, blk_idx, stream=None) -> None:

@@ -110,6 +110,13 @@ const char* msa_status_str(msa_status status);
 msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
                           int32_t* blk_idx, void* workspace, size_t workspace_bytes, msa_stream stream);
 
+/* Scoring and block max-pool alone (the first half of msa_index_topk), for
+ * callers that want the pooled scores themselves.
+ *   bscore [batch][n_q][h_kv][nblk] fp32 out, as msa_index_topk documents for
+ *          its workspace (entries j > jl unspecified). */
+msa_status msa_index_scores(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,
+                            msa_stream stream);
+
 /* The top-k step alone, on pooled scores in the layout msa_index_topk leaves in
  * its workspace (lumi-systems summary: exponential-free top-k).
  *   bscore  [batch][n_q][h_kv][nblk] fp32 (only entries j < jl are read)

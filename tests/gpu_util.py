@@ -104,7 +104,9 @@ class OutCheck:
 
 def check_index_rows(s: Shape, q_idx64, kseq64_of, blk_gpu, bscore_gpu, rows):
     """Bit-exact check of pooled scores (j <= jl) and selections on (b, t) rows.
+    q_idx64 is an fp64 array [b][t][g][d_idx] or a callable (b, t) -> [g][d_idx];
     kseq64_of(b) returns the fp64 index keys of sequence b."""
+    qrow = q_idx64 if callable(q_idx64) else (lambda b, t: q_idx64[b, t])
     sels = {}
     for b, t in rows:
         p = s.pos0 + t
@@ -113,7 +115,7 @@ def check_index_rows(s: Shape, q_idx64, kseq64_of, blk_gpu, bscore_gpu, rows):
         bs = bscore_gpu[b, t, :, : jl + 1].cpu().numpy()
         bk = blk_gpu[b, t].cpu().numpy()
         for g in range(s.h_kv):
-            pooled, sel = O.index_topk_row(q_idx64[b, t, g], kseq, p, s.block, s.topk)
+            pooled, sel = O.index_topk_row(qrow(b, t)[g], kseq, p, s.block, s.topk)
             assert np.array_equal(bs[g], pooled.astype(np.float32)), f"bscore mismatch b={b} t={t} g={g}"
             assert np.array_equal(bk[g], sel.astype(np.int32)), \
                 f"selection mismatch b={b} t={t} g={g}: gpu={bk[g].tolist()} oracle={sel.tolist()}"

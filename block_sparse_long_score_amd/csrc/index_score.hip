@@ -18,6 +18,8 @@
 //   * index_scores_skinny: at most 16 query rows per sequence (decode).  Pure
 //     index-key streaming: every wave pulls its key blocks straight from HBM into
 //     MFMA A operands (no LDS round trip), bound by HBM bandwidth.
+#include <algorithm>
+
 #include "launch.h"
 #include "msa_device.h"
 
@@ -25,26 +27,75 @@ namespace msa {
 namespace {
 
 constexpr int kTiledWaves = 8;
-constexpr int kTiledColsPerWave = 128;                   // 8 MFMA column tiles
+constexpr int kTiledColsPerWave = 128;                   // 4 MFMA column tiles of 32
 constexpr int kTiledRows = kTiledWaves * kTiledColsPerWave;
+constexpr int kFlush = 16;                               // pooled blocks buffered per row in LDS
 
 template <int DI>
-struct KeyTile {
-  static constexpr int S = DI + 8;                      // padded row stride
-  uint16_t k[kBlock * S];
+struct IndexSmem {
+  static constexpr int S = DI + 8;                      // padded key row stride (elements)
+  static constexpr int OS = kFlush + 1;                 // padded pooled-row stride (floats)
+  uint16_t k[2][kBlock * S];                            // double-buffered key block
+  float o[kTiledRows * OS];                             // pooled maxima awaiting write-out (per-wave rows)
 };
+
+// Scores of one 128-key block against this wave's 128 columns, reduced to the
+// per-lane partial max rm[ct] over the 64 keys this lane's rows cover.  Work
+// runs in 16 units (32-key tile kt, 32-column tile ct) of 8 chained MFMAs; the
+// max-reduction of unit u-1 is issued after the MFMAs of unit u so the vector
+// ALUs run while the matrix pipe is busy.  MASK adds the causal test (only the
+// blocks reaching past some column's position need it).
+template <int DI, bool MASK>
+__device__ __forceinline__ void score_block(const uint16_t* __restrict__ kt_lds, const u32x4 (&qb)[4][DI / 16],
+                                            int key0, const int (&plim)[4], float (&rm)[4]) {
+  constexpr int KC = DI / 16;
+  constexpr int S = DI + 8;
+  const int lane = lane_id();
+  const int half = lane >> 5, r32 = lane & 31;
+  f32x16 acc[2];
+  auto reduce = [&](const f32x16& a, int u) {
+    const int kt = u >> 2, ct = u & 3;
+    float m = rm[ct];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x = a[v];
+      if (MASK && (key0 + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3)) > plim[ct]) x = -INFINITY;
+      m = vmax(m, x);
+    }
+    rm[ct] = m;
+  };
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    u32x4 a[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      a[kc] = *reinterpret_cast<const u32x4*>(kt_lds + (kt * 32 + r32) * S + kc * 16 + half * 8);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int u = kt * 4 + ct;
+      f32x16& cur = acc[u & 1];
+      cur = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) cur = mfma_32x32x16(a[kc], qb[ct][kc], cur);
+      if (u > 0) reduce(acc[(u - 1) & 1], u - 1);
+    }
+  }
+  reduce(acc[1], 15);
+}
 
 template <int DI>
 __global__ __launch_bounds__(kTiledWaves * 64) void index_scores_tiled(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, float* __restrict__ bscore,
     int n_q, int n_kv, int pos0, int h_kv, int nblk, int blocks_per_chunk) {
-  constexpr int CC = DI / 32;                            // 32-wide contraction chunks
+  constexpr int KC = DI / 16;                            // 16-wide contraction chunks
   constexpr int NT = kTiledWaves * 64;
-  __shared__ KeyTile<DI> tiles[2];
+  using Smem = IndexSmem<DI>;
+  __shared__ Smem sm;
 
   const int b = blockIdx.z;
   const int64_t nrows = (int64_t)n_q * h_kv;
-  const int64_t r0 = (int64_t)blockIdx.y * kTiledRows;
+  // Latest (longest) row tiles are dispatched first, so the short ones fill the tail.
+  const int64_t r0 = (int64_t)(gridDim.y - 1 - blockIdx.y) * kTiledRows;
   const int64_t r_end = min(r0 + (int64_t)kTiledRows, nrows);
   const int t_last = (int)((r_end - 1) / h_kv);
   const int jmax = (pos0 + t_last) / kBlock;
@@ -54,111 +105,93 @@ __global__ __launch_bounds__(kTiledWaves * 64) void index_scores_tiled(
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int q = lane >> 4, cl = lane & 15;
+  const int half = lane >> 5, r32 = lane & 31;
 
-  // This wave's columns.
+  // This wave's columns: rows rw0 + 32*ct + r32.
   const int64_t rw0 = r0 + (int64_t)wave * kTiledColsPerWave;
   const bool wave_live = rw0 < r_end;
   const int tw0 = wave_live ? (int)(rw0 / h_kv) : 0;
   const int tw1 = wave_live ? (int)((min(rw0 + kTiledColsPerWave, r_end) - 1) / h_kv) : 0;
   const int jw_max = (pos0 + tw1) / kBlock;              // last block any column of the wave needs
+  const int jw_mask = (pos0 + tw0 + 1) / kBlock;         // first block reaching past the earliest column
 
-  u32x4 qb[8][CC];
-  int plim[8];
-  bool cvalid[8];
-  float* orow[8];
-  const uint16_t* kseq = k_idx + (int64_t)b * n_kv * DI;
+  u32x4 qb[4][KC];
+  int plim[4];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    const int64_t r = rw0 + ct * 16 + cl;
-    cvalid[ct] = wave_live && r < r_end;
-    const int t = cvalid[ct] ? (int)(r / h_kv) : 0;
-    plim[ct] = pos0 + t;
-    orow[ct] = bscore + ((int64_t)b * nrows + (cvalid[ct] ? r : 0)) * nblk;
+  for (int ct = 0; ct < 4; ++ct) {
+    const int64_t r = rw0 + ct * 32 + r32;
+    const bool valid = wave_live && r < r_end;
+    plim[ct] = valid ? pos0 + (int)(r / h_kv) : -1;      // -1: column never written
     const uint16_t* qr = q_idx + ((int64_t)b * nrows + r) * DI;
 #pragma unroll
-    for (int cc = 0; cc < CC; ++cc)
-      qb[ct][cc] = cvalid[ct] ? ld16(qr + cc * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int kc = 0; kc < KC; ++kc)
+      qb[ct][kc] = valid ? ld16(qr + kc * 16 + half * 8) : u32x4{0u, 0u, 0u, 0u};
   }
+  float* const orow = sm.o + (wave * kTiledColsPerWave + r32) * Smem::OS;   // + ct*32*OS
+  float* const grow = bscore + ((int64_t)b * nrows + rw0 + r32) * nblk;      // + ct*32*nblk
 
-  // Key block staging: each thread moves ITEMS 16-byte chunks.
+  // Key block staging: item i of this thread is key row key0 + i * KSTEP.
   constexpr int CHUNKS = kBlock * DI / 8;
   constexpr int ITEMS = CHUNKS / NT;
   static_assert(CHUNKS % NT == 0, "tile staging must divide evenly");
+  constexpr int KSTEP = NT / (DI / 8);
+  const uint16_t* kseq = k_idx + (int64_t)b * n_kv * DI;
+  const int skey0 = tid / (DI / 8);
+  const int goff0 = skey0 * DI + (tid % (DI / 8)) * 8;
+  const int loff0 = skey0 * Smem::S + (tid % (DI / 8)) * 8;
   u32x4 pre[ITEMS];
   auto fetch = [&](int j) {
+    const uint16_t* kb = kseq + (int64_t)j * kBlock * DI + goff0;
+    const int lim = n_kv - j * kBlock - skey0;
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int w = tid + i * NT;
-      const int key = w / (DI / 8), dc = w % (DI / 8);
-      const int s = j * kBlock + key;
-      pre[i] = (s < n_kv) ? ld16(kseq + (int64_t)s * DI + dc * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < ITEMS; ++i)
+      pre[i] = (i * KSTEP < lim) ? ld16(kb + i * KSTEP * DI) : u32x4{0u, 0u, 0u, 0u};
   };
-  auto stash = [&](KeyTile<DI>& t) {
+  auto stash = [&](uint16_t* t) {
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int w = tid + i * NT;
-      const int key = w / (DI / 8), dc = w % (DI / 8);
-      st16(&t.k[key * KeyTile<DI>::S + dc * 8], pre[i]);
-    }
+    for (int i = 0; i < ITEMS; ++i) st16(t + loff0 + i * KSTEP * Smem::S, pre[i]);
   };
 
   fetch(jb);
-  stash(tiles[0]);
+  stash(sm.k[0]);
   __syncthreads();
 
-  float wbuf[8];
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) wbuf[ct] = 0.f;
-
+  int jf = jb;                                           // first block of the group being buffered
   for (int j = jb; j < je; ++j) {
     const int cur = (j - jb) & 1;
     if (j + 1 < je) fetch(j + 1);
-    if (wave_live && j <= jw_max) {
-      const KeyTile<DI>& t = tiles[cur];
-      const bool need_mask = (j * kBlock + kBlock - 1) > (pos0 + tw0);
-      float rm[8];
+    const bool live = wave_live && j <= jw_max;
+    if (live) {
+      float rm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (j >= jw_mask)
+        score_block<DI, true>(sm.k[cur], qb, j * kBlock, plim, rm);
+      else
+        score_block<DI, false>(sm.k[cur], qb, j * kBlock, plim, rm);
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) rm[ct] = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        f32x4 acc[8];
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cc = 0; cc < CC; ++cc) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(&t.k[(kt * 16 + cl) * KeyTile<DI>::S + cc * 32 + q * 8]);
-#pragma unroll
-          for (int ct = 0; ct < 8; ++ct) acc[ct] = mfma_16x16x32(a, qb[ct][cc], acc[ct]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float v = acc[ct][r];
-            if (need_mask && (j * kBlock + kt * 16 + q * 4 + r) > plim[ct]) v = -INFINITY;
-            rm[ct] = fmaxf(rm[ct], v);
-          }
-      }
-      // Lane group q buffers block jb + 4n + q; every fourth block (or at the
-      // end) the four groups write four consecutive blocks of each row.
-      const int slot = (j - jb) & 3;
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const float m = colgroup_max(rm[ct]) + 0.0f;     // + 0 turns -0 into +0
-        if (slot == q) wbuf[ct] = m;
-      }
-      if (slot == 3 || j == je - 1 || j == jw_max) {
-        const int jj = j - slot + q;
-        if (jj <= j) {
-#pragma unroll
-          for (int ct = 0; ct < 8; ++ct)
-            if (cvalid[ct] && jj * kBlock <= plim[ct]) orow[ct][jj] = wbuf[ct];
-        }
+      for (int ct = 0; ct < 4; ++ct) {
+        const float m = vmax(rm[ct], shfl_xor_f(rm[ct], 32)) + 0.0f;   // + 0 turns -0 into +0
+        if (half == 0) orow[ct * 32 * Smem::OS + (j - jf)] = m;
       }
     }
-    if (j + 1 < je) stash(tiles[cur ^ 1]);
+    // Write out a full group (or the last one): lane half h writes entries
+    // jf + 8h .. jf + 8h + 7 of its rows, skipping blocks past the row's own.
+    if (live && (j - jf == kFlush - 1 || j == je - 1 || j == jw_max)) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int n = j - jf + 1;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int jl = plim[ct] >= 0 ? plim[ct] / kBlock : -1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int jj = half * 8 + e;
+          if (jj < n && jf + jj <= jl) grow[(int64_t)ct * 32 * nblk + jf + jj] = orow[ct * 32 * Smem::OS + jj];
+        }
+      }
+      jf = j + 1;
+    }
+    if (j + 1 < je) stash(sm.k[cur ^ 1]);
     __syncthreads();
   }
 }
@@ -209,7 +242,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void index_scores_skinny(
       for (int r = 0; r < 4; ++r) {
         float v = acc[r];
         if ((j * kBlock + kt * 16 + q * 4 + r) > plim) v = -INFINITY;
-        rm = fmaxf(rm, v);
+        rm = vmax(rm, v);
       }
     }
     rm = colgroup_max(rm) + 0.0f;
@@ -230,8 +263,19 @@ hipError_t launch_index_scores_t(const Dims& d, const uint16_t* q_idx, const uin
                        d.n_q, d.n_kv, d.pos0, d.h_kv, nblk);
   } else {
     const int jmax = (d.pos0 + d.n_q - 1) / kBlock;
-    const int bpc = jmax >= 512 ? 32 : (jmax >= 128 ? 16 : 4);
     const int64_t tiles = (nrows + kTiledRows - 1) / kTiledRows;
+    // Block iterations over all tiles (each tile needs blocks 0..its last
+    // token's block); chunks sized for about 1024 workgroups in total, in
+    // multiples of the write-out group.
+    int64_t iters = 0;
+    for (int64_t t = 0; t < tiles; ++t) {
+      const int64_t last_tok = (std::min<int64_t>((t + 1) * kTiledRows, nrows) - 1) / d.h_kv;
+      iters += (d.pos0 + last_tok) / kBlock + 1;
+    }
+    iters *= d.batch;
+    int64_t bpc64 = (iters + 1023) / 1024;
+    bpc64 = std::max<int64_t>(kFlush, (bpc64 + kFlush - 1) / kFlush * kFlush);
+    const int bpc = (int)std::min<int64_t>(bpc64, jmax + 1);
     dim3 grid((jmax + bpc) / bpc, (unsigned)tiles, d.batch);
     hipLaunchKernelGGL(index_scores_tiled<DI>, grid, dim3(kTiledWaves * 64), 0, stream, q_idx, k_idx, bscore,
                        d.n_q, d.n_kv, d.pos0, d.h_kv, nblk, bpc);

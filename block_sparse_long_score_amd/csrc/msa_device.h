@@ -22,6 +22,7 @@ namespace msa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
@@ -31,6 +32,14 @@ constexpr int kBlock = 128;   // KV block size B (tokens); the only size support
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_bf16: lane l supplies A[row = l % 32][k = 8*(l/32) .. +7]
+// and B[k = 8*(l/32) .. +7][col = l % 32]; accumulator element v of lane l is
+// D[row = 8*(v/4) + 4*(l/32) + v%4][col = l % 32].
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
@@ -51,10 +60,15 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
+// IEEE-754 maximum (NaN-propagating).  Lowers to v_maximum3_f32 on gfx950
+// without the canonicalising v_max_f32 x, x, x that fmaxf needs on every MFMA
+// result; inputs here are finite or -inf, so the NaN rule never matters.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max over the four lane groups (l/16) that share a column.
 __device__ __forceinline__ float colgroup_max(float v) {
-  v = fmaxf(v, shfl_xor_f(v, 16));
-  v = fmaxf(v, shfl_xor_f(v, 32));
+  v = vmax(v, shfl_xor_f(v, 16));
+  v = vmax(v, shfl_xor_f(v, 32));
   return v;
 }
 
@@ -197,13 +211,13 @@ __device__ __forceinline__ void block_scores_softmax(const KVTile<D>& t, const u
           if (key > plim[ct]) v = -INFINITY;
         }
         s[kt][ct][r] = v;
-        mx = fmaxf(mx, v);
+        mx = vmax(mx, v);
       }
     mx = colgroup_max(mx);
     bmax[ct] = mx;
     // Reference max for the exponentials: the block max, or (online softmax)
     // the caller's running max merged with it.
-    const float mr = use_mref ? fmaxf(mref[ct], mx) : mx;
+    const float mr = use_mref ? vmax(mref[ct], mx) : mx;
     mref[ct] = mr;
     float sum = 0.f;
 #pragma unroll
@@ -314,10 +328,10 @@ __device__ __forceinline__ void decode_attend(const uint16_t* __restrict__ qhead
         float v = sc[kt][r] * sl2;
         if (s0 + kt * 16 + q * 4 + r > plim) v = -INFINITY;
         sc[kt][r] = v;
-        mx = fmaxf(mx, v);
+        mx = vmax(mx, v);
       }
     mx = colgroup_max(mx);
-    const float m_new = fmaxf(m_run, mx);               // finite: the first block has key s0 <= plim
+    const float m_new = vmax(m_run, mx);               // finite: the first block has key s0 <= plim
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float sum = 0.f;
 #pragma unroll

@@ -190,13 +190,15 @@ __device__ __forceinline__ void block_scores_softmax(const KVTile<D>& t, const u
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) s[kt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int cc = 0; cc < D / 32; ++cc) {
+  for (int kt = 0; kt < 8; ++kt) {
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
+    for (int cc = 0; cc < D / 32; ++cc) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(&t.k[(kt * 16 + (lane & 15)) * KVTile<D>::KS + cc * 32 + q * 8]);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) s[kt][ct] = mfma_16x16x32(a, qb[ct][cc], s[kt][ct]);
     }
+    // keep the LDS operand reads of later key tiles from being hoisted (register pressure)
+    if (kt & 1) __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
@@ -247,6 +249,7 @@ __device__ __forceinline__ void block_pv(const KVTile<D>& t, const u32x4 (&pb)[2
   const int m = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int pp = 0; pp < D / 32; ++pp)
 #pragma unroll

@@ -109,7 +109,7 @@ __global__ void csr_fill(const int32_t* __restrict__ blk, const int* __restrict_
 // --------------------------------------------------------- KV-outer ---------
 
 template <int D, int LOG2G>
-__global__ __launch_bounds__(kAttnThreads) void sparse_kv_outer(
+__global__ __launch_bounds__(kAttnThreads, 2) void sparse_kv_outer(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int* __restrict__ cnt, const int* __restrict__ off, const int* __restrict__ item_off,
     const int* __restrict__ entries, uint16_t* __restrict__ part_o, float* __restrict__ part_ml, int n_q, int n_kv,
@@ -147,31 +147,49 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_kv_outer(
   const int ncols = E << LOG2G;
   const int ngroups = (ncols + 31) >> 5;
   const int q4 = lane >> 4;
-  for (int cg = wave; cg < ngroups; cg += kAttnThreads / 64) {
+  // Column (token, head) bookkeeping of one 32-column group.
+  struct Cols {
     const uint16_t* qrow[2];
     int plim[2];
-    bool valid[2];
     int64_t prow[2];
-    bool mask_any = false;
+    bool valid[2];
+    bool mask_any;
+  };
+  auto describe = [&](int cg, Cols& c) {
+    c.mask_any = false;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const int col = cg * 32 + ct * 16 + (lane & 15);
       const int e = col >> LOG2G, hh = col & (G - 1);
-      valid[ct] = e < E;
-      const int en = valid[ct] ? ent[e] : 0;
+      c.valid[ct] = e < E;
+      const int en = c.valid[ct] ? ent[e] : 0;
       const int t = en >> 5, slot = en & 31;
       const int p = pos0 + t;
-      qrow[ct] = valid[ct] ? q + (((int64_t)b * n_q + t) * h_q + g * G + hh) * D : nullptr;
-      plim[ct] = valid[ct] ? p : INT_MAX;
-      prow[ct] = ((((int64_t)b * n_q + t) * h_kv + g) * topk + slot) * G + hh;
-      mask_any |= valid[ct] && (p < s0 + kBlock - 1);
+      c.qrow[ct] = c.valid[ct] ? q + (((int64_t)b * n_q + t) * h_q + g * G + hh) * D : nullptr;
+      c.plim[ct] = c.valid[ct] ? p : INT_MAX;
+      c.prow[ct] = ((((int64_t)b * n_q + t) * h_kv + g) * topk + slot) * G + hh;
+      c.mask_any |= c.valid[ct] && (p < s0 + kBlock - 1);
     }
-    const bool need_mask = ballot(mask_any) != 0ull;
-    u32x4 qb[2][D / 32];
-    load_q_operand<D>(qb, qrow);
+  };
+  // The next group's queries are loaded while the current group computes.
+  Cols cur_c, nxt_c;
+  u32x4 qb[2][D / 32], qn[2][D / 32];
+  int cg = wave;
+  if (cg < ngroups) {
+    describe(cg, cur_c);
+    load_q_operand<D>(qb, cur_c.qrow);
+  }
+#pragma unroll 1
+  for (; cg < ngroups; cg += kAttnThreads / 64) {
+    const int cn = cg + kAttnThreads / 64;
+    if (cn < ngroups) {
+      describe(cn, nxt_c);
+      load_q_operand<D>(qn, nxt_c.qrow);
+    }
+    const bool need_mask = ballot(cur_c.mask_any) != 0ull;
     float bmax[2], bsum[2], mref[2] = {0.f, 0.f};
     u32x4 pb[2][4];
-    block_scores_softmax<D>(tile, qb, sl2, s0, plim, need_mask, bmax, bsum, pb, mref, false);
+    block_scores_softmax<D>(tile, qb, sl2, s0, cur_c.plim, need_mask, bmax, bsum, pb, mref, false);
     f32x4 acc[2][D / 32][2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
@@ -182,9 +200,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_kv_outer(
     block_pv<D>(tile, pb, acc);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      if (!valid[ct]) continue;
+      if (!cur_c.valid[ct]) continue;
       const float inv = 1.f / bsum[ct];
-      uint16_t* dst = part_o + prow[ct] * D;
+      uint16_t* dst = part_o + cur_c.prow[ct] * D;
 #pragma unroll
       for (int pp = 0; pp < D / 32; ++pp) {
         const f32x4 a0 = acc[ct][pp][0], a1 = acc[ct][pp][1];
@@ -193,10 +211,15 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_kv_outer(
         st16(dst + 32 * pp + 8 * q4, o);
       }
       if (q4 == 0) {
-        part_ml[2 * prow[ct]] = bmax[ct];
-        part_ml[2 * prow[ct] + 1] = bsum[ct];
+        part_ml[2 * cur_c.prow[ct]] = bmax[ct];
+        part_ml[2 * cur_c.prow[ct] + 1] = bsum[ct];
       }
     }
+    cur_c = nxt_c;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int cc = 0; cc < D / 32; ++cc) qb[ct][cc] = qn[ct][cc];
   }
 }
 

@@ -265,29 +265,54 @@ __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict
   const int h_kv = h_q / G;
   const int jl = (pos0 + t) / kBlock;
   const int64_t unit0 = (bt * h_kv + g) * nslot;
-  auto live = [&](int s) {
-    if (blk) {
-      const int j = blk[unit0 + s];
-      return j >= 0 && j <= jl;
-    }
-    return s * per <= jl;
-  };
+  const int32_t* brow = blk ? blk + unit0 : nullptr;
+  // Slots go in batches of 8 so each thread keeps 16 independent loads in
+  // flight.  Every slot is loaded (address clamped into the row) and dead ones
+  // are dropped with selects only: their memory may hold anything, and the
+  // branch-per-slot form of this loop was miscompiled by the gfx950 toolchain
+  // (wrong sums for rows with dead slots).
+  // Pass 1: the largest partial max.  Pass 2: weighted sum.
   float M = -INFINITY;
-  for (int s = 0; s < nslot; ++s)
-    if (live(s)) M = fmaxf(M, part_ml[2 * ((unit0 + s) * G + hh)]);
+  for (int s0 = 0; s0 < nslot; s0 += 8) {
+    float mv[8];
+    bool on[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = min(s0 + i, nslot - 1);
+      const int j = brow ? brow[s] : s * per;
+      on[i] = (s0 + i < nslot) && j >= 0 && j <= jl;
+      mv[i] = part_ml[2 * ((unit0 + s) * G + hh)];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) M = on[i] ? vmax(M, mv[i]) : M;
+  }
   float L = 0.f, acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int s = 0; s < nslot; ++s) {
-    if (!live(s)) continue;
-    const int64_t pr = (unit0 + s) * G + hh;
-    const float w = part_ml[2 * pr + 1] * __builtin_amdgcn_exp2f(part_ml[2 * pr] - M);
-    L += w;
-    const u32x4 o = ld16(part_o + pr * D + dl * 8);
+  for (int s0 = 0; s0 < nslot; s0 += 8) {
+    u32x4 o[8];
+    float w[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] = fmaf(w, bf16_to_f32(o[e] & 0xffffu), acc[2 * e]);
-      acc[2 * e + 1] = fmaf(w, bf16_to_f32(o[e] >> 16), acc[2 * e + 1]);
+    for (int i = 0; i < 8; ++i) {
+      const int s = min(s0 + i, nslot - 1);
+      const int j = brow ? brow[s] : s * per;
+      const bool on = (s0 + i < nslot) && j >= 0 && j <= jl;
+      const int64_t pr = (unit0 + s) * G + hh;
+      const float mm = part_ml[2 * pr], ll = part_ml[2 * pr + 1];
+      const u32x4 ov = ld16(part_o + pr * D + dl * 8);
+      const float ww = ll * __builtin_amdgcn_exp2f(mm - M);
+      w[i] = on ? ww : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[i][e] = on ? ov[e] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      L += w[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(w[i], bf16_to_f32(o[i][e] & 0xffffu), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(w[i], bf16_to_f32(o[i][e] >> 16), acc[2 * e + 1]);
+      }
     }
   }
   const float inv = 1.f / L;

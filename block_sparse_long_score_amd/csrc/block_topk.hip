@@ -60,24 +60,74 @@ __device__ __forceinline__ uint32_t kth_largest_all(const uint32_t (&key)[V], in
   return T;
 }
 
-// Write every key > T and the first `need` keys == T (block order) to out[0..).
-template <int V>
-__device__ __forceinline__ void emit_threshold(const uint32_t (&key)[V], uint32_t T, int need, int32_t* out) {
+// Exact top-kk of the keys a wave holds (element e = 64*i + lane, key 0 =
+// absent), ties to the lower element; sink(pos, key, e) receives the kk
+// winners in ascending element order, pos = 0..kk-1.  Needs kk <= #present.
+// cbuf: this wave's 64-entry LDS compaction buffer.
+template <int V, typename Sink>
+__device__ __forceinline__ void wave_select(const uint32_t (&key)[V], int kk, uint32_t* ck, int32_t* ci,
+                                            Sink sink) {
   const int lane = lane_id();
-  int base = 0, eqbase = 0;
+  auto emit_threshold = [&](uint32_t T, int need) {
+    int base = 0, eqbase = 0;
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const bool gt = key[i] > T, eq = key[i] == T;
-    const uint64_t eqm = ballot(eq);
-    const int er = eqbase + lanes_below(eqm);
-    eqbase += __popcll(eqm);
-    const bool sel = gt || (eq && er < need);
-    const uint64_t sm = ballot(sel);
-    if (sel) out[base + lanes_below(sm)] = i * 64 + lane;
-    base += __popcll(sm);
+    for (int i = 0; i < V; ++i) {
+      const bool gt = key[i] > T, eq = key[i] == T;
+      const uint64_t eqm = ballot(eq);
+      const int er = eqbase + lanes_below(eqm);
+      eqbase += __popcll(eqm);
+      const bool sel = gt || (eq && er < need);
+      const uint64_t sm = ballot(sel);
+      if (sel) sink(base + lanes_below(sm), key[i], i * 64 + lane);
+      base += __popcll(sm);
+    }
+  };
+  uint32_t lm = 0u;
+#pragma unroll
+  for (int i = 0; i < V; ++i) lm = max(lm, key[i]);
+  const uint32_t T0 = kth_largest_wave(lm, kk);
+  int c_gt = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) c_gt += __popcll(ballot(key[i] > T0));
+  if (c_gt < kk) {                                     // case 2: threshold is T0
+    emit_threshold(T0, kk - c_gt);
+    return;
   }
+  if (c_gt <= 64) {                                    // case 3: compact the keys > T0
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const bool gt = key[i] > T0;
+      const uint64_t m = ballot(gt);
+      if (gt) {
+        const int pos = base + lanes_below(m);
+        ck[pos] = key[i];
+        ci[pos] = i * 64 + lane;
+      }
+      base += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t my = lane < c_gt ? ck[lane] : 0u;
+    const int32_t myi = lane < c_gt ? ci[lane] : 0;
+    const uint32_t T = kth_largest_wave(my, kk);
+    const int n_gt = __popcll(ballot(my > T));
+    const uint64_t eqm = ballot(my == T);
+    const bool sel = my > T || (my == T && lanes_below(eqm) < kk - n_gt);
+    const uint64_t sm = ballot(sel);
+    if (sel) sink(lanes_below(sm), my, myi);
+    return;
+  }
+  // case 4
+  const uint32_t T = kth_largest_all<V>(key, kk);
+  int n_gt = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) n_gt += __popcll(ballot(key[i] > T));
+  emit_threshold(T, kk - n_gt);
 }
 
+// One wave per (query, group) row; rows of up to 64*V candidates.
 template <int V>
 __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* __restrict__ bscore,
                                                                    int32_t* __restrict__ blk, int n_q, int pos0,
@@ -97,58 +147,89 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* 
   const int kk = topk - 1;
   if (lane == 0) out[kk] = jl;                         // the local block is the largest index
   if (kk == 0) return;
-
   const float* sc = bscore + row * nblk;
   const int n = jl;                                    // candidates 0..jl-1, n > kk
   uint32_t key[V];
-  uint32_t lm = 0u;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int e = i * 64 + lane;
     key[i] = (e < n) ? order_key(sc[e]) : 0u;          // 0 is below every finite key
-    lm = max(lm, key[i]);
   }
-  const uint32_t T0 = kth_largest_wave(lm, kk);
-  int c_gt = 0;
-#pragma unroll
-  for (int i = 0; i < V; ++i) c_gt += __popcll(ballot(key[i] > T0));
+  wave_select<V>(key, kk, ck[wave], ci[wave], [&](int pos, uint32_t, int e) { out[pos] = e; });
+}
 
-  if (c_gt < kk) {                                     // case 2: threshold is T0
-    emit_threshold<V>(key, T0, kk - c_gt, out);
+// Long rows (up to 256*V candidates): a workgroup per row.  Wave w selects the
+// exact top-kk of its contiguous quarter [w*n/4, (w+1)*n/4) into LDS; the
+// quarters are in block order, so wave 0's exact top-kk over the (at most 4*kk)
+// survivors, ties broken by position, is the row's answer.
+constexpr int kWgWaves = 4;
+template <int V>
+__global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __restrict__ bscore,
+                                                               int32_t* __restrict__ blk, int n_q, int pos0,
+                                                               int h_kv, int nblk, int topk) {
+  __shared__ uint32_t ck[kWgWaves][64];
+  __shared__ int32_t ci[kWgWaves][64];
+  __shared__ uint32_t cand_k[kWgWaves][32];
+  __shared__ int32_t cand_i[kWgWaves][32];
+  __shared__ int cand_n[kWgWaves];
+  __shared__ uint32_t cat_k[kWgWaves * 32];
+  __shared__ int32_t cat_i[kWgWaves * 32];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = blockIdx.x;
+  const int t = (int)((row / h_kv) % n_q);
+  const int jl = (pos0 + t) / kBlock;
+  int32_t* out = blk + row * topk;
+  if (jl + 1 <= topk) {                                // whole workgroup leaves together
+    for (int i = threadIdx.x; i < topk; i += kWgWaves * 64) out[i] = (i <= jl) ? i : -1;
     return;
   }
-  if (c_gt <= 64) {                                    // case 3: compact the keys > T0
-    int base = 0;
+  const int kk = topk - 1;
+  if (threadIdx.x == 0) out[kk] = jl;
+  if (kk == 0) return;
+  const float* sc = bscore + row * nblk;
+  const int n = jl;
+  const int q0 = (int)((int64_t)n * wave / kWgWaves), q1 = (int)((int64_t)n * (wave + 1) / kWgWaves);
+  const int nq = q1 - q0;
+  if (nq <= kk) {                                      // the whole quarter survives
+    for (int e = lane; e < nq; e += 64) {
+      cand_k[wave][e] = order_key(sc[q0 + e]);
+      cand_i[wave][e] = q0 + e;
+    }
+    if (lane == 0) cand_n[wave] = nq;
+  } else {
+    uint32_t key[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const bool gt = key[i] > T0;
-      const uint64_t m = ballot(gt);
-      if (gt) {
-        const int pos = base + lanes_below(m);
-        ck[wave][pos] = key[i];
-        ci[wave][pos] = i * 64 + lane;
-      }
-      base += __popcll(m);
+      const int e = i * 64 + lane;
+      key[i] = (e < nq) ? order_key(sc[q0 + e]) : 0u;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint32_t my = lane < c_gt ? ck[wave][lane] : 0u;
-    const int32_t myi = lane < c_gt ? ci[wave][lane] : 0;
-    const uint32_t T = kth_largest_wave(my, kk);
-    const int n_gt = __popcll(ballot(my > T));
-    const uint64_t eqm = ballot(my == T);
-    const bool sel = my > T || (my == T && lanes_below(eqm) < kk - n_gt);
-    const uint64_t sm = ballot(sel);
-    if (sel) out[lanes_below(sm)] = myi;
-    return;
+    wave_select<V>(key, kk, ck[wave], ci[wave], [&](int pos, uint32_t k, int e) {
+      cand_k[wave][pos] = k;
+      cand_i[wave][pos] = q0 + e;
+    });
+    if (lane == 0) cand_n[wave] = kk;
   }
-  // case 4
-  const uint32_t T = kth_largest_all<V>(key, kk);
-  int n_gt = 0;
+  __syncthreads();
+  // Concatenate the quarters' survivors in block order into cat_*.
+  int start = 0, total = 0;
 #pragma unroll
-  for (int i = 0; i < V; ++i) n_gt += __popcll(ballot(key[i] > T));
-  emit_threshold<V>(key, T, kk - n_gt, out);
+  for (int w = 0; w < kWgWaves; ++w) {
+    if (w < wave) start += cand_n[w];
+    total += cand_n[w];
+  }
+  for (int e = lane; e < cand_n[wave]; e += 64) {
+    cat_k[start + e] = cand_k[wave][e];
+    cat_i[start + e] = cand_i[wave][e];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  uint32_t key[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = i * 64 + lane;
+    key[i] = c < total ? cat_k[c] : 0u;
+  }
+  wave_select<2>(key, kk, ck[0], ci[0], [&](int pos, uint32_t, int c) { out[pos] = cat_i[c]; });
 }
 
 template <int V>
@@ -157,6 +238,14 @@ hipError_t launch_v(const Dims& d, const float* bscore, int32_t* blk, hipStream_
   const int64_t wgs = (nrows + kRowsPerWg - 1) / kRowsPerWg;
   hipLaunchKernelGGL(block_topk_rows<V>, dim3((unsigned)wgs), dim3(kRowsPerWg * 64), 0, stream, bscore, blk,
                      d.n_q, d.pos0, d.h_kv, d.nblk(), d.topk, nrows);
+  return hipGetLastError();
+}
+
+template <int V>
+hipError_t launch_wg(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
+  const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
+  hipLaunchKernelGGL(block_topk_wg<V>, dim3((unsigned)nrows), dim3(kWgWaves * 64), 0, stream, bscore, blk, d.n_q,
+                     d.pos0, d.h_kv, d.nblk(), d.topk);
   return hipGetLastError();
 }
 
@@ -171,8 +260,10 @@ hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk, h
   if (per_lane <= 8) return launch_v<8>(d, bscore, blk, stream);
   if (per_lane <= 16) return launch_v<16>(d, bscore, blk, stream);
   if (per_lane <= 32) return launch_v<32>(d, bscore, blk, stream);
-  if (per_lane <= 64) return launch_v<64>(d, bscore, blk, stream);
-  return launch_v<128>(d, bscore, blk, stream);         // the C-ABI caps nblk at 8192
+  // longer rows: a workgroup per row, a quarter row per wave
+  const int per_lane_q = ((jl_max + kWgWaves - 1) / kWgWaves + 63) / 64;
+  if (per_lane_q <= 16) return launch_wg<16>(d, bscore, blk, stream);
+  return launch_wg<32>(d, bscore, blk, stream);         // the C-ABI caps nblk at 8192
 }
 
 }  // namespace msa

@@ -163,3 +163,25 @@ def test_block_topk_entry_matches_oracle_selection():
             for gg in range(s.h_kv):
                 want = O.select_blocks(sc[b, t, gg, : jl + 1], jl, s.topk)
                 assert (got[b, t, gg] == want).all(), (b, t, gg)
+
+
+@pytest.mark.parametrize("jl_span,topk", [((1048000, 1048575), 16), ((300000, 300127), 32), ((1040000, 1040200), 1)])
+def test_block_topk_long_rows_workgroup_path(jl_span, topk):
+    """Rows longer than 2,048 candidates take the workgroup-per-row kernel
+    (quarters selected separately, then merged); heavy ties on every row."""
+    lo, hi = jl_span
+    n_kv = 1048576
+    s = Shape(1, hi - lo, n_kv, lo, 8, 4, 128, 128, topk=topk)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(78 + topk)
+    bscore = torch.randint(-3, 4, (s.batch, s.n_q, s.h_kv, s.nblk), generator=g, device="cuda").float()
+    blk = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.int32, device="cuda")
+    from block_sparse_long_score_amd import msa as M
+    M.msa_block_topk(s, bscore, blk)
+    got = blk.cpu().numpy()
+    sc = bscore.cpu().numpy().astype(np.float64)
+    for t in range(0, s.n_q, max(1, s.n_q // 40)):
+        jl = (s.pos0 + t) // s.block
+        for gg in range(s.h_kv):
+            want = O.select_blocks(sc[0, t, gg, : jl + 1], jl, s.topk)
+            assert (got[0, t, gg] == want).all(), (t, gg, got[0, t, gg], want)

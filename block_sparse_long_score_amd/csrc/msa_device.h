@@ -95,23 +95,34 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
 }
 
 // ---------------------------------------------------------------------------
-// One KV block of one K/V head staged in LDS.
-//   k  : [128 keys][D + 8]   row-major, padded so 16-byte MFMA operand reads of
-//        16 consecutive rows fall in distinct banks.
-//   vt : [D][128 + 8]        V transposed (d-major), so an MFMA operand that
-//        needs 8 keys at a fixed d is two 8-byte LDS reads.
+// One KV block of one K/V head staged in LDS, rows 16-byte aligned and
+// unpadded; 16-byte chunks are XOR-swizzled per row (chunk c of row r sits at
+// c ^ tile_swz(r)) so that every staging write and operand read below touches
+// each bank the minimum number of times.
+//   k  : [128 keys][D]       row-major.
+//   vt : [D][128 keys]       V transposed (d-major): the P*V operand of 8
+//                            consecutive keys at a fixed d is one chunk.
+// Key order inside the score tiles: MFMA row m of key tile kt holds key
+//   kt_key(kt, m) = 32*(kt/2) + 8*(m/4) + 4*(kt%2) + m%4,
+// so lane group q of a column ends up with keys 32*kc + 8*q + [0, 8) in the two
+// tiles 2*kc, 2*kc+1 -- exactly one chunk of a vt row.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int kt_key(int kt, int m) { return 32 * (kt >> 1) + 8 * (m >> 2) + 4 * (kt & 1) + (m & 3); }
+__device__ __forceinline__ int tile_swz(int r) { return (((r >> 3) & 3) << 2) | (r & 3); }
+
 template <int D>
 struct KVTile {
-  static constexpr int KS = D + 8;
-  static constexpr int VS = kBlock + 8;
-  uint16_t k[kBlock * KS];
-  uint16_t vt[D * VS];
+  static constexpr int DC = D / 8;          // 16-byte chunks per K row
+  uint16_t k[kBlock * D];
+  uint16_t vt[D * kBlock];
+  __device__ __forceinline__ const uint16_t* k_chunk(int row, int c) const {
+    return &k[row * D + 8 * (c ^ (tile_swz(row) & (DC - 1)))];
+  }
+  __device__ __forceinline__ const uint16_t* vt_chunk(int d, int c) const {
+    return &vt[d * kBlock + 8 * (c ^ tile_swz(d))];
+  }
 };
 
-// Stage keys [s0, s0 + 128) of one K/V head into LDS; rows at or past n_kv are
-// zero-filled.  kbase/vbase point at token 0 of the sequence for this head;
-// row_stride is the distance between consecutive tokens in elements (h_kv * D).
 template <int D, int NT>
 __device__ __forceinline__ void stage_kv_block(KVTile<D>& t, const uint16_t* __restrict__ kbase,
                                                const uint16_t* __restrict__ vbase, int64_t row_stride,
@@ -123,25 +134,28 @@ __device__ __forceinline__ void stage_kv_block(KVTile<D>& t, const uint16_t* __r
     const int s = s0 + key;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (s < n_kv) val = ld16(kbase + (int64_t)s * row_stride + dc * 8);
-    st16(&t.k[key * KVTile<D>::KS + dc * 8], val);
+    st16(&t.k[key * D + 8 * (dc ^ (tile_swz(key) & (DC - 1)))], val);
   }
-  // V: four consecutive keys x 8 dims per work item, transposed into vt.
-  for (int w = tid; w < (kBlock / 4) * DC; w += NT) {
-    const int kq = w / DC, dc = w % DC;
-    u32x4 r[4];
+  __builtin_amdgcn_sched_barrier(0);
+  // V: an 8-key x 8-dim tile per work item (16 lanes read one 256-byte row),
+  // transposed in registers into 8 rows of 8 keys.
+  for (int w = tid; w < (kBlock / 8) * DC; w += NT) {
+    const int kg = w / DC, dg = w % DC;
+    u32x4 r[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = s0 + kq * 4 + i;
-      r[i] = (s < n_kv) ? ld16(vbase + (int64_t)s * row_stride + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 8; ++i) {
+      const int s = s0 + kg * 8 + i;
+      r[i] = (s < n_kv) ? ld16(vbase + (int64_t)s * row_stride + dg * 8) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // element e of each of the 4 rows -> one 8-byte write vt[dc*8+e][kq*4 .. +3]
       const int word = e >> 1, sh = (e & 1) * 16;
-      const uint32_t x0 = (r[0][word] >> sh) & 0xffffu, x1 = (r[1][word] >> sh) & 0xffffu;
-      const uint32_t x2 = (r[2][word] >> sh) & 0xffffu, x3 = (r[3][word] >> sh) & 0xffffu;
-      u32x2 pk = {x0 | (x1 << 16), x2 | (x3 << 16)};
-      *reinterpret_cast<u32x2*>(&t.vt[(dc * 8 + e) * KVTile<D>::VS + kq * 4]) = pk;
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = ((r[2 * j][word] >> sh) & 0xffffu) | (((r[2 * j + 1][word] >> sh) & 0xffffu) << 16);
+      const int d = dg * 8 + e;
+      st16(&t.vt[d * kBlock + 8 * (kg ^ tile_swz(d))], o);
     }
   }
 }
@@ -193,7 +207,7 @@ __device__ __forceinline__ void block_scores_softmax(const KVTile<D>& t, const u
   for (int kt = 0; kt < 8; ++kt) {
 #pragma unroll
     for (int cc = 0; cc < D / 32; ++cc) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&t.k[(kt * 16 + (lane & 15)) * KVTile<D>::KS + cc * 32 + q * 8]);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(t.k_chunk(kt_key(kt, lane & 15), 4 * cc + q));
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) s[kt][ct] = mfma_16x16x32(a, qb[ct][cc], s[kt][ct]);
     }
@@ -208,10 +222,7 @@ __device__ __forceinline__ void block_scores_softmax(const KVTile<D>& t, const u
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = s[kt][ct][r] * sl2;
-        if (need_mask) {
-          const int key = s0 + kt * 16 + q * 4 + r;
-          if (key > plim[ct]) v = -INFINITY;
-        }
+        if (need_mask && s0 + kt_key(kt, 4 * q + r) > plim[ct]) v = -INFINITY;
         s[kt][ct][r] = v;
         mx = vmax(mx, v);
       }
@@ -241,7 +252,8 @@ __device__ __forceinline__ void block_scores_softmax(const KVTile<D>& t, const u
 }
 
 // acc[ct][pp][half] += V^T * P^T for the block.  acc rows are permuted so that
-// lane group q ends up holding d = 32*pp + 8*q + 4*half + r.
+// lane group q ends up holding d = 32*pp + 8*q + 4*half + r; the contraction
+// slots of lane group q are keys 32*kc + 8*q + [0, 8) on both operands.
 template <int D>
 __device__ __forceinline__ void block_pv(const KVTile<D>& t, const u32x4 (&pb)[2][4],
                                          f32x4 (&acc)[2][D / 32][2]) {
@@ -255,10 +267,7 @@ __device__ __forceinline__ void block_pv(const KVTile<D>& t, const u32x4 (&pb)[2
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
         const int d = 32 * pp + 8 * (m >> 2) + 4 * hlf + (m & 3);
-        const uint16_t* row = &t.vt[d * KVTile<D>::VS + 32 * kc + 4 * q];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        const u32x4 a = *reinterpret_cast<const u32x4*>(t.vt_chunk(d, 4 * kc + q));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) acc[ct][pp][hlf] = mfma_16x16x32(a, pb[ct][kc], acc[ct][pp][hlf]);
       }

@@ -19,6 +19,8 @@
 //     index-key streaming: every wave pulls its key blocks straight from HBM into
 //     MFMA A operands (no LDS round trip), bound by HBM bandwidth.
 #include <algorithm>
+#include <atomic>
+#include <cmath>
 
 #include "launch.h"
 #include "msa_device.h"
@@ -83,25 +85,27 @@ __device__ __forceinline__ void score_block(const uint16_t* __restrict__ kt_lds,
   reduce(acc[1], 15);
 }
 
+// Number of KV blocks row tile t of a sequence needs: blocks 0 .. the block of
+// the tile's last token.
+__device__ __host__ __forceinline__ int tile_blocks(int t, int64_t nrows, int h_kv, int pos0) {
+  const int64_t end = (int64_t)(t + 1) * kTiledRows;
+  const int64_t last_row = (end < nrows ? end : nrows) - 1;
+  return (pos0 + (int)(last_row / h_kv)) / kBlock + 1;
+}
+
+// One segment: row tile `tile` of sequence b against key blocks [jb, je).
+// Double-buffered key staging through LDS with one barrier per block; pooled
+// maxima collect in LDS per wave and go out in groups of kFlush blocks.
 template <int DI>
-__global__ __launch_bounds__(kTiledWaves * 64) void index_scores_tiled(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, float* __restrict__ bscore,
-    int n_q, int n_kv, int pos0, int h_kv, int nblk, int blocks_per_chunk) {
+__device__ __forceinline__ void tiled_segment(IndexSmem<DI>& sm, const uint16_t* __restrict__ q_idx,
+                                              const uint16_t* __restrict__ k_idx, float* __restrict__ bscore, int b,
+                                              int tile, int jb, int je, int n_kv, int pos0, int h_kv, int nblk,
+                                              int64_t nrows) {
   constexpr int KC = DI / 16;                            // 16-wide contraction chunks
   constexpr int NT = kTiledWaves * 64;
   using Smem = IndexSmem<DI>;
-  __shared__ Smem sm;
-
-  const int b = blockIdx.z;
-  const int64_t nrows = (int64_t)n_q * h_kv;
-  // Latest (longest) row tiles are dispatched first, so the short ones fill the tail.
-  const int64_t r0 = (int64_t)(gridDim.y - 1 - blockIdx.y) * kTiledRows;
+  const int64_t r0 = (int64_t)tile * kTiledRows;
   const int64_t r_end = min(r0 + (int64_t)kTiledRows, nrows);
-  const int t_last = (int)((r_end - 1) / h_kv);
-  const int jmax = (pos0 + t_last) / kBlock;
-  const int jb = blockIdx.x * blocks_per_chunk;
-  if (jb > jmax) return;
-  const int je = min(jb + blocks_per_chunk, jmax + 1);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -173,6 +177,9 @@ __global__ __launch_bounds__(kTiledWaves * 64) void index_scores_tiled(
         if (half == 0) orow[ct * 32 * Smem::OS + (j - jf)] = m;
       }
     }
+    // The next key block goes to LDS before any pooled stores are issued, so
+    // the wait for its loads never includes the stores of a write-out.
+    if (j + 1 < je) stash(sm.k[cur ^ 1]);
     // Write out a full group (or the last one): lane half h writes entries
     // jf + 8h .. jf + 8h + 7 of its rows, skipping blocks past the row's own.
     if (live && (j - jf == kFlush - 1 || j == je - 1 || j == jw_max)) {
@@ -191,8 +198,37 @@ __global__ __launch_bounds__(kTiledWaves * 64) void index_scores_tiled(
       }
       jf = j + 1;
     }
-    if (j + 1 < je) stash(sm.k[cur ^ 1]);
     __syncthreads();
+  }
+}
+
+// Work decomposition.  Row tile t of a sequence needs blocks 0 .. ~t, so tile
+// t is paired with tile T-1-t: every pair needs nearly the same number of
+// block iterations.  Each pair's iterations (the long tile's blocks, then the
+// short tile's) are cut into `pieces` equal ranges, one workgroup each, so all
+// workgroups carry equal work whatever XCD and CU they land on.  A range spans
+// at most the two tiles of its pair.
+template <int DI>
+__global__ __launch_bounds__(kTiledWaves * 64) void index_scores_tiled(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, float* __restrict__ bscore,
+    int n_q, int n_kv, int pos0, int h_kv, int nblk, int tiles, int pairs, int pieces) {
+  __shared__ IndexSmem<DI> sm;
+  const int64_t nrows = (int64_t)n_q * h_kv;
+  const int w = blockIdx.x;
+  const int k = w % pieces;
+  const int p = (w / pieces) % pairs;
+  const int b = w / (pieces * pairs);
+  const int ta = tiles - 1 - p, tb = p;                  // long tile, short tile (ta == tb: unpaired middle)
+  const int na = tile_blocks(ta, nrows, h_kv, pos0);
+  const int nb = ta != tb ? tile_blocks(tb, nrows, h_kv, pos0) : 0;
+  const int total = na + nb;                             // <= 2 * 8192 blocks, so total * pieces fits an int
+  const int lo = total * k / pieces, hi = total * (k + 1) / pieces;
+#pragma nounroll
+  for (int seg = 0; seg < 2; ++seg) {
+    const int tile = __builtin_amdgcn_readfirstlane(seg == 0 ? ta : tb);
+    const int jb = __builtin_amdgcn_readfirstlane(seg == 0 ? lo : max(lo, na) - na);
+    const int je = __builtin_amdgcn_readfirstlane(seg == 0 ? min(hi, na) : hi - na);
+    if (jb < je) tiled_segment<DI>(sm, q_idx, k_idx, bscore, b, tile, jb, je, n_kv, pos0, h_kv, nblk, nrows);
   }
 }
 
@@ -250,6 +286,44 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void index_scores_skinny(
   }
 }
 
+// Compute units of the current device (cached per device id).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Pieces per tile pair.  Workgroups carry equal work, so the launch runs in
+// ceil(W / slots) rounds of whole workgroups; the choice trades the idle part
+// of the last round against the fixed cost of each piece (query operand load
+// and pipeline fill, about kPieceCost block iterations).
+int choose_pieces(int64_t units, double pair_iters, int64_t slots) {
+  constexpr double kPieceCost = 4.0;
+  const int kmax = (int)std::max<double>(1.0, std::min<double>(1024.0, pair_iters));
+  int best = 1;
+  double best_score = -1.0;
+  for (int k = 1; k <= kmax; ++k) {
+    const double w = (double)units * k;
+    const double rounds = std::ceil(w / (double)slots);
+    const double fill = w / (rounds * (double)slots);
+    const double len = pair_iters / k;
+    const double score = fill * len / (len + kPieceCost);
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = k;
+    }
+  }
+  return best;
+}
+
 template <int DI>
 hipError_t launch_index_scores_t(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,
                                  hipStream_t stream) {
@@ -262,23 +336,15 @@ hipError_t launch_index_scores_t(const Dims& d, const uint16_t* q_idx, const uin
     hipLaunchKernelGGL(index_scores_skinny<DI>, grid, dim3(kSkinnyWaves * 64), 0, stream, q_idx, k_idx, bscore,
                        d.n_q, d.n_kv, d.pos0, d.h_kv, nblk);
   } else {
-    const int jmax = (d.pos0 + d.n_q - 1) / kBlock;
     const int64_t tiles = (nrows + kTiledRows - 1) / kTiledRows;
-    // Block iterations over all tiles (each tile needs blocks 0..its last
-    // token's block); chunks sized for about 1024 workgroups in total, in
-    // multiples of the write-out group.
-    int64_t iters = 0;
-    for (int64_t t = 0; t < tiles; ++t) {
-      const int64_t last_tok = (std::min<int64_t>((t + 1) * kTiledRows, nrows) - 1) / d.h_kv;
-      iters += (d.pos0 + last_tok) / kBlock + 1;
-    }
-    iters *= d.batch;
-    int64_t bpc64 = (iters + 1023) / 1024;
-    bpc64 = std::max<int64_t>(kFlush, (bpc64 + kFlush - 1) / kFlush * kFlush);
-    const int bpc = (int)std::min<int64_t>(bpc64, jmax + 1);
-    dim3 grid((jmax + bpc) / bpc, (unsigned)tiles, d.batch);
+    const int64_t pairs = (tiles + 1) / 2;
+    int64_t iters = 0;                                   // block iterations over all tiles of a sequence
+    for (int64_t t = 0; t < tiles; ++t) iters += tile_blocks((int)t, nrows, d.h_kv, d.pos0);
+    const int64_t slots = (int64_t)device_cu_count();    // one resident workgroup per CU (LDS-bound)
+    const int pieces = choose_pieces(pairs * d.batch, (double)iters / pairs, slots);
+    dim3 grid((unsigned)(d.batch * pairs * pieces));
     hipLaunchKernelGGL(index_scores_tiled<DI>, grid, dim3(kTiledWaves * 64), 0, stream, q_idx, k_idx, bscore,
-                       d.n_q, d.n_kv, d.pos0, d.h_kv, nblk, bpc);
+                       d.n_q, d.n_kv, d.pos0, d.h_kv, nblk, (int)tiles, (int)pairs, pieces);
   }
   return hipGetLastError();
 }

@@ -17,8 +17,8 @@ struct Dims {
 // Sparse-prefill workspace: CSR inversion of the block selection plus the
 // per-(query, group, slot) partial softmax results.  Offsets in bytes.
 struct PrefillWs {
-  size_t cnt, off, item_off, cursor, entries, part_o, part_ml, total;
-  int64_t lists, entries_max, items_max;
+  size_t cnt, off, item_off, ccnt, entries, part_o, part_ml, total;
+  int64_t lists, chunks, entries_max, items_max;
 };
 PrefillWs prefill_ws_layout(const Dims& d);
 

@@ -16,6 +16,7 @@
 //
 // Decode streams the <= k selected blocks of each (sequence, group) straight
 // from HBM, one wave per block, and merges the same way.
+#include <algorithm>
 #include <climits>
 
 #include "launch.h"
@@ -30,23 +31,69 @@ constexpr int kAttnThreads = 256;
 int64_t prefill_entries_max(const Dims& d) { return (int64_t)d.batch * d.n_q * d.h_kv * d.topk; }
 
 // ---------------------------------------------------------------- CSR --------
+//
+// The selection is inverted per (b, g, token chunk): one workgroup counts, in
+// an LDS histogram over the blocks, how often each block was selected by the
+// chunk's tokens, and later places the chunk's entries through LDS cursors.
+// Global memory sees one count per (chunk, list) instead of one atomic per
+// selection, and each list comes out ordered by token chunk.
 
-__global__ void fill_zero_i32(int* __restrict__ a, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) a[i] = 0;
+constexpr int kCsrThreads = 256;
+constexpr int kCsrMaxBlocks = 8192;                    // nblk <= 8192 (n_kv <= 1M)
+constexpr int kCsrTargetWgs = 1024;
+
+// Token chunks per (b, g): enough workgroups to fill the chip.
+int csr_chunks(const Dims& d) {
+  const int64_t bg = (int64_t)d.batch * d.h_kv;
+  if (bg <= 0 || d.n_q <= 0) return 1;
+  int64_t c = (kCsrTargetWgs + bg - 1) / bg;
+  c = std::max<int64_t>(1, std::min<int64_t>(c, d.n_q));
+  const int64_t tc = (d.n_q + c - 1) / c;
+  return (int)((d.n_q + tc - 1) / tc);
 }
 
-__global__ void csr_count(const int32_t* __restrict__ blk, int* __restrict__ cnt, int64_t nent, int n_q, int h_kv,
-                          int topk, int nblk, int pos0) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nent) return;
-  const int j = blk[i];
-  const int64_t row = i / topk;                        // (b * n_q + t) * h_kv + g
-  const int t = (int)((row / h_kv) % n_q);
-  if (j < 0 || j > (pos0 + t) / kBlock) return;        // padding, or not a causal block
-  const int g = (int)(row % h_kv);
-  const int b = (int)(row / ((int64_t)h_kv * n_q));
-  atomicAdd(&cnt[((int64_t)b * h_kv + g) * nblk + j], 1);
+// Selected, causal block of entry (t, slot) or -1.
+__device__ __forceinline__ int entry_block(const int32_t* __restrict__ blk, int64_t row, int slot, int topk, int t,
+                                           int pos0) {
+  const int j = blk[row * topk + slot];
+  return (j >= 0 && j <= (pos0 + t) / kBlock) ? j : -1;
+}
+
+// ccnt[(b, g, c)][j] = number of tokens of chunk c (of sequence b, group g)
+// that selected block j.
+__global__ __launch_bounds__(kCsrThreads) void csr_count_chunks(const int32_t* __restrict__ blk,
+                                                                int* __restrict__ ccnt, int n_q, int h_kv, int topk,
+                                                                int nblk, int pos0, int tc, int chunks) {
+  __shared__ int hist[kCsrMaxBlocks];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int t0 = c * tc, t1 = min(n_q, t0 + tc);
+  for (int j = threadIdx.x; j < nblk; j += kCsrThreads) hist[j] = 0;
+  __syncthreads();
+  const int n = (t1 - t0) * topk;
+  for (int k = threadIdx.x; k < n; k += kCsrThreads) {
+    const int t = t0 + k / topk, slot = k % topk;
+    const int j = entry_block(blk, ((int64_t)b * n_q + t) * h_kv + g, slot, topk, t, pos0);
+    if (j >= 0) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  int* dst = ccnt + (((int64_t)b * h_kv + g) * chunks + c) * nblk;
+  for (int j = threadIdx.x; j < nblk; j += kCsrThreads) dst[j] = hist[j];
+}
+
+// Per list (b, g, j): ccnt over the chunks becomes its exclusive prefix, and
+// cnt[list] the list's size.
+__global__ void csr_chunk_scan(int* __restrict__ ccnt, int* __restrict__ cnt, int lists, int chunks, int nblk) {
+  const int list = blockIdx.x * blockDim.x + threadIdx.x;
+  if (list >= lists) return;
+  const int bg = list / nblk, j = list % nblk;
+  int* col = ccnt + (int64_t)bg * chunks * nblk + j;
+  int run = 0;
+  for (int c = 0; c < chunks; ++c) {
+    const int v = col[(int64_t)c * nblk];
+    col[(int64_t)c * nblk] = run;
+    run += v;
+  }
+  cnt[list] = run;
 }
 
 // One workgroup: exclusive scans of the list sizes and of their item counts.
@@ -89,21 +136,27 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan(const int* __restrict__
   }
 }
 
-__global__ void csr_fill(const int32_t* __restrict__ blk, const int* __restrict__ off, int* __restrict__ cursor,
-                         int* __restrict__ entries, int64_t nent, int n_q, int h_kv, int topk, int nblk, int pos0) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nent) return;
-  const int j = blk[i];
-  const int64_t row = i / topk;
-  const int slot = (int)(i % topk);
-  const int g = (int)(row % h_kv);
-  const int64_t bt = row / h_kv;
-  const int t = (int)(bt % n_q);
-  if (j < 0 || j > (pos0 + t) / kBlock) return;
-  const int b = (int)(bt / n_q);
-  const int64_t list = ((int64_t)b * h_kv + g) * nblk + j;
-  const int pos = off[list] + atomicAdd(&cursor[list], 1);
-  entries[pos] = (t << 5) | slot;                      // slot < 32, t < 2^26
+// Entries of chunk c go to off[list] + (prefix of earlier chunks) + a rank
+// taken from an LDS cursor, so lists are ordered by chunk (ranks inside a
+// chunk follow the LDS atomics and do not affect any result).
+__global__ __launch_bounds__(kCsrThreads) void csr_fill_chunks(const int32_t* __restrict__ blk,
+                                                               const int* __restrict__ off,
+                                                               const int* __restrict__ ccnt,
+                                                               int* __restrict__ entries, int n_q, int h_kv, int topk,
+                                                               int nblk, int pos0, int tc, int chunks) {
+  __shared__ int cur[kCsrMaxBlocks];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int t0 = c * tc, t1 = min(n_q, t0 + tc);
+  const int* pre = ccnt + (((int64_t)b * h_kv + g) * chunks + c) * nblk;
+  const int* loff = off + ((int64_t)b * h_kv + g) * nblk;
+  for (int j = threadIdx.x; j < nblk; j += kCsrThreads) cur[j] = loff[j] + pre[j];
+  __syncthreads();
+  const int n = (t1 - t0) * topk;
+  for (int k = threadIdx.x; k < n; k += kCsrThreads) {
+    const int t = t0 + k / topk, slot = k % topk;
+    const int j = entry_block(blk, ((int64_t)b * n_q + t) * h_kv + g, slot, topk, t, pos0);
+    if (j >= 0) entries[atomicAdd(&cur[j], 1)] = (t << 5) | slot;   // slot < 32, t < 2^26
+  }
 }
 
 // --------------------------------------------------------- KV-outer ---------
@@ -343,22 +396,22 @@ hipError_t launch_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k,
   int* cnt = reinterpret_cast<int*>(base + L.cnt);
   int* off = reinterpret_cast<int*>(base + L.off);
   int* item_off = reinterpret_cast<int*>(base + L.item_off);
-  int* cursor = reinterpret_cast<int*>(base + L.cursor);
+  int* ccnt = reinterpret_cast<int*>(base + L.ccnt);
   int* entries = reinterpret_cast<int*>(base + L.entries);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
   const int nblk = d.nblk();
-  const int64_t nent = L.entries_max;
   const int lists = (int)L.lists;
-  hipLaunchKernelGGL(fill_zero_i32, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream, cnt, (int64_t)lists);
-  hipLaunchKernelGGL(fill_zero_i32, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream, cursor,
-                     (int64_t)lists);
-  const unsigned egrid = (unsigned)((nent + 255) / 256);
-  hipLaunchKernelGGL(csr_count, dim3(egrid), dim3(256), 0, stream, blk, cnt, nent, d.n_q, d.h_kv, d.topk, nblk,
-                     d.pos0);
+  const int chunks = (int)L.chunks;
+  const int tc = (d.n_q + chunks - 1) / chunks;
+  const dim3 cgrid((unsigned)chunks, (unsigned)d.h_kv, (unsigned)d.batch);
+  hipLaunchKernelGGL(csr_count_chunks, cgrid, dim3(kCsrThreads), 0, stream, blk, ccnt, d.n_q, d.h_kv, d.topk, nblk,
+                     d.pos0, tc, chunks);
+  hipLaunchKernelGGL(csr_chunk_scan, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream, ccnt, cnt, lists,
+                     chunks, nblk);
   hipLaunchKernelGGL(csr_scan, dim3(1), dim3(kScanThreads), 0, stream, cnt, off, item_off, lists, kEntriesPerItem);
-  hipLaunchKernelGGL(csr_fill, dim3(egrid), dim3(256), 0, stream, blk, off, cursor, entries, nent, d.n_q, d.h_kv,
-                     d.topk, nblk, d.pos0);
+  hipLaunchKernelGGL(csr_fill_chunks, cgrid, dim3(kCsrThreads), 0, stream, blk, off, ccnt, entries, d.n_q, d.h_kv,
+                     d.topk, nblk, d.pos0, tc, chunks);
   hipLaunchKernelGGL((sparse_kv_outer<D, LOG2G>), dim3((unsigned)L.items_max), dim3(kAttnThreads), 0, stream, q, k,
                      v, cnt, off, item_off, entries, part_o, part_ml, d.n_q, d.n_kv, d.pos0, d.h_q, d.h_kv, nblk,
                      d.topk, lists, sl2);
@@ -415,7 +468,8 @@ PrefillWs prefill_ws_layout(const Dims& d) {
   L.cnt = take(sizeof(int) * L.lists);
   L.off = take(sizeof(int) * (L.lists + 1));
   L.item_off = take(sizeof(int) * (L.lists + 1));
-  L.cursor = take(sizeof(int) * L.lists);
+  L.chunks = csr_chunks(d);
+  L.ccnt = take(sizeof(int) * (size_t)L.lists * L.chunks);
   L.entries = take(sizeof(int) * L.entries_max);
   L.part_o = take((size_t)L.entries_max * d.group() * d.d * 2);
   L.part_ml = take((size_t)L.entries_max * d.group() * 2 * sizeof(float));

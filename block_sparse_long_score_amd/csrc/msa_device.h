@@ -47,11 +47,12 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 pair, packed low|high (hardware convert).
+// Round-to-nearest-even fp32 -> bf16 pair, packed low|high: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
@@ -214,19 +215,26 @@ __device__ __forceinline__ void block_scores_softmax(const KVTile<D>& t, const u
     // keep the LDS operand reads of later key tiles from being hoisted (register pressure)
     if (kt & 1) __builtin_amdgcn_sched_barrier(0);
   }
+  // Causal mask (only blocks that reach past some column's position).
+  if (need_mask) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (s0 + kt_key(kt, 4 * q + r) > plim[ct]) s[kt][ct][r] = -INFINITY;
+  }
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
+    // The max of the raw scores times sl2 > 0 is the max of the rounded scaled
+    // scores (rounding is monotone), so one FMA per score forms the exponent.
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = s[kt][ct][r] * sl2;
-        if (need_mask && s0 + kt_key(kt, 4 * q + r) > plim[ct]) v = -INFINITY;
-        s[kt][ct][r] = v;
-        mx = vmax(mx, v);
-      }
-    mx = colgroup_max(mx);
+      for (int r = 0; r < 4; ++r) mx = vmax(mx, s[kt][ct][r]);
+    mx = colgroup_max(mx) * sl2;
     bmax[ct] = mx;
     // Reference max for the exponentials: the block max, or (online softmax)
     // the caller's running max merged with it.
@@ -240,7 +248,7 @@ __device__ __forceinline__ void block_scores_softmax(const KVTile<D>& t, const u
       for (int hlf = 0; hlf < 2; ++hlf)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[2 * kc + hlf][ct][r] - mr);
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[2 * kc + hlf][ct][r], sl2, -mr));
           p[hlf * 4 + r] = e;
           sum += e;
         }
@@ -283,9 +291,9 @@ __device__ __forceinline__ void block_pv(const KVTile<D>& t, const u32x4 (&pb)[2
 // streams with 16-byte loads into a VALU accumulation.  pt is this wave's LDS
 // scratch of kBlock * 16 + 16 floats (probabilities and per-head rescales).
 //
-// Writes the normalised partial o (bf16, [G][D]) and (m2, l) per head, where
-// m2 is the running max of the scaled logits in log2 units and l the sum of
-// exp2(logit2 - m2).  Keys past plim (the query position) are masked.
+// Writes the unnormalised partial o = sum exp2(logit2 - m2) * v (bf16, [G][D])
+// and (m2, l) per head, where m2 is the running max of the scaled logits in
+// log2 units and l the sum of exp2(logit2 - m2).  Keys past plim (the query position) are masked.
 // ---------------------------------------------------------------------------
 template <int D, int G>
 __device__ __forceinline__ void decode_attend(const uint16_t* __restrict__ qheads,
@@ -417,10 +425,9 @@ __device__ __forceinline__ void decode_attend(const uint16_t* __restrict__ qhead
   if (kg == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float inv = 1.f / alpha_s[h];
       u32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[h][2 * e] * inv, acc[h][2 * e + 1] * inv);
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[h][2 * e], acc[h][2 * e + 1]);
       st16(out_o + h * D + dl * 8, o);
     }
   }

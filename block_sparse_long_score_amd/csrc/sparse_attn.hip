@@ -9,9 +9,10 @@
 // kernel): the selection blk_idx[b][t][g][slot] is inverted into per-(b, g,
 // block) lists of (t, slot); one workgroup stages a 128-token K/V block of one
 // K/V head in LDS once and runs every (query token x group head) column that
-// selected it through MFMA, writing one normalised partial (o, m, l) per
-// (t, g, slot, head).  A merge kernel then combines the <= k partials of each
-// (t, head) with log-sum-exp weights.  Every partial is computed from its own
+// selected it through MFMA, writing one partial (o, m, l) per
+// (t, g, slot, head): o unnormalised (sum of exp2(logit2 - m) * v, bf16), m
+// and l.  A merge kernel then combines the <= k partials of each (t, head)
+// with log-sum-exp weights.  Every partial is computed from its own
 // column only, so the order of a list never changes a result bit.
 //
 // Decode streams the <= k selected blocks of each (sequence, group) straight
@@ -254,13 +255,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_kv_outer(
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       if (!cur_c.valid[ct]) continue;
-      const float inv = 1.f / bsum[ct];
       uint16_t* dst = part_o + cur_c.prow[ct] * D;
 #pragma unroll
       for (int pp = 0; pp < D / 32; ++pp) {
         const f32x4 a0 = acc[ct][pp][0], a1 = acc[ct][pp][1];
-        u32x4 o = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
-                   pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
+        u32x4 o = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
+                   pack_bf16x2(a1[2], a1[3])};
         st16(dst + 32 * pp + 8 * q4, o);
       }
       if (q4 == 0) {
@@ -300,7 +300,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_decode_blocks(
 
 // Slot s of a row takes part when it holds a result: for the sparse paths when
 // blk[.., s] is a block index in [0, jl]; for split dense decode (blk == nullptr)
-// when s * per <= jl.
+// when s * per <= jl.  With M the largest partial max and w_s = exp2(m_s - M):
+// out = sum_s w_s o_s / sum_s w_s l_s  (o_s unnormalised), lse = ln2 (M + log2 L).
 template <int D>
 __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int s0 = 0; s0 < nslot; s0 += 8) {
     u32x4 o[8];
-    float w[8];
+    float w[8], wl[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int s = min(s0 + i, nslot - 1);
@@ -353,14 +354,15 @@ __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict
       const int64_t pr = (unit0 + s) * G + hh;
       const float mm = part_ml[2 * pr], ll = part_ml[2 * pr + 1];
       const u32x4 ov = ld16(part_o + pr * D + dl * 8);
-      const float ww = ll * __builtin_amdgcn_exp2f(mm - M);
+      const float ww = __builtin_amdgcn_exp2f(mm - M);
       w[i] = on ? ww : 0.f;
+      wl[i] = on ? ww * ll : 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[i][e] = on ? ov[e] : 0u;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      L += w[i];
+      L += wl[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc[2 * e] = fmaf(w[i], bf16_to_f32(o[i][e] & 0xffffu), acc[2 * e]);

@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-topk-compare", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -104,16 +106,42 @@ def decode_bytes(s) -> float:
     return float(kidx + kv + small)
 
 
+# ----------------------------------------------------------- HBM traffic --
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch (read + written) from the committed counter
+    summary, or None when there is none for this kernel and workload or the
+    kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    from block_sparse_long_score_amd.profiling import kernel_sources_sha256
+    e = rec.get(kernel, {}).get(workload)
+    if not e or e.get("sources_sha256") != kernel_sources_sha256(kernel):
+        return None
+    return float(e["read_bytes"] + e["write_bytes"])
+
+
 # ------------------------------------------------------------------ timing --
 
-def time_calls(torch, fns, steps, warmup):
+def time_calls(torch, fns, steps, warmup, M=None):
     """Run the list of zero-argument launches `fns` as one step; returns the
     mean per-step wall time (events around the whole timed region) and the mean
-    time of each launch (events between launches) in milliseconds."""
+    time of each launch (events between launches) in milliseconds.  With the
+    binding module M, the library's own per-kernel timing (HIP event pairs
+    around each kernel on its stream) runs over the timed region and the
+    per-kernel totals are returned as a third value."""
     for _ in range(warmup):
         for f in fns:
             f()
     torch.cuda.synchronize()
+    if M is not None:
+        M.msa_profile_begin()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -126,8 +154,11 @@ def time_calls(torch, fns, steps, warmup):
             ev[i][j + 1].record()
     end.record()
     torch.cuda.synchronize()
+    kernels = M.msa_profile_end() if M is not None else None
     total = start.elapsed_time(end) / steps
     per = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps for j in range(len(fns))]
+    if M is not None:
+        return total, per, kernels
     return total, per
 
 
@@ -185,6 +216,16 @@ def main():
     from block_sparse_long_score_amd import msa as M
     from block_sparse_long_score_amd.inputs import WORKLOADS, make_inputs
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
+
     M.lib()                                            # fail loudly if the HIP library is missing
     if not torch.cuda.is_available():
         log("no GPU visible")
@@ -206,7 +247,7 @@ def main():
         lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
     ]
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms_step, (ms_idx, ms_topk, ms_sparse) = time_calls(torch, stages, args.steps, args.warmup)
+    ms_step, (ms_idx, ms_topk, ms_sparse), kern = time_calls(torch, stages, args.steps, args.warmup, M)
     tokens = s.batch * s.n_q
     value = tokens / (ms_step * 1e-3)
     f_idx, f_sp = index_flops(s), sparse_flops(s)
@@ -222,12 +263,28 @@ def main():
     }
     for v in per_stage.values():
         v["frac"] = v["achieved"] / v["peak"]
-    # The index scoring stage is a single kernel launch, so its event time is
-    # that kernel's duration; it is the roofline reported.
-    dom = per_stage["index_scores"]
-    roofline = {"kernel": "index_scores_tiled", "bound": "mfma", "achieved": dom["achieved"], "peak": dom["peak"],
-                "unit": "TFLOP/s", "frac": dom["frac"], "traffic": None,
-                "algorithmic_per_launch": f_idx, "avg_launch_ms": ms_idx}
+    # Per-kernel device times from the library's event pairs over the timed
+    # region; the roofline is reported for the kernel with the largest total.
+    kernels = {name: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / args.steps}
+               for name, (n, tot) in kern.items()}
+    algorithmic = {   # kernel -> (bound, algorithmic work of one launch, peak, unit scale, unit)
+        "index_scores_tiled": ("mfma", f_idx, PEAK_BF16_FLOPS, 1e12, "TFLOP/s"),
+        "sparse_kv_outer": ("mfma", f_sp, PEAK_BF16_FLOPS, 1e12, "TFLOP/s"),
+        "block_topk_rows": ("hbm", topk_bytes(s), PEAK_HBM_BYTES, 1e9, "GB/s"),
+        "block_topk_wg": ("hbm", topk_bytes(s), PEAK_HBM_BYTES, 1e9, "GB/s"),
+    }
+    dom_name = max(kern, key=lambda n: kern[n][1])
+    if dom_name not in algorithmic:
+        raise RuntimeError(f"no algorithmic work defined for the dominant kernel {dom_name}")
+    bound, work, peak, scale, unit = algorithmic[dom_name]
+    avg = kernels[dom_name]["avg_ms"]
+    achieved = work / (avg * 1e-3)
+    roofline = {"kernel": dom_name, "bound": bound, "achieved": achieved / scale, "peak": peak / scale,
+                "unit": unit, "frac": achieved / peak,
+                "traffic": measured_traffic(dom_name, args.workload),
+                "algorithmic_per_launch": work, "avg_launch_ms": avg}
+    log(f"dominant kernel {dom_name}: {avg:.3f} ms per launch, {achieved / scale:.1f} {unit} "
+        f"({achieved / peak:.1%} of peak)")
 
     result = {
         "metric": METRIC,
@@ -246,6 +303,7 @@ def main():
                    "h_q": s.h_q, "h_kv": s.h_kv, "d": s.d, "d_idx": s.d_idx, "block": s.block, "topk": s.topk},
         "roofline": roofline,
         "stages": per_stage,
+        "kernels": kernels,
         "end_to_end_mfma_frac": (f_idx + f_sp) / (ms_step * 1e-3) / PEAK_BF16_FLOPS,
     }
 
@@ -287,16 +345,26 @@ def main():
         dout = torch.empty((ds.batch, 1, ds.h_q, ds.d), dtype=torch.bfloat16, device=dev)
         dlse = torch.empty((ds.batch, 1, ds.h_q), dtype=torch.float32, device=dev)
         dsteps = max(args.steps, 20)
-        ms_dec, (ms_di, ms_ds) = time_calls(torch, [
+        dec_calls = [
             lambda: M.msa_index_topk(ds, dinp["q_idx"], dinp["k_idx"], dblk, dws_i),
             lambda: M.msa_sparse_decode(ds, dinp["q"], dinp["k"], dinp["v"], dblk, dout, dlse, dws_s),
-        ], dsteps, args.warmup)
+        ]
+        ms_dec, (ms_di, ms_ds) = time_calls(torch, dec_calls, dsteps, args.warmup)
+        # Per-kernel times from a second pass: event records would weigh on
+        # these sub-millisecond steps, so they stay out of the timed one.
+        _, _, dkern = time_calls(torch, dec_calls, dsteps, 1, M)
         by = decode_bytes(ds)
+        kidx_bytes = float(ds.batch * ds.n_kv * ds.d_idx * 2)
         dec = {"workload": args.decode_workload, "batch": ds.batch, "n_kv": ds.n_kv, "steps": dsteps,
                "ms_per_step": ms_dec, "tok_s": ds.batch / (ms_dec * 1e-3),
                "index_topk_ms": ms_di, "sparse_decode_ms": ms_ds,
                "algorithmic_bytes": by, "hbm_gbs": by / (ms_dec * 1e-3) / 1e9,
-               "hbm_frac": by / (ms_dec * 1e-3) / PEAK_HBM_BYTES}
+               "hbm_frac": by / (ms_dec * 1e-3) / PEAK_HBM_BYTES,
+               "kernels": {name: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / dsteps}
+                           for name, (n, tot) in dkern.items()}}
+        if "index_scores_skinny" in dkern:
+            n, tot = dkern["index_scores_skinny"]
+            dec["index_scores_skinny_hbm_frac"] = kidx_bytes / (tot / n * 1e-3) / PEAK_HBM_BYTES
         log(f"decode step {ms_dec:.3f} ms ({ms_di:.3f} index top-k + {ms_ds:.3f} sparse) -> "
             f"{dec['tok_s']:.4g} tok/s, {dec['hbm_frac'] * 100:.1f}% of HBM peak")
         if not args.no_dense:

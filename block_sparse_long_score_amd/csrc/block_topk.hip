@@ -236,16 +236,22 @@ template <int V>
 hipError_t launch_v(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
   const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
   const int64_t wgs = (nrows + kRowsPerWg - 1) / kRowsPerWg;
-  hipLaunchKernelGGL(block_topk_rows<V>, dim3((unsigned)wgs), dim3(kRowsPerWg * 64), 0, stream, bscore, blk,
-                     d.n_q, d.pos0, d.h_kv, d.nblk(), d.topk, nrows);
+  {
+    LaunchTimer timer("block_topk_rows", stream);
+    hipLaunchKernelGGL(block_topk_rows<V>, dim3((unsigned)wgs), dim3(kRowsPerWg * 64), 0, stream, bscore, blk,
+                       d.n_q, d.pos0, d.h_kv, d.nblk(), d.topk, nrows);
+  }
   return hipGetLastError();
 }
 
 template <int V>
 hipError_t launch_wg(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
   const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
-  hipLaunchKernelGGL(block_topk_wg<V>, dim3((unsigned)nrows), dim3(kWgWaves * 64), 0, stream, bscore, blk, d.n_q,
-                     d.pos0, d.h_kv, d.nblk(), d.topk);
+  {
+    LaunchTimer timer("block_topk_wg", stream);
+    hipLaunchKernelGGL(block_topk_wg<V>, dim3((unsigned)nrows), dim3(kWgWaves * 64), 0, stream, bscore, blk, d.n_q,
+                       d.pos0, d.h_kv, d.nblk(), d.topk);
+  }
   return hipGetLastError();
 }
 

@@ -135,8 +135,11 @@ hipError_t prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k, const 
                      uint16_t* out, float* lse, hipStream_t stream) {
   constexpr int TQ = kColsPerWg >> LOG2G;
   dim3 grid((d.n_q + TQ - 1) / TQ, d.h_kv, d.batch);
-  hipLaunchKernelGGL((dense_prefill<D, LOG2G>), grid, dim3(kThreads), 0, stream, q, k, v, out, lse, d.n_q, d.n_kv,
-                     d.pos0, d.h_q, d.h_kv, sl2);
+  {
+    LaunchTimer timer("dense_prefill", stream);
+    hipLaunchKernelGGL((dense_prefill<D, LOG2G>), grid, dim3(kThreads), 0, stream, q, k, v, out, lse, d.n_q, d.n_kv,
+                       d.pos0, d.h_q, d.h_kv, sl2);
+  }
   return hipGetLastError();
 }
 
@@ -148,8 +151,11 @@ hipError_t decode_t(const Dims& d, const uint16_t* q, const uint16_t* k, const u
   uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
   const int64_t units = (int64_t)d.batch * d.h_kv * L.nslot;
-  hipLaunchKernelGGL((dense_decode_chunks<D, G>), dim3((unsigned)((units + 3) / 4)), dim3(kThreads), 0, stream, q,
-                     k, v, part_o, part_ml, d.n_kv, d.pos0, d.h_q, d.h_kv, L.nslot, units, sl2);
+  {
+    LaunchTimer timer("dense_decode_chunks", stream);
+    hipLaunchKernelGGL((dense_decode_chunks<D, G>), dim3((unsigned)((units + 3) / 4)), dim3(kThreads), 0, stream, q,
+                       k, v, part_o, part_ml, d.n_kv, d.pos0, d.h_q, d.h_kv, L.nslot, units, sl2);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_merge(d, part_o, part_ml, nullptr, out, lse, L.nslot, kChunkBlocks, stream);

@@ -333,8 +333,11 @@ hipError_t launch_index_scores_t(const Dims& d, const uint16_t* q_idx, const uin
     const int jmax = (d.pos0 + d.n_q - 1) / kBlock;
     const int per_wg = kSkinnyWaves * kSkinnyBlocksPerWave;
     dim3 grid((jmax + per_wg) / per_wg, d.batch);
-    hipLaunchKernelGGL(index_scores_skinny<DI>, grid, dim3(kSkinnyWaves * 64), 0, stream, q_idx, k_idx, bscore,
-                       d.n_q, d.n_kv, d.pos0, d.h_kv, nblk);
+    {
+      LaunchTimer timer("index_scores_skinny", stream);
+      hipLaunchKernelGGL(index_scores_skinny<DI>, grid, dim3(kSkinnyWaves * 64), 0, stream, q_idx, k_idx, bscore,
+                         d.n_q, d.n_kv, d.pos0, d.h_kv, nblk);
+    }
   } else {
     const int64_t tiles = (nrows + kTiledRows - 1) / kTiledRows;
     const int64_t pairs = (tiles + 1) / 2;
@@ -343,8 +346,11 @@ hipError_t launch_index_scores_t(const Dims& d, const uint16_t* q_idx, const uin
     const int64_t slots = (int64_t)device_cu_count();    // one resident workgroup per CU (LDS-bound)
     const int pieces = choose_pieces(pairs * d.batch, (double)iters / pairs, slots);
     dim3 grid((unsigned)(d.batch * pairs * pieces));
-    hipLaunchKernelGGL(index_scores_tiled<DI>, grid, dim3(kTiledWaves * 64), 0, stream, q_idx, k_idx, bscore,
-                       d.n_q, d.n_kv, d.pos0, d.h_kv, nblk, (int)tiles, (int)pairs, pieces);
+    {
+      LaunchTimer timer("index_scores_tiled", stream);
+      hipLaunchKernelGGL(index_scores_tiled<DI>, grid, dim3(kTiledWaves * 64), 0, stream, q_idx, k_idx, bscore,
+                         d.n_q, d.n_kv, d.pos0, d.h_kv, nblk, (int)tiles, (int)pairs, pieces);
+    }
   }
   return hipGetLastError();
 }

@@ -8,6 +8,22 @@
 
 namespace msa {
 
+// Kernel timing hook (msa_profile_begin / msa_profile_end): constructed right
+// before a launch, destroyed right after it; records a HIP event pair around
+// the launch on its stream while recording is on, and does nothing otherwise.
+class LaunchTimer {
+ public:
+  LaunchTimer(const char* name, hipStream_t stream);
+  ~LaunchTimer();
+  LaunchTimer(const LaunchTimer&) = delete;
+  LaunchTimer& operator=(const LaunchTimer&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr;
+};
+
 struct Dims {
   int batch, n_q, n_kv, pos0, h_q, h_kv, d, d_idx, block, topk;
   int nblk() const { return (n_kv + block - 1) / block; }

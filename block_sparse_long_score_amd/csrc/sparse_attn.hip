@@ -384,8 +384,11 @@ hipError_t launch_merge_t(const Dims& d, const uint16_t* part_o, const float* pa
   const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_q;
   const int rows_per_wg = 256 / (D / 8);
   const int64_t wgs = (nrows + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(merge_partials<D>, dim3((unsigned)wgs), dim3(256), 0, stream, part_o, part_ml, blk, out, lse,
-                     nrows, d.n_q, d.pos0, d.h_q, d.group(), nslot, per);
+  {
+    LaunchTimer timer("merge_partials", stream);
+    hipLaunchKernelGGL(merge_partials<D>, dim3((unsigned)wgs), dim3(256), 0, stream, part_o, part_ml, blk, out, lse,
+                       nrows, d.n_q, d.pos0, d.h_q, d.group(), nslot, per);
+  }
   return hipGetLastError();
 }
 
@@ -407,16 +410,31 @@ hipError_t launch_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k,
   const int chunks = (int)L.chunks;
   const int tc = (d.n_q + chunks - 1) / chunks;
   const dim3 cgrid((unsigned)chunks, (unsigned)d.h_kv, (unsigned)d.batch);
-  hipLaunchKernelGGL(csr_count_chunks, cgrid, dim3(kCsrThreads), 0, stream, blk, ccnt, d.n_q, d.h_kv, d.topk, nblk,
-                     d.pos0, tc, chunks);
-  hipLaunchKernelGGL(csr_chunk_scan, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream, ccnt, cnt, lists,
-                     chunks, nblk);
-  hipLaunchKernelGGL(csr_scan, dim3(1), dim3(kScanThreads), 0, stream, cnt, off, item_off, lists, kEntriesPerItem);
-  hipLaunchKernelGGL(csr_fill_chunks, cgrid, dim3(kCsrThreads), 0, stream, blk, off, ccnt, entries, d.n_q, d.h_kv,
-                     d.topk, nblk, d.pos0, tc, chunks);
-  hipLaunchKernelGGL((sparse_kv_outer<D, LOG2G>), dim3((unsigned)L.items_max), dim3(kAttnThreads), 0, stream, q, k,
-                     v, cnt, off, item_off, entries, part_o, part_ml, d.n_q, d.n_kv, d.pos0, d.h_q, d.h_kv, nblk,
-                     d.topk, lists, sl2);
+  {
+    LaunchTimer timer("csr_count_chunks", stream);
+    hipLaunchKernelGGL(csr_count_chunks, cgrid, dim3(kCsrThreads), 0, stream, blk, ccnt, d.n_q, d.h_kv, d.topk, nblk,
+                       d.pos0, tc, chunks);
+  }
+  {
+    LaunchTimer timer("csr_chunk_scan", stream);
+    hipLaunchKernelGGL(csr_chunk_scan, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream, ccnt, cnt, lists,
+                       chunks, nblk);
+  }
+  {
+    LaunchTimer timer("csr_scan", stream);
+    hipLaunchKernelGGL(csr_scan, dim3(1), dim3(kScanThreads), 0, stream, cnt, off, item_off, lists, kEntriesPerItem);
+  }
+  {
+    LaunchTimer timer("csr_fill_chunks", stream);
+    hipLaunchKernelGGL(csr_fill_chunks, cgrid, dim3(kCsrThreads), 0, stream, blk, off, ccnt, entries, d.n_q, d.h_kv,
+                       d.topk, nblk, d.pos0, tc, chunks);
+  }
+  {
+    LaunchTimer timer("sparse_kv_outer", stream);
+    hipLaunchKernelGGL((sparse_kv_outer<D, LOG2G>), dim3((unsigned)L.items_max), dim3(kAttnThreads), 0, stream, q, k,
+                       v, cnt, off, item_off, entries, part_o, part_ml, d.n_q, d.n_kv, d.pos0, d.h_q, d.h_kv, nblk,
+                       d.topk, lists, sl2);
+  }
   return launch_merge_t<D>(d, part_o, part_ml, blk, out, lse, d.topk, 1, stream);
 }
 
@@ -429,8 +447,11 @@ hipError_t launch_decode_t(const Dims& d, const uint16_t* q, const uint16_t* k, 
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
   const int64_t units = (int64_t)d.batch * d.h_kv * d.topk;
   const int64_t wgs = (units + 3) / 4;
-  hipLaunchKernelGGL((sparse_decode_blocks<D, G>), dim3((unsigned)wgs), dim3(kAttnThreads), 0, stream, q, k, v, blk,
-                     part_o, part_ml, d.n_kv, d.pos0, d.h_q, d.h_kv, d.topk, units, sl2);
+  {
+    LaunchTimer timer("sparse_decode_blocks", stream);
+    hipLaunchKernelGGL((sparse_decode_blocks<D, G>), dim3((unsigned)wgs), dim3(kAttnThreads), 0, stream, q, k, v, blk,
+                       part_o, part_ml, d.n_kv, d.pos0, d.h_q, d.h_kv, d.topk, units, sl2);
+  }
   return launch_merge_t<D>(d, part_o, part_ml, blk, out, lse, d.topk, 1, stream);
 }
 

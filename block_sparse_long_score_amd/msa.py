@@ -43,6 +43,8 @@ EXPORTED = (
     "msa_sparse_prefill",
     "msa_sparse_decode",
     "msa_dense_gqa",
+    "msa_profile_begin",
+    "msa_profile_end",
 )
 
 
@@ -56,6 +58,10 @@ class MsaError(RuntimeError):
 class MsaDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "n_q", "n_kv", "pos0", "h_q", "h_kv", "d", "d_idx", "block", "topk")]
+
+
+class MsaKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
 def dims_of(s: Shape) -> MsaDims:
@@ -85,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.msa_sparse_prefill.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
     L.msa_sparse_decode.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
     L.msa_dense_gqa.argtypes = [D, P, P, P, F, P, P, P, S, VP]
+    L.msa_profile_begin.argtypes = []
+    L.msa_profile_end.argtypes = [ctypes.POINTER(MsaKernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     for fn in EXPORTED[2:]:
         getattr(L, fn).restype = I32
     _lib = L
@@ -206,3 +214,16 @@ def msa_dense_gqa(s: Shape, q, k, v, out, lse=None, workspace=None, scale: float
     st = lib().msa_dense_gqa(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), ctypes.c_float(scale), _ptr(out),
                              _ptr(lse), wp, wb, _stream(stream))
     _raise(st, "msa_dense_gqa")
+
+
+def msa_profile_begin() -> None:
+    """Start per-kernel timing: every library launch gets a HIP event pair on its stream."""
+    _raise(lib().msa_profile_begin(), "msa_profile_begin")
+
+
+def msa_profile_end(capacity: int = 64) -> dict:
+    """Stop per-kernel timing; returns {kernel name: (launches, total device ms)}."""
+    buf = (MsaKernelTime * capacity)()
+    n = ctypes.c_int32(0)
+    _raise(lib().msa_profile_end(buf, capacity, ctypes.byref(n)), "msa_profile_end")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n.value, capacity))}

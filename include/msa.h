@@ -156,6 +156,32 @@ msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint
 msa_status msa_dense_gqa(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v, float scale,
                          uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, msa_stream stream);
 
+
+/* Kernel timing (a profiling aid, not part of the computation).  Between
+ * msa_profile_begin and msa_profile_end every kernel the library launches is
+ * bracketed by two HIP events recorded on the launch's own stream, so each
+ * duration is that kernel's execution on the device.  msa_profile_end waits
+ * for the recorded events, sums the durations per kernel name, stops
+ * recording and releases the events.  msa_profile_begin creates a pool of
+ * 4096 HIP events on the host (no device memory; more are created if a run
+ * records over 2048 launches) and returns MSA_ERR_HIP if it cannot; recording
+ * adds two event records to the stream per launch, so leave it off outside
+ * measurements.  Not thread-safe against concurrent begin/end calls; launches
+ * from several threads are recorded safely.
+ *   out       array of `capacity` entries, filled with the kernels in order of
+ *             decreasing total time (may be NULL when capacity is 0)
+ *   count     out: number of distinct kernels recorded (may exceed capacity)
+ * Returns MSA_ERR_NULL for a NULL count, MSA_ERR_HIP if an event call fails
+ * (recording is stopped and the events released either way). */
+typedef struct {
+  char name[64];      /* kernel function name, without template arguments */
+  int32_t launches;   /* launches recorded */
+  double total_ms;    /* summed device time */
+} msa_kernel_time;
+
+msa_status msa_profile_begin(void);
+msa_status msa_profile_end(msa_kernel_time* out, int32_t capacity, int32_t* count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -286,20 +286,6 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void index_scores_skinny(
   }
 }
 
-// Compute units of the current device (cached per device id).
-int device_cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 // Pieces per tile pair.  Workgroups carry equal work, so the launch runs in
 // ceil(W / slots) rounds of whole workgroups; the choice trades the idle part

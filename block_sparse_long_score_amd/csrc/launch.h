@@ -24,6 +24,9 @@ class LaunchTimer {
   hipEvent_t start_ = nullptr;
 };
 
+// Compute units of the current device (cached per device id; 256 if the query fails).
+int device_cu_count();
+
 struct Dims {
   int batch, n_q, n_kv, pos0, h_q, h_kv, d, d_idx, block, topk;
   int nblk() const { return (n_kv + block - 1) / block; }
@@ -33,8 +36,8 @@ struct Dims {
 // Sparse-prefill workspace: CSR inversion of the block selection plus the
 // per-(query, group, slot) partial softmax results.  Offsets in bytes.
 struct PrefillWs {
-  size_t cnt, off, item_off, ccnt, entries, part_o, part_ml, total;
-  int64_t lists, chunks, entries_max, items_max;
+  size_t cnt, off, ccnt, entries, part_o, part_ml, total;
+  int64_t lists, chunks, entries_max;
 };
 PrefillWs prefill_ws_layout(const Dims& d);
 

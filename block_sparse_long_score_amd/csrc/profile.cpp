@@ -1,5 +1,6 @@
-// Kernel timing hook: HIP event pairs around every library launch while
-// recording is on (msa_profile_begin / msa_profile_end in include/msa.h).
+// Host-side runtime helpers: the kernel timing hook (HIP event pairs around
+// every library launch while recording is on; msa_profile_begin /
+// msa_profile_end in include/msa.h) and the device's compute-unit count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -62,6 +63,21 @@ LaunchTimer::~LaunchTimer() {
   if (!stop || hipEventRecord(stop, stream_) != hipSuccess) return;
   std::lock_guard<std::mutex> lock(g_mu);
   g_records.push_back(Record{name_, start_, stop});
+}
+
+// Compute units of the current device (cached per device id).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 }  // namespace msa

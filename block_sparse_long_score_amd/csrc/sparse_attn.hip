@@ -26,7 +26,6 @@
 namespace msa {
 namespace {
 
-constexpr int kEntriesPerItem = 64;   // list entries (query tokens) per KV-outer workgroup
 constexpr int kAttnThreads = 256;
 
 int64_t prefill_entries_max(const Dims& d) { return (int64_t)d.batch * d.n_q * d.h_kv * d.topk; }
@@ -97,44 +96,30 @@ __global__ void csr_chunk_scan(int* __restrict__ ccnt, int* __restrict__ cnt, in
   cnt[list] = run;
 }
 
-// One workgroup: exclusive scans of the list sizes and of their item counts.
+// One workgroup: exclusive scan of the list sizes; off[lists] = all entries.
 constexpr int kScanThreads = 1024;
 __global__ __launch_bounds__(kScanThreads) void csr_scan(const int* __restrict__ cnt, int* __restrict__ off,
-                                                        int* __restrict__ item_off, int lists, int per_item) {
+                                                        int lists) {
   __shared__ int s_e[kScanThreads];
-  __shared__ int s_i[kScanThreads];
   const int tid = threadIdx.x;
   const int per = (lists + kScanThreads - 1) / kScanThreads;
   const int lo = min(lists, tid * per), hi = min(lists, lo + per);
-  int se = 0, si = 0;
-  for (int i = lo; i < hi; ++i) {
-    const int c = cnt[i];
-    se += c;
-    si += (c + per_item - 1) / per_item;
-  }
+  int se = 0;
+  for (int i = lo; i < hi; ++i) se += cnt[i];
   s_e[tid] = se;
-  s_i[tid] = si;
   __syncthreads();
   for (int o = 1; o < kScanThreads; o <<= 1) {         // inclusive Hillis-Steele scan
     const int ae = tid >= o ? s_e[tid - o] : 0;
-    const int ai = tid >= o ? s_i[tid - o] : 0;
     __syncthreads();
     s_e[tid] += ae;
-    s_i[tid] += ai;
     __syncthreads();
   }
-  int re = s_e[tid] - se, ri = s_i[tid] - si;          // exclusive prefix of this thread's range
+  int re = s_e[tid] - se;                              // exclusive prefix of this thread's range
   for (int i = lo; i < hi; ++i) {
     off[i] = re;
-    item_off[i] = ri;
-    const int c = cnt[i];
-    re += c;
-    ri += (c + per_item - 1) / per_item;
+    re += cnt[i];
   }
-  if (tid == kScanThreads - 1) {
-    off[lists] = s_e[tid];
-    item_off[lists] = s_i[tid];
-  }
+  if (tid == kScanThreads - 1) off[lists] = s_e[tid];
 }
 
 // Entries of chunk c go to off[list] + (prefix of earlier chunks) + a rank
@@ -161,118 +146,229 @@ __global__ __launch_bounds__(kCsrThreads) void csr_fill_chunks(const int32_t* __
 }
 
 // --------------------------------------------------------- KV-outer ---------
+//
+// Persistent: one 8-wave workgroup per CU takes an equal, contiguous range of
+// the list entries (lists are consecutive in `entries`, in (b, g, block)
+// order), so it walks a few dozen lists one after the other.  A list's K/V
+// block is staged in LDS once for the whole segment of the list the range
+// covers; the next list's block is loaded into registers while the current
+// segment computes and is written to the other LDS buffer before the switch.
+// Within a segment, waves take 32-column groups (column = entry x group head)
+// round-robin and load the next group's queries and entries while computing.
+
+constexpr int kKvThreads = 512;
+
+// Registers of one K/V block in flight: K as 16-byte chunks, V as 4-key x
+// 8-dim tiles that are transposed into the vt rows when written to LDS.
+template <int D>
+struct KVPrefetch {
+  static constexpr int DC = D / 8;
+  static constexpr int KI = kBlock * DC / kKvThreads;            // K chunks per thread
+  static constexpr int VQ = (kBlock / 4) * DC;                    // V tiles per block
+  static constexpr int VI = (VQ + kKvThreads - 1) / kKvThreads;   // V tiles per thread
+  static_assert(KI * kKvThreads == kBlock * DC, "K staging must divide evenly");
+  u32x4 kr[KI];
+  u32x4 vr[VI][4];
+
+  __device__ __forceinline__ void fetch(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                        int64_t rs, int s0, int n_kv, int tid) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int w = tid + i * kKvThreads, key = w / DC, dc = w % DC;
+      const int s = s0 + key;
+      kr[i] = s < n_kv ? ld16(kb + (int64_t)s * rs + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int w = tid + i * kKvThreads, kq = w / DC, dg = w % DC;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = s0 + 4 * kq + r;
+        vr[i][r] = (w < VQ && s < n_kv) ? ld16(vb + (int64_t)s * rs + dg * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void stash(KVTile<D>& t, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int w = tid + i * kKvThreads, key = w / DC, dc = w % DC;
+      st16(&t.k[key * D + 8 * (dc ^ (tile_swz(key) & (DC - 1)))], kr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int w = tid + i * kKvThreads, kq = w / DC, dg = w % DC;
+      if (w >= VQ) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int word = e >> 1, sh = (e & 1) * 16, d = dg * 8 + e;
+        u32x2 o;
+        o[0] = ((vr[i][0][word] >> sh) & 0xffffu) | (((vr[i][1][word] >> sh) & 0xffffu) << 16);
+        o[1] = ((vr[i][2][word] >> sh) & 0xffffu) | (((vr[i][3][word] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<u32x2*>(&t.vt[d * kBlock + 8 * ((kq >> 1) ^ tile_swz(d)) + 4 * (kq & 1)]) = o;
+      }
+    }
+  }
+};
+
+// The list holding entry e: the first list L' > L whose range ends past e
+// (off is nondecreasing; empty lists are stepped over 64 at a time).
+__device__ __forceinline__ int next_list(const int* __restrict__ off, int lists, int L, int e) {
+  for (int base = L + 1;; base += 64) {
+    const int cand = base + lane_id();
+    const uint64_t m = ballot(cand < lists && off[cand + 1] > e);
+    if (m) return base + __builtin_ctzll(m);
+  }
+}
 
 template <int D, int LOG2G>
-__global__ __launch_bounds__(kAttnThreads, 2) void sparse_kv_outer(
+__global__ __launch_bounds__(kKvThreads, 1) void sparse_kv_outer(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int* __restrict__ cnt, const int* __restrict__ off, const int* __restrict__ item_off,
-    const int* __restrict__ entries, uint16_t* __restrict__ part_o, float* __restrict__ part_ml, int n_q, int n_kv,
-    int pos0, int h_q, int h_kv, int nblk, int topk, int lists, float sl2) {
+    const int* __restrict__ off, const int* __restrict__ entries, uint16_t* __restrict__ part_o,
+    float* __restrict__ part_ml, int64_t sink_row, int n_q, int n_kv, int pos0, int h_q, int h_kv, int nblk,
+    int topk, int lists, float sl2) {
   constexpr int G = 1 << LOG2G;
-  __shared__ KVTile<D> tile;
-  __shared__ int ent[kEntriesPerItem];
-  __shared__ int s_list;
-  const int item = blockIdx.x;
-  if (item >= item_off[lists]) return;                 // grid is an upper bound
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid == 0) {
-    int lo = 0, hi = lists - 1;                        // last list with item_off <= item
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (item_off[mid] <= item) lo = mid; else hi = mid - 1;
+  constexpr int NW = kKvThreads / 64;
+  __shared__ KVTile<D> tile[2];
+  const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int total = off[lists];
+  const int lo = (int)((int64_t)total * blockIdx.x / gridDim.x);
+  const int hi = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
+  if (lo >= hi) return;
+  int L;                                               // list holding entry lo: last L with off[L] <= lo
+  {
+    int a = 0, z = lists - 1;
+    while (a < z) {
+      const int mid = (a + z + 1) >> 1;
+      if (off[mid] <= lo) a = mid; else z = mid - 1;
     }
-    s_list = lo;
+    L = a;
+    while (off[L + 1] <= lo) ++L;                      // step over empty lists sharing the offset
   }
-  __syncthreads();
-  const int list = s_list;
-  const int c = item - item_off[list];
-  const int e0 = off[list] + c * kEntriesPerItem;
-  const int E = min(kEntriesPerItem, cnt[list] - c * kEntriesPerItem);
-  const int j = list % nblk;
-  const int bg = list / nblk;
-  const int g = bg % h_kv, b = bg / h_kv;
-  if (tid < E) ent[tid] = entries[e0 + tid];
   const int64_t row_stride = (int64_t)h_kv * D;
-  const int64_t head0 = ((int64_t)b * n_kv * h_kv + g) * D;
-  stage_kv_block<D, kAttnThreads>(tile, k + head0, v + head0, row_stride, j * kBlock, n_kv, tid);
+  auto block_base = [&](int list, const uint16_t* base) {
+    const int bg = list / nblk;
+    return base + ((int64_t)(bg / h_kv) * n_kv * h_kv + bg % h_kv) * D;
+  };
+  KVPrefetch<D> pf;
+  pf.fetch(block_base(L, k), block_base(L, v), row_stride, (L % nblk) * kBlock, n_kv, tid);
+  pf.stash(tile[0], tid);
   __syncthreads();
+  int buf = 0;
+  int seg_end = min(hi, off[L + 1]);
+  int Ln = seg_end < hi ? next_list(off, lists, L, seg_end) : -1;
+  if (Ln >= 0) pf.fetch(block_base(Ln, k), block_base(Ln, v), row_stride, (Ln % nblk) * kBlock, n_kv, tid);
 
-  const int s0 = j * kBlock;
-  const int ncols = E << LOG2G;
-  const int ngroups = (ncols + 31) >> 5;
-  const int q4 = lane >> 4;
-  // Column (token, head) bookkeeping of one 32-column group.
+  // Column (token, head) bookkeeping of one 32-column group.  Columns past a
+  // segment's end read a clamped entry and write their partial to the sink
+  // row, so that no load or store of the loop sits behind a per-lane branch:
+  // the compiler then counts outstanding memory operations exactly, and the
+  // wait for a group's entries or queries never includes the partial stores
+  // issued after them.
   struct Cols {
     const uint16_t* qrow[2];
     int plim[2];
     int64_t prow[2];
-    bool valid[2];
     bool mask_any;
   };
-  auto describe = [&](int cg, Cols& c) {
-    c.mask_any = false;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int col = cg * 32 + ct * 16 + (lane & 15);
-      const int e = col >> LOG2G, hh = col & (G - 1);
-      c.valid[ct] = e < E;
-      const int en = c.valid[ct] ? ent[e] : 0;
-      const int t = en >> 5, slot = en & 31;
-      const int p = pos0 + t;
-      c.qrow[ct] = c.valid[ct] ? q + (((int64_t)b * n_q + t) * h_q + g * G + hh) * D : nullptr;
-      c.plim[ct] = c.valid[ct] ? p : INT_MAX;
-      c.prow[ct] = ((((int64_t)b * n_q + t) * h_kv + g) * topk + slot) * G + hh;
-      c.mask_any |= c.valid[ct] && (p < s0 + kBlock - 1);
-    }
-  };
-  // The next group's queries are loaded while the current group computes.
-  Cols cur_c, nxt_c;
-  u32x4 qb[2][D / 32], qn[2][D / 32];
-  int cg = wave;
-  if (cg < ngroups) {
-    describe(cg, cur_c);
-    load_q_operand<D>(qb, cur_c.qrow);
-  }
 #pragma unroll 1
-  for (; cg < ngroups; cg += kAttnThreads / 64) {
-    const int cn = cg + kAttnThreads / 64;
-    if (cn < ngroups) {
-      describe(cn, nxt_c);
-      load_q_operand<D>(qn, nxt_c.qrow);
-    }
-    const bool need_mask = ballot(cur_c.mask_any) != 0ull;
-    float bmax[2], bsum[2], mref[2] = {0.f, 0.f};
-    u32x4 pb[2][4];
-    block_scores_softmax<D>(tile, qb, sl2, s0, cur_c.plim, need_mask, bmax, bsum, pb, mref, false);
-    f32x4 acc[2][D / 32][2];
+  for (;;) {
+    const int j = L % nblk, bg = L / nblk;
+    const int g = bg % h_kv, b = bg / h_kv;
+    const int s0 = j * kBlock;
+    const int ea = max(lo, off[L]), eb = seg_end;      // this segment's entries
+    const int ngroups = (((eb - ea) << LOG2G) + 31) >> 5;
+    auto entry_of = [&](int cg, int ct) { return ea + ((cg * 32 + ct * 16 + (lane & 15)) >> LOG2G); };
+    auto load_entries = [&](int cg, int (&en)[2]) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 2; ++ct) en[ct] = entries[min(entry_of(cg, ct), eb - 1)];
+    };
+    auto describe = [&](int cg, const int (&en)[2], Cols& c) {
+      c.mask_any = false;
 #pragma unroll
-      for (int pp = 0; pp < D / 32; ++pp)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) acc[ct][pp][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-    block_pv<D>(tile, pb, acc);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      if (!cur_c.valid[ct]) continue;
-      uint16_t* dst = part_o + cur_c.prow[ct] * D;
-#pragma unroll
-      for (int pp = 0; pp < D / 32; ++pp) {
-        const f32x4 a0 = acc[ct][pp][0], a1 = acc[ct][pp][1];
-        u32x4 o = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
-                   pack_bf16x2(a1[2], a1[3])};
-        st16(dst + 32 * pp + 8 * q4, o);
+      for (int ct = 0; ct < 2; ++ct) {
+        const bool valid = entry_of(cg, ct) < eb;
+        const int hh = (cg * 32 + ct * 16 + (lane & 15)) & (G - 1);
+        const int t = en[ct] >> 5, slot = en[ct] & 31;
+        const int p = pos0 + t;
+        c.qrow[ct] = q + (((int64_t)b * n_q + t) * h_q + g * G + hh) * D;
+        c.plim[ct] = valid ? p : INT_MAX;
+        c.prow[ct] = valid ? ((((int64_t)b * n_q + t) * h_kv + g) * topk + slot) * G + hh : sink_row + hh;
+        c.mask_any |= valid && (p < s0 + kBlock - 1);
       }
-      if (q4 == 0) {
-        part_ml[2 * cur_c.prow[ct]] = bmax[ct];
-        part_ml[2 * cur_c.prow[ct] + 1] = bsum[ct];
-      }
+    };
+    const KVTile<D>& tl = tile[buf];
+    auto load_q = [&](const Cols& c, u32x4 (&qv)[2][D / 32]) {   // unconditional: every qrow is a real row
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int cc = 0; cc < D / 32; ++cc) qv[ct][cc] = ld16(c.qrow[ct] + cc * 32 + q4 * 8);
+    };
+    Cols cur_c, nxt_c;
+    u32x4 qb[2][D / 32], qn[2][D / 32];
+    int en1[2];
+    int cg = wave;
+    if (cg < ngroups) {
+      int en0[2];
+      load_entries(cg, en0);
+      describe(cg, en0, cur_c);
+      load_q(cur_c, qb);
+      load_entries(min(cg + NW, ngroups - 1), en1);
     }
-    cur_c = nxt_c;
+    // Drain the memory counters once per segment: the loop header then sees
+    // only the loop's own outstanding operations, and the compiler can wait
+    // for each prefetch by count instead of draining every iteration.
+    __builtin_amdgcn_s_waitcnt(0);
+    // Straight-line body: the prefetches of the last iterations re-read the
+    // segment's last group (clamped) and are not used.
+#pragma unroll 1
+    for (; cg < ngroups; cg += NW) {
+      const int cn = min(cg + NW, ngroups - 1);
+      describe(cn, en1, nxt_c);                        // queries of the next group (entries loaded a group ago)
+      load_q(nxt_c, qn);
+      const bool need_mask = ballot(cur_c.mask_any) != 0ull;
+      float bmax[2], bsum[2], mref[2] = {0.f, 0.f};
+      u32x4 pb[2][4];
+      block_scores_softmax<D>(tl, qb, sl2, s0, cur_c.plim, need_mask, bmax, bsum, pb, mref, false);
+      f32x4 acc[2][D / 32][2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int cc = 0; cc < D / 32; ++cc) qb[ct][cc] = qn[ct][cc];
+        for (int pp = 0; pp < D / 32; ++pp)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) acc[ct][pp][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      block_pv<D>(tl, pb, acc);
+      // Entries of the group after next, issued before this group's stores.
+      load_entries(min(cg + 2 * NW, ngroups - 1), en1);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        uint16_t* dst = part_o + cur_c.prow[ct] * D;
+#pragma unroll
+        for (int pp = 0; pp < D / 32; ++pp) {
+          const f32x4 a0 = acc[ct][pp][0], a1 = acc[ct][pp][1];
+          u32x4 o = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
+                     pack_bf16x2(a1[2], a1[3])};
+          st16(dst + 32 * pp + 8 * q4, o);
+        }
+        // (m, l) is replicated over the column's four lane groups; all store it.
+        *reinterpret_cast<float2*>(part_ml + 2 * cur_c.prow[ct]) = make_float2(bmax[ct], bsum[ct]);
+      }
+      cur_c = nxt_c;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int cc = 0; cc < D / 32; ++cc) qb[ct][cc] = qn[ct][cc];
+    }
+    if (Ln < 0) break;
+    // The other buffer was last read before the previous switch's barrier.
+    pf.stash(tile[buf ^ 1], tid);
+    __syncthreads();
+    buf ^= 1;
+    L = Ln;
+    seg_end = min(hi, off[L + 1]);
+    Ln = seg_end < hi ? next_list(off, lists, L, seg_end) : -1;
+    if (Ln >= 0) pf.fetch(block_base(Ln, k), block_base(Ln, v), row_stride, (Ln % nblk) * kBlock, n_kv, tid);
   }
 }
 
@@ -400,7 +496,6 @@ hipError_t launch_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k,
   char* base = static_cast<char*>(ws);
   int* cnt = reinterpret_cast<int*>(base + L.cnt);
   int* off = reinterpret_cast<int*>(base + L.off);
-  int* item_off = reinterpret_cast<int*>(base + L.item_off);
   int* ccnt = reinterpret_cast<int*>(base + L.ccnt);
   int* entries = reinterpret_cast<int*>(base + L.entries);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
@@ -422,7 +517,7 @@ hipError_t launch_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k,
   }
   {
     LaunchTimer timer("csr_scan", stream);
-    hipLaunchKernelGGL(csr_scan, dim3(1), dim3(kScanThreads), 0, stream, cnt, off, item_off, lists, kEntriesPerItem);
+    hipLaunchKernelGGL(csr_scan, dim3(1), dim3(kScanThreads), 0, stream, cnt, off, lists);
   }
   {
     LaunchTimer timer("csr_fill_chunks", stream);
@@ -431,9 +526,9 @@ hipError_t launch_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k,
   }
   {
     LaunchTimer timer("sparse_kv_outer", stream);
-    hipLaunchKernelGGL((sparse_kv_outer<D, LOG2G>), dim3((unsigned)L.items_max), dim3(kAttnThreads), 0, stream, q, k,
-                       v, cnt, off, item_off, entries, part_o, part_ml, d.n_q, d.n_kv, d.pos0, d.h_q, d.h_kv, nblk,
-                       d.topk, lists, sl2);
+    hipLaunchKernelGGL((sparse_kv_outer<D, LOG2G>), dim3((unsigned)device_cu_count()), dim3(kKvThreads), 0, stream,
+                       q, k, v, off, entries, part_o, part_ml, L.entries_max * d.group(), d.n_q, d.n_kv, d.pos0,
+                       d.h_q, d.h_kv, nblk, d.topk, lists, sl2);
   }
   return launch_merge_t<D>(d, part_o, part_ml, blk, out, lse, d.topk, 1, stream);
 }
@@ -485,17 +580,16 @@ PrefillWs prefill_ws_layout(const Dims& d) {
   PrefillWs L{};
   L.lists = (int64_t)d.batch * d.h_kv * d.nblk();
   L.entries_max = prefill_entries_max(d);
-  L.items_max = (L.entries_max + kEntriesPerItem - 1) / kEntriesPerItem + L.lists;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
   L.cnt = take(sizeof(int) * L.lists);
   L.off = take(sizeof(int) * (L.lists + 1));
-  L.item_off = take(sizeof(int) * (L.lists + 1));
   L.chunks = csr_chunks(d);
   L.ccnt = take(sizeof(int) * (size_t)L.lists * L.chunks);
   L.entries = take(sizeof(int) * L.entries_max);
-  L.part_o = take((size_t)L.entries_max * d.group() * d.d * 2);
-  L.part_ml = take((size_t)L.entries_max * d.group() * 2 * sizeof(float));
+  // partials per (entry, head), plus one sink row of G heads for idle columns
+  L.part_o = take((size_t)(L.entries_max + 1) * d.group() * d.d * 2);
+  L.part_ml = take((size_t)(L.entries_max + 1) * d.group() * 2 * sizeof(float));
   L.total = o;
   return L;
 }

@@ -416,55 +416,51 @@ __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict
   const int jl = (pos0 + t) / kBlock;
   const int64_t unit0 = (bt * h_kv + g) * nslot;
   const int32_t* brow = blk ? blk + unit0 : nullptr;
-  // Slots go in batches of 8 so each thread keeps 16 independent loads in
-  // flight.  Every slot is loaded (address clamped into the row) and dead ones
-  // are dropped with selects only: their memory may hold anything, and the
-  // branch-per-slot form of this loop was miscompiled by the gfx950 toolchain
-  // (wrong sums for rows with dead slots).
-  // Pass 1: the largest partial max.  Pass 2: weighted sum.
-  float M = -INFINITY;
+  // One pass with a running maximum: slots go in batches of 8, each thread
+  // keeping 8 (m, l) pairs and 8 16-byte loads of o in flight.  Every slot is
+  // loaded (address clamped into the row) and dead ones are dropped with
+  // selects only: their memory may hold anything, and the branch-per-slot form
+  // of such a loop was miscompiled by the gfx950 toolchain (wrong sums for
+  // rows with dead slots).
+  float M = -INFINITY, L = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int s0 = 0; s0 < nslot; s0 += 8) {
-    float mv[8];
+    u32x4 o[8];
+    float mv[8], lv[8];
     bool on[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int s = min(s0 + i, nslot - 1);
       const int j = brow ? brow[s] : s * per;
       on[i] = (s0 + i < nslot) && j >= 0 && j <= jl;
-      mv[i] = part_ml[2 * ((unit0 + s) * G + hh)];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) M = on[i] ? vmax(M, mv[i]) : M;
-  }
-  float L = 0.f, acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int s0 = 0; s0 < nslot; s0 += 8) {
-    u32x4 o[8];
-    float w[8], wl[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = min(s0 + i, nslot - 1);
-      const int j = brow ? brow[s] : s * per;
-      const bool on = (s0 + i < nslot) && j >= 0 && j <= jl;
       const int64_t pr = (unit0 + s) * G + hh;
-      const float mm = part_ml[2 * pr], ll = part_ml[2 * pr + 1];
-      const u32x4 ov = ld16(part_o + pr * D + dl * 8);
-      const float ww = __builtin_amdgcn_exp2f(mm - M);
-      w[i] = on ? ww : 0.f;
-      wl[i] = on ? ww * ll : 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[i][e] = on ? ov[e] : 0u;
+      const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
+      mv[i] = ml.x;
+      lv[i] = ml.y;
+      o[i] = ld16(part_o + pr * D + dl * 8);
     }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bm = on[i] ? vmax(bm, mv[i]) : bm;
+    const float Mn = vmax(M, bm);
+    // Mn = -inf only while every slot so far is dead; then nothing is added.
+    const float scale = Mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(M - Mn);
+    L *= scale;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= scale;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      L += wl[i];
+      const float w = on[i] ? __builtin_amdgcn_exp2f(mv[i] - Mn) : 0.f;
+      L = fmaf(w, on[i] ? lv[i] : 0.f, L);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = fmaf(w[i], bf16_to_f32(o[i][e] & 0xffffu), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(w[i], bf16_to_f32(o[i][e] >> 16), acc[2 * e + 1]);
+        const uint32_t ov = on[i] ? o[i][e] : 0u;
+        acc[2 * e] = fmaf(w, bf16_to_f32(ov & 0xffffu), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(w, bf16_to_f32(ov >> 16), acc[2 * e + 1]);
       }
     }
+    M = Mn;
   }
   const float inv = 1.f / L;
   u32x4 r;

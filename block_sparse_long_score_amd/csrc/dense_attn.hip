@@ -4,10 +4,11 @@
 // "Minimax-sparse-Attention", "what is MHA, MQA, GQA?": each group of query
 // heads shares one K/V head).
 //
-// Prefill: a workgroup owns 128 (token x group-head) columns of one K/V head,
+// Prefill: a workgroup owns 256 (token x group-head) columns of one K/V head,
 // keeps their queries in registers and streams the head's 128-token K/V blocks
-// through LDS with online softmax (flash-attention order), so each K/V block is
-// read once per 128 columns.  Tiles run longest (latest tokens) first.
+// through double-buffered LDS with online softmax (flash-attention order), so
+// each K/V block is read once per 256 columns; query tiles are paired so every
+// workgroup carries the same number of block iterations.
 // Decode: the keys are split into chunks of kChunkBlocks blocks; one wave per
 // (sequence, group, chunk) streams its chunk from HBM, and the per-chunk
 // partials are merged with log-sum-exp weights.
@@ -19,93 +20,115 @@
 namespace msa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kColsPerWg = 128;
+constexpr int kThreads = 256;                          // decode
 constexpr int kChunkBlocks = 16;
+constexpr int kColsPerWg = 256;                        // prefill: 8 waves x 32 (token, group head) columns
 
+// Prefill.  A workgroup owns 256 (token x group head) columns of one K/V head
+// (TQ = 256 / G tokens), keeps their queries in registers and sweeps the
+// head's 128-token K/V blocks 0 .. the last token's block with online softmax
+// (flash-attention order).  Blocks are double-buffered in LDS: block j + 1 is
+// written from registers while block j is in use and block j + 2 is loaded,
+// with one barrier per block.  Query tile t needs ~t blocks, so tile t is paired
+// with tile T-1-t and one workgroup runs the pair: equal work per workgroup.
 template <int D, int LOG2G>
-__global__ __launch_bounds__(kThreads) void dense_prefill(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse, int n_q, int n_kv, int pos0,
-                                                          int h_q, int h_kv, float sl2) {
+__global__ __launch_bounds__(kKvThreads, 1) void dense_prefill(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ k,
+                                                               const uint16_t* __restrict__ v,
+                                                               uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                               int n_q, int n_kv, int pos0, int h_q, int h_kv,
+                                                               int tiles, float sl2) {
   constexpr int G = 1 << LOG2G;
-  constexpr int TQ = kColsPerWg >> LOG2G;               // tokens per workgroup
-  __shared__ KVTile<D> tile;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int TQ = kColsPerWg >> LOG2G;               // tokens per tile
+  __shared__ KVTile<D> tile[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int tile_idx = gridDim.x - 1 - blockIdx.x;      // latest tokens first: they have the most blocks
-  const int t0 = tile_idx * TQ;
-  const int t_last = min(t0 + TQ, n_q) - 1;
-  const int jmax = (pos0 + t_last) / kBlock;
-
-  const int twmin = t0 + ((wave * 32) >> LOG2G);
-  const int twmax = min(t0 + ((wave * 32 + 31) >> LOG2G), n_q - 1);
-  const bool wave_live = twmin < n_q;
-  const int jw = wave_live ? (pos0 + twmax) / kBlock : -1;
-
-  const uint16_t* qrow[2];
-  int plim[2];
-  bool valid[2];
-  int64_t orow[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int c = wave * 32 + ct * 16 + (lane & 15);
-    const int tt = t0 + (c >> LOG2G), hh = c & (G - 1);
-    valid[ct] = tt < n_q;
-    orow[ct] = ((int64_t)b * n_q + tt) * h_q + g * G + hh;
-    qrow[ct] = valid[ct] ? q + orow[ct] * D : nullptr;
-    plim[ct] = valid[ct] ? pos0 + tt : INT_MAX;
-  }
-  u32x4 qb[2][D / 32];
-  load_q_operand<D>(qb, qrow);
-
-  float mref[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
-  f32x4 acc[2][D / 32][2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-    for (int pp = 0; pp < D / 32; ++pp)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) acc[ct][pp][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int64_t row_stride = (int64_t)h_kv * D;
   const int64_t head0 = ((int64_t)b * n_kv * h_kv + g) * D;
-  for (int j = 0; j <= jmax; ++j) {
-    __syncthreads();
-    stage_kv_block<D, kThreads>(tile, k + head0, v + head0, row_stride, j * kBlock, n_kv, tid);
-    __syncthreads();
-    if (j > jw) continue;
-    const bool need_mask = (j * kBlock + kBlock - 1) > (pos0 + twmin);
-    float m_old[2] = {mref[0], mref[1]};
-    float bmax[2], bsum[2];
-    u32x4 pb[2][4];
-    block_scores_softmax<D>(tile, qb, sl2, j * kBlock, plim, need_mask, bmax, bsum, pb, mref, true);
+  KVPrefetch<D> pf;
+
+#pragma unroll 1
+  for (int seg = 0; seg < 2; ++seg) {
+    const int ti = seg == 0 ? tiles - 1 - p : p;
+    if (seg == 1 && ti == tiles - 1 - p) break;          // unpaired middle tile
+    const int t0 = ti * TQ;
+    const int t_last = min(t0 + TQ, n_q) - 1;
+    const int jmax = (pos0 + t_last) / kBlock;
+    const int twmin = t0 + ((wave * 32) >> LOG2G);
+    const int twmax = min(t0 + ((wave * 32 + 31) >> LOG2G), n_q - 1);
+    const bool wave_live = twmin < n_q;
+    const int jw = wave_live ? (pos0 + twmax) / kBlock : -1;
+
+    const uint16_t* qrow[2];
+    int plim[2];
+    bool valid[2];
+    int64_t orow[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const float alpha = __builtin_amdgcn_exp2f(m_old[ct] - mref[ct]);   // 0 on the first block
-      lrun[ct] = lrun[ct] * alpha + bsum[ct];
+      const int c = wave * 32 + ct * 16 + (lane & 15);
+      const int tt = t0 + (c >> LOG2G), hh = c & (G - 1);
+      valid[ct] = tt < n_q;
+      orow[ct] = ((int64_t)b * n_q + tt) * h_q + g * G + hh;
+      qrow[ct] = valid[ct] ? q + orow[ct] * D : nullptr;
+      plim[ct] = valid[ct] ? pos0 + tt : INT_MAX;
+    }
+    u32x4 qb[2][D / 32];
+    load_q_operand<D>(qb, qrow);
+
+    float mref[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+    f32x4 acc[2][D / 32][2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int pp = 0; pp < D / 32; ++pp)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) acc[ct][pp][h] *= alpha;
-    }
-    block_pv<D>(tile, pb, acc);
-  }
+        for (int h = 0; h < 2; ++h) acc[ct][pp][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (seg == 1) __syncthreads();                     // the first tile's last block is no longer read
+    pf.fetch(k + head0, v + head0, row_stride, 0, n_kv, tid);
+    pf.stash(tile[0], tid);
+    __syncthreads();
+    if (jmax >= 1) pf.fetch(k + head0, v + head0, row_stride, kBlock, n_kv, tid);
+#pragma unroll 1
+    for (int j = 0; j <= jmax; ++j) {
+      const KVTile<D>& tl = tile[j & 1];
+      if (j <= jw) {
+        const bool need_mask = (j * kBlock + kBlock - 1) > (pos0 + twmin);
+        float m_old[2] = {mref[0], mref[1]};
+        float bmax[2], bsum[2];
+        u32x4 pb[2][4];
+        block_scores_softmax<D>(tl, qb, sl2, j * kBlock, plim, need_mask, bmax, bsum, pb, mref, true);
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    if (!valid[ct]) continue;
-    const float inv = 1.f / lrun[ct];
-    uint16_t* dst = out + orow[ct] * D;
+        for (int ct = 0; ct < 2; ++ct) {
+          const float alpha = __builtin_amdgcn_exp2f(m_old[ct] - mref[ct]);   // 0 on the first block
+          lrun[ct] = lrun[ct] * alpha + bsum[ct];
 #pragma unroll
-    for (int pp = 0; pp < D / 32; ++pp) {
-      const f32x4 a0 = acc[ct][pp][0], a1 = acc[ct][pp][1];
-      u32x4 o = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
-                 pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
-      st16(dst + 32 * pp + 8 * q4, o);
+          for (int pp = 0; pp < D / 32; ++pp)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) acc[ct][pp][h] *= alpha;
+        }
+        block_pv<D>(tl, pb, acc);
+      }
+      if (j + 1 <= jmax) pf.stash(tile[(j + 1) & 1], tid);   // read last in block j - 1, before the barrier
+      __syncthreads();
+      if (j + 2 <= jmax) pf.fetch(k + head0, v + head0, row_stride, (j + 2) * kBlock, n_kv, tid);
     }
-    if (lse && q4 == 0) lse[orow[ct]] = (mref[ct] + __log2f(lrun[ct])) * kLn2;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      if (!valid[ct]) continue;
+      const float inv = 1.f / lrun[ct];
+      uint16_t* dst = out + orow[ct] * D;
+#pragma unroll
+      for (int pp = 0; pp < D / 32; ++pp) {
+        const f32x4 a0 = acc[ct][pp][0], a1 = acc[ct][pp][1];
+        u32x4 o = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
+                   pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
+        st16(dst + 32 * pp + 8 * q4, o);
+      }
+      if (lse && q4 == 0) lse[orow[ct]] = (mref[ct] + __log2f(lrun[ct])) * kLn2;
+    }
   }
 }
 
@@ -134,11 +157,12 @@ template <int D, int LOG2G>
 hipError_t prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v, float sl2,
                      uint16_t* out, float* lse, hipStream_t stream) {
   constexpr int TQ = kColsPerWg >> LOG2G;
-  dim3 grid((d.n_q + TQ - 1) / TQ, d.h_kv, d.batch);
+  const int tiles = (d.n_q + TQ - 1) / TQ;
+  dim3 grid((tiles + 1) / 2, d.h_kv, d.batch);
   {
     LaunchTimer timer("dense_prefill", stream);
-    hipLaunchKernelGGL((dense_prefill<D, LOG2G>), grid, dim3(kThreads), 0, stream, q, k, v, out, lse, d.n_q, d.n_kv,
-                       d.pos0, d.h_q, d.h_kv, sl2);
+    hipLaunchKernelGGL((dense_prefill<D, LOG2G>), grid, dim3(kKvThreads), 0, stream, q, k, v, out, lse, d.n_q,
+                       d.n_kv, d.pos0, d.h_q, d.h_kv, tiles, sl2);
   }
   return hipGetLastError();
 }

@@ -156,61 +156,6 @@ __global__ __launch_bounds__(kCsrThreads) void csr_fill_chunks(const int32_t* __
 // Within a segment, waves take 32-column groups (column = entry x group head)
 // round-robin and load the next group's queries and entries while computing.
 
-constexpr int kKvThreads = 512;
-
-// Registers of one K/V block in flight: K as 16-byte chunks, V as 4-key x
-// 8-dim tiles that are transposed into the vt rows when written to LDS.
-template <int D>
-struct KVPrefetch {
-  static constexpr int DC = D / 8;
-  static constexpr int KI = kBlock * DC / kKvThreads;            // K chunks per thread
-  static constexpr int VQ = (kBlock / 4) * DC;                    // V tiles per block
-  static constexpr int VI = (VQ + kKvThreads - 1) / kKvThreads;   // V tiles per thread
-  static_assert(KI * kKvThreads == kBlock * DC, "K staging must divide evenly");
-  u32x4 kr[KI];
-  u32x4 vr[VI][4];
-
-  __device__ __forceinline__ void fetch(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
-                                        int64_t rs, int s0, int n_kv, int tid) {
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int w = tid + i * kKvThreads, key = w / DC, dc = w % DC;
-      const int s = s0 + key;
-      kr[i] = s < n_kv ? ld16(kb + (int64_t)s * rs + dc * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int w = tid + i * kKvThreads, kq = w / DC, dg = w % DC;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = s0 + 4 * kq + r;
-        vr[i][r] = (w < VQ && s < n_kv) ? ld16(vb + (int64_t)s * rs + dg * 8) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-
-  __device__ __forceinline__ void stash(KVTile<D>& t, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int w = tid + i * kKvThreads, key = w / DC, dc = w % DC;
-      st16(&t.k[key * D + 8 * (dc ^ (tile_swz(key) & (DC - 1)))], kr[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int w = tid + i * kKvThreads, kq = w / DC, dg = w % DC;
-      if (w >= VQ) continue;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int word = e >> 1, sh = (e & 1) * 16, d = dg * 8 + e;
-        u32x2 o;
-        o[0] = ((vr[i][0][word] >> sh) & 0xffffu) | (((vr[i][1][word] >> sh) & 0xffffu) << 16);
-        o[1] = ((vr[i][2][word] >> sh) & 0xffffu) | (((vr[i][3][word] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(&t.vt[d * kBlock + 8 * ((kq >> 1) ^ tile_swz(d)) + 4 * (kq & 1)]) = o;
-      }
-    }
-  }
-};
-
 // The list holding entry e: the first list L' > L whose range ends past e
 // (off is nondecreasing; empty lists are stepped over 64 at a time).
 __device__ __forceinline__ int next_list(const int* __restrict__ off, int lists, int L, int e) {

@@ -127,7 +127,10 @@ __device__ __forceinline__ void wave_select(const uint32_t (&key)[V], int kk, ui
   emit_threshold(T, kk - n_gt);
 }
 
-// One wave per (query, group) row; rows of up to 64*V candidates.
+// Rows of up to 64*V candidates: one wave per kRowsPerWave consecutive
+// (query, group) rows, the next row's scores loaded while the current row is
+// selected.
+constexpr int kRowsPerWave = 8;
 template <int V>
 __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* __restrict__ bscore,
                                                                    int32_t* __restrict__ blk, int n_q, int pos0,
@@ -135,27 +138,47 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* 
   __shared__ uint32_t ck[kRowsPerWg][64];
   __shared__ int32_t ci[kRowsPerWg][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + wave;
-  if (row >= nrows) return;
-  const int t = (int)((row / h_kv) % n_q);
-  const int jl = (pos0 + t) / kBlock;
-  int32_t* out = blk + row * topk;
-  if (jl + 1 <= topk) {
-    for (int i = lane; i < topk; i += 64) out[i] = (i <= jl) ? i : -1;
-    return;
-  }
+  const int64_t row0 = ((int64_t)blockIdx.x * kRowsPerWg + wave) * kRowsPerWave;
+  if (row0 >= nrows) return;
+  const int64_t row_end = min(row0 + (int64_t)kRowsPerWave, nrows);
   const int kk = topk - 1;
-  if (lane == 0) out[kk] = jl;                         // the local block is the largest index
-  if (kk == 0) return;
-  const float* sc = bscore + row * nblk;
-  const int n = jl;                                    // candidates 0..jl-1, n > kk
-  uint32_t key[V];
+  // Candidates of a row: blocks 0 .. jl-1 (0 when the row keeps all its blocks).
+  auto n_cand = [&](int64_t row) {
+    const int jl = (pos0 + (int)((row / h_kv) % n_q)) / kBlock;
+    return jl + 1 <= topk ? 0 : jl;
+  };
+  auto load = [&](int64_t row, float (&f)[V]) {
+    const float* sc = bscore + row * nblk;
+    const int n = n_cand(row);
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int e = i * 64 + lane;
-    key[i] = (e < n) ? order_key(sc[e]) : 0u;          // 0 is below every finite key
+    for (int i = 0; i < V; ++i) {
+      const int e = i * 64 + lane;
+      f[i] = sc[min(e, max(n - 1, 0))];                // clamped: every load is in the row
+    }
+  };
+  float cur[V], nxt[V];
+  load(row0, cur);
+#pragma unroll 1
+  for (int64_t row = row0; row < row_end; ++row) {
+    if (row + 1 < row_end) load(row + 1, nxt);
+    const int t = (int)((row / h_kv) % n_q);
+    const int jl = (pos0 + t) / kBlock;
+    int32_t* out = blk + row * topk;
+    if (jl + 1 <= topk) {
+      for (int i = lane; i < topk; i += 64) out[i] = (i <= jl) ? i : -1;
+    } else {
+      if (lane == 0) out[kk] = jl;                     // the local block is the largest index
+      if (kk > 0) {
+        const int n = jl;                              // candidates 0..jl-1, n > kk
+        uint32_t key[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) key[i] = (i * 64 + lane < n) ? order_key(cur[i]) : 0u;   // 0: below every key
+        wave_select<V>(key, kk, ck[wave], ci[wave], [&](int pos, uint32_t, int e) { out[pos] = e; });
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) cur[i] = nxt[i];
   }
-  wave_select<V>(key, kk, ck[wave], ci[wave], [&](int pos, uint32_t, int e) { out[pos] = e; });
 }
 
 // Long rows (up to 256*V candidates): a workgroup per row.  Wave w selects the
@@ -235,7 +258,8 @@ __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __re
 template <int V>
 hipError_t launch_v(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
   const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
-  const int64_t wgs = (nrows + kRowsPerWg - 1) / kRowsPerWg;
+  const int64_t per_wg = (int64_t)kRowsPerWg * kRowsPerWave;
+  const int64_t wgs = (nrows + per_wg - 1) / per_wg;
   {
     LaunchTimer timer("block_topk_rows", stream);
     hipLaunchKernelGGL(block_topk_rows<V>, dim3((unsigned)wgs), dim3(kRowsPerWg * 64), 0, stream, bscore, blk,

@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--decode-workload", default="decode_1m_b8")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill-1m", action="store_true",
+                    help="skip the whole 1M-token chunked prefill leg")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-topk-compare", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -375,6 +377,48 @@ def main():
             dec["msa_speedup"] = ms_dd / ms_dec
             log(f"dense decode {ms_dd:.3f} ms -> MSA decode speedup {ms_dd / ms_dec:.2f}x")
         result["decode"] = dec
+
+        # Variable-length decode on the same caches: each sequence holds its
+        # own number of tokens of the 1M capacity.
+        lens = [ds.n_kv, 786432, 524288, 262144, 100000, 10000, 1000, 100][: ds.batch]
+        lens += [ds.n_kv] * (ds.batch - len(lens))
+        lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+        vl_calls = [
+            lambda: M.msa_index_topk_varlen(ds, lens_t, dinp["q_idx"], dinp["k_idx"], dblk, dws_i),
+            lambda: M.msa_sparse_decode_varlen(ds, lens_t, dinp["q"], dinp["k"], dinp["v"], dblk, dout, dlse, dws_s),
+        ]
+        ms_vl, _ = time_calls(torch, vl_calls, dsteps, args.warmup)
+        by_vl = sum(decode_bytes(ds.replace(batch=1, n_kv=n, pos0=n - 1)) for n in lens)
+        result["decode_varlen"] = {"workload": f"{args.decode_workload} caches, per-sequence lengths", "lengths": lens,
+                                   "ms_per_step": ms_vl, "tok_s": ds.batch / (ms_vl * 1e-3),
+                                   "algorithmic_bytes": by_vl, "hbm_gbs": by_vl / (ms_vl * 1e-3) / 1e9,
+                                   "hbm_frac": by_vl / (ms_vl * 1e-3) / PEAK_HBM_BYTES}
+        log(f"varlen decode {ms_vl:.3f} ms over lengths {lens} -> "
+            f"{result['decode_varlen']['hbm_frac'] * 100:.1f}% of HBM peak")
+
+    if not args.no_prefill_1m:
+        if not args.no_decode:
+            del dinp, dws_i, dws_s, dblk, dout, dlse
+            torch.cuda.empty_cache()
+        # A whole 1M-token prefill, chunk by chunk (index branch + sparse
+        # attention per 8,192 queries over the growing causal range).
+        fid, fs = WORKLOADS["prefill_1m_full"]
+        chunk = 8192
+        log(f"1M prefill workload prefill_1m_full: {fs}, chunks of {chunk}")
+        finp = make_inputs(fs, fid, device=dev)
+        fblk = torch.empty((fs.batch, fs.n_q, fs.h_kv, fs.topk), dtype=torch.int32, device=dev)
+        fout = torch.empty((fs.batch, fs.n_q, fs.h_q, fs.d), dtype=torch.bfloat16, device=dev)
+        fws = torch.empty(M.msa_prefill_chunked_workspace_size(fs, chunk), dtype=torch.uint8, device=dev)
+        ms_1m, _ = time_calls(torch, [lambda: M.msa_prefill_chunked(fs, chunk, finp["q_idx"], finp["k_idx"], finp["q"],
+                                                                    finp["k"], finp["v"], fblk, fout, None, fws)],
+                              2, 1)
+        f1 = index_flops(fs) + sparse_flops(fs)
+        result["prefill_1m_chunked"] = {
+            "workload": "prefill_1m_full", "chunk": chunk, "ms": ms_1m, "tok_s": fs.n_q / (ms_1m * 1e-3),
+            "mfma_frac": f1 / (ms_1m * 1e-3) / PEAK_BF16_FLOPS, "algorithmic_flops": f1,
+            "workspace_bytes": int(fws.numel())}
+        log(f"1M prefill in chunks of {chunk}: {ms_1m:.1f} ms -> {fs.n_q / (ms_1m * 1e-3):.4g} tok/s, "
+            f"{result['prefill_1m_chunked']['mfma_frac'] * 100:.1f}% of MFMA peak")
 
     print(json.dumps(result), flush=True)
 

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "launch.h"
@@ -71,6 +72,17 @@ unsigned op_needs(msa_op op) {
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
 float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
+
+// Workspace of msa_prefill_chunked: pooled scores and the sparse-prefill
+// workspace of one chunk (one sequence, `chunk` queries).
+size_t chunked_ws_bytes(const Dims& d, int chunk, size_t* prefill_off) {
+  Dims c = d;
+  c.batch = 1;
+  c.n_q = chunk;
+  const size_t idx = index_ws_bytes(c);
+  if (prefill_off) *prefill_off = idx;
+  return idx + msa::prefill_ws_layout(c).total;
+}
 
 }  // namespace
 
@@ -168,6 +180,95 @@ msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint
       (lse && misaligned(lse)))
     return MSA_ERR_ALIGN;
   const Dims d = to_dims(*dims);
+  const size_t need = msa::sparse_decode_ws_layout(d).total;
+  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_sparse_decode(d, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+size_t msa_prefill_chunked_workspace_size(const msa_dims* dims, int32_t chunk) {
+  if (check_dims(dims, kNeedD | kNeedDIdx | kCsr) != MSA_OK || chunk < 1) return 0;
+  return chunked_ws_bytes(to_dims(*dims), std::min<int>(chunk, std::max(dims->n_q, 1)), nullptr);
+}
+
+msa_status msa_prefill_chunked(const msa_dims* dims, int32_t chunk, const uint16_t* q_idx, const uint16_t* k_idx,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v, float scale,
+                               int32_t* blk_idx, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                               msa_stream stream) {
+  msa_status st = check_dims(dims, kNeedD | kNeedDIdx | kCsr);
+  if (st != MSA_OK) return st;
+  if (chunk < 1) return MSA_ERR_SHAPE;
+  if (empty(*dims)) return MSA_OK;
+  if (!q_idx || !k_idx || !q || !k || !v || !blk_idx || !out) return MSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(k_idx) || misaligned(q) || misaligned(k) || misaligned(v) ||
+      misaligned(blk_idx) || misaligned(out) || (lse && misaligned(lse)))
+    return MSA_ERR_ALIGN;
+  const Dims d = to_dims(*dims);
+  const int cq = std::min(chunk, d.n_q);
+  size_t pre_off = 0;
+  if (!workspace || workspace_bytes < chunked_ws_bytes(d, cq, &pre_off)) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float sc = resolve_scale(scale, d.d);
+  float* bscore = static_cast<float*>(workspace);
+  void* pws = static_cast<char*>(workspace) + pre_off;
+  for (int b = 0; b < d.batch; ++b) {
+    for (int t0 = 0; t0 < d.n_q; t0 += cq) {
+      Dims c = d;
+      c.batch = 1;
+      c.n_q = std::min(cq, d.n_q - t0);
+      c.pos0 = d.pos0 + t0;
+      const int64_t row = (int64_t)b * d.n_q + t0;      // first (sequence, query) row of the chunk
+      const uint16_t* ci = q_idx + row * d.h_kv * d.d_idx;
+      const uint16_t* ck = k_idx + (int64_t)b * d.n_kv * d.d_idx;
+      const uint16_t* cqp = q + row * d.h_q * d.d;
+      const int64_t kv_off = (int64_t)b * d.n_kv * d.h_kv * d.d;
+      int32_t* cb = blk_idx + row * d.h_kv * d.topk;
+      uint16_t* co = out + row * d.h_q * d.d;
+      float* cl = lse ? lse + row * d.h_q : nullptr;
+      st = hip_status(msa::launch_index_scores(c, ci, ck, bscore, s));
+      if (st == MSA_OK) st = hip_status(msa::launch_block_topk(c, bscore, cb, s));
+      if (st == MSA_OK) st = hip_status(msa::launch_sparse_prefill(c, cqp, k + kv_off, v + kv_off, cb, sc, co, cl, pws, s));
+      if (st != MSA_OK) return st;
+    }
+  }
+  return MSA_OK;
+}
+
+msa_status msa_index_topk_varlen(const msa_dims* dims, const int32_t* seq_len, const uint16_t* q_idx,
+                                 const uint16_t* k_idx, int32_t* blk_idx, void* workspace, size_t workspace_bytes,
+                                 msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_INDEX_TOPK) | kDecode);
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  if ((int64_t)dims->n_q * dims->h_kv > 16) return MSA_ERR_UNSUPPORTED;
+  if (!seq_len || !q_idx || !k_idx || !blk_idx) return MSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(k_idx) || misaligned(blk_idx)) return MSA_ERR_ALIGN;
+  Dims d = to_dims(*dims);
+  d.seq_len = seq_len;
+  if (!workspace || workspace_bytes < index_ws_bytes(d)) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* bscore = static_cast<float*>(workspace);
+  st = hip_status(msa::launch_index_scores(d, q_idx, k_idx, bscore, s));
+  if (st != MSA_OK) return st;
+  return hip_status(msa::launch_block_topk(d, bscore, blk_idx, s));
+}
+
+msa_status msa_sparse_decode_varlen(const msa_dims* dims, const int32_t* seq_len, const uint16_t* q,
+                                    const uint16_t* k, const uint16_t* v, const int32_t* blk_idx, float scale,
+                                    uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                    msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_DECODE));
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  if (!seq_len || !q || !k || !v || !blk_idx || !out) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(blk_idx) || misaligned(out) ||
+      (lse && misaligned(lse)))
+    return MSA_ERR_ALIGN;
+  Dims d = to_dims(*dims);
+  d.seq_len = seq_len;
   const size_t need = msa::sparse_decode_ws_layout(d).total;
   if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;

@@ -134,7 +134,8 @@ constexpr int kRowsPerWave = 8;
 template <int V>
 __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* __restrict__ bscore,
                                                                    int32_t* __restrict__ blk, int n_q, int pos0,
-                                                                   int h_kv, int nblk, int topk, int64_t nrows) {
+                                                                   int h_kv, int nblk, int topk, int64_t nrows,
+                                                                   int n_kv, const int* __restrict__ seq_len) {
   __shared__ uint32_t ck[kRowsPerWg][64];
   __shared__ int32_t ci[kRowsPerWg][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -143,8 +144,12 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* 
   const int64_t row_end = min(row0 + (int64_t)kRowsPerWave, nrows);
   const int kk = topk - 1;
   // Candidates of a row: blocks 0 .. jl-1 (0 when the row keeps all its blocks).
+  auto local_block = [&](int64_t row) {
+    const int64_t bt = row / h_kv;
+    return (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + (int)(bt % n_q)) / kBlock;
+  };
   auto n_cand = [&](int64_t row) {
-    const int jl = (pos0 + (int)((row / h_kv) % n_q)) / kBlock;
+    const int jl = local_block(row);
     return jl + 1 <= topk ? 0 : jl;
   };
   auto load = [&](int64_t row, float (&f)[V]) {
@@ -161,8 +166,7 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* 
 #pragma unroll 1
   for (int64_t row = row0; row < row_end; ++row) {
     if (row + 1 < row_end) load(row + 1, nxt);
-    const int t = (int)((row / h_kv) % n_q);
-    const int jl = (pos0 + t) / kBlock;
+    const int jl = local_block(row);
     int32_t* out = blk + row * topk;
     if (jl + 1 <= topk) {
       for (int i = lane; i < topk; i += 64) out[i] = (i <= jl) ? i : -1;
@@ -189,7 +193,8 @@ constexpr int kWgWaves = 4;
 template <int V>
 __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __restrict__ bscore,
                                                                int32_t* __restrict__ blk, int n_q, int pos0,
-                                                               int h_kv, int nblk, int topk) {
+                                                               int h_kv, int nblk, int topk, int n_kv,
+                                                               const int* __restrict__ seq_len) {
   __shared__ uint32_t ck[kWgWaves][64];
   __shared__ int32_t ci[kWgWaves][64];
   __shared__ uint32_t cand_k[kWgWaves][32];
@@ -199,8 +204,8 @@ __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __re
   __shared__ int32_t cat_i[kWgWaves * 32];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = blockIdx.x;
-  const int t = (int)((row / h_kv) % n_q);
-  const int jl = (pos0 + t) / kBlock;
+  const int64_t bt = row / h_kv;
+  const int jl = (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + (int)(bt % n_q)) / kBlock;
   int32_t* out = blk + row * topk;
   if (jl + 1 <= topk) {                                // whole workgroup leaves together
     for (int i = threadIdx.x; i < topk; i += kWgWaves * 64) out[i] = (i <= jl) ? i : -1;
@@ -263,7 +268,7 @@ hipError_t launch_v(const Dims& d, const float* bscore, int32_t* blk, hipStream_
   {
     LaunchTimer timer("block_topk_rows", stream);
     hipLaunchKernelGGL(block_topk_rows<V>, dim3((unsigned)wgs), dim3(kRowsPerWg * 64), 0, stream, bscore, blk,
-                       d.n_q, d.pos0, d.h_kv, d.nblk(), d.topk, nrows);
+                       d.n_q, d.pos0, d.h_kv, d.nblk(), d.topk, nrows, d.n_kv, d.seq_len);
   }
   return hipGetLastError();
 }
@@ -274,7 +279,7 @@ hipError_t launch_wg(const Dims& d, const float* bscore, int32_t* blk, hipStream
   {
     LaunchTimer timer("block_topk_wg", stream);
     hipLaunchKernelGGL(block_topk_wg<V>, dim3((unsigned)nrows), dim3(kWgWaves * 64), 0, stream, bscore, blk, d.n_q,
-                       d.pos0, d.h_kv, d.nblk(), d.topk);
+                       d.pos0, d.h_kv, d.nblk(), d.topk, d.n_kv, d.seq_len);
   }
   return hipGetLastError();
 }
@@ -282,7 +287,7 @@ hipError_t launch_wg(const Dims& d, const float* bscore, int32_t* blk, hipStream
 }  // namespace
 
 hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
-  const int jl_max = (d.pos0 + d.n_q - 1) / kBlock;      // most candidates any row has
+  const int jl_max = d.seq_len ? (d.n_kv - 1) / kBlock : (d.pos0 + d.n_q - 1) / kBlock;   // most candidates of a row
   const int per_lane = (jl_max + 63) / 64;
   if (per_lane <= 1) return launch_v<1>(d, bscore, blk, stream);
   if (per_lane <= 2) return launch_v<2>(d, bscore, blk, stream);

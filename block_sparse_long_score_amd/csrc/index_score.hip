@@ -239,12 +239,13 @@ constexpr int kSkinnyBlocksPerWave = 4;
 template <int DI>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void index_scores_skinny(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, float* __restrict__ bscore,
-    int n_q, int n_kv, int pos0, int h_kv, int nblk) {
+    int n_q, int n_kv, int pos0, int h_kv, int nblk, const int* __restrict__ seq_len) {
   constexpr int CC = DI / 32;
   const int b = blockIdx.y;
   const int nrows = n_q * h_kv;                         // <= 16
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, cl = lane & 15;
+  pos0 = seq_pos0(seq_len, b, pos0, n_q, n_kv);
   const int jmax = (pos0 + n_q - 1) / kBlock;
   const int jw = (blockIdx.x * kSkinnyWaves + wave) * kSkinnyBlocksPerWave;
   if (jw > jmax) return;
@@ -316,13 +317,13 @@ hipError_t launch_index_scores_t(const Dims& d, const uint16_t* q_idx, const uin
   const int nblk = d.nblk();
   const int64_t nrows = (int64_t)d.n_q * d.h_kv;
   if (nrows <= 16) {
-    const int jmax = (d.pos0 + d.n_q - 1) / kBlock;
+    const int jmax = d.seq_len ? (d.n_kv - 1) / kBlock : (d.pos0 + d.n_q - 1) / kBlock;
     const int per_wg = kSkinnyWaves * kSkinnyBlocksPerWave;
     dim3 grid((jmax + per_wg) / per_wg, d.batch);
     {
       LaunchTimer timer("index_scores_skinny", stream);
       hipLaunchKernelGGL(index_scores_skinny<DI>, grid, dim3(kSkinnyWaves * 64), 0, stream, q_idx, k_idx, bscore,
-                         d.n_q, d.n_kv, d.pos0, d.h_kv, nblk);
+                         d.n_q, d.n_kv, d.pos0, d.h_kv, nblk, d.seq_len);
     }
   } else {
     const int64_t tiles = (nrows + kTiledRows - 1) / kTiledRows;

@@ -29,6 +29,11 @@ int device_cu_count();
 
 struct Dims {
   int batch, n_q, n_kv, pos0, h_q, h_kv, d, d_idx, block, topk;
+  // Variable-length decode: per-sequence lengths (device array of `batch`
+  // int32) or nullptr.  With it, sequence b holds seq_len[b] tokens of its
+  // n_kv-token cache and its n_q queries sit at seq_len[b] - n_q ...; pos0 is
+  // not used.
+  const int* seq_len = nullptr;
   int nblk() const { return (n_kv + block - 1) / block; }
   int group() const { return h_q / h_kv; }
 };

@@ -57,6 +57,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Position of sequence b's first query: pos0, or with per-sequence lengths
+// seq_len[b] - n_q, the length clamped into [n_q, n_kv] so that every access
+// stays inside the cache whatever the array holds.
+__device__ __forceinline__ int seq_pos0(const int* __restrict__ seq_len, int b, int pos0, int n_q, int n_kv) {
+  if (!seq_len) return pos0;
+  return min(max(seq_len[b], n_q), n_kv) - n_q;
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int m) {
   return __shfl_xor(v, m, 64);
 }

@@ -323,15 +323,16 @@ template <int D, int G>
 __global__ __launch_bounds__(kAttnThreads) void sparse_decode_blocks(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ blk, uint16_t* __restrict__ part_o, float* __restrict__ part_ml, int n_kv, int pos0,
-    int h_q, int h_kv, int topk, int64_t units, float sl2) {
+    int h_q, int h_kv, int topk, int64_t units, float sl2, const int* __restrict__ seq_len) {
   __shared__ float pt[kAttnThreads / 64][kBlock * 16 + 16];
   const int wave = threadIdx.x >> 6;
   const int64_t unit = (int64_t)blockIdx.x * (kAttnThreads / 64) + wave;   // (b, g, slot)
   if (unit >= units) return;
-  const int j = blk[unit];
-  if (j < 0 || j > pos0 / kBlock) return;              // padding, or not a causal block
   const int64_t bg = unit / topk;
   const int g = (int)(bg % h_kv), b = (int)(bg / h_kv);
+  pos0 = seq_pos0(seq_len, b, pos0, 1, n_kv);
+  const int j = blk[unit];
+  if (j < 0 || j > pos0 / kBlock) return;              // padding, or not a causal block
   const int64_t head0 = ((int64_t)b * n_kv * h_kv + g) * D;
   decode_attend<D, G>(q + ((int64_t)b * h_q + g * G) * D, k + head0, v + head0, (int64_t)h_kv * D, n_kv, pos0, j,
                       j + 1, sl2, pt[wave], part_o + unit * G * D, part_ml + unit * G * 2);
@@ -348,7 +349,8 @@ __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict
                                                       const float* __restrict__ part_ml,
                                                       const int32_t* __restrict__ blk, uint16_t* __restrict__ out,
                                                       float* __restrict__ lse, int64_t nrows, int n_q, int pos0,
-                                                      int h_q, int G, int nslot, int per) {
+                                                      int h_q, int G, int nslot, int per, int n_kv,
+                                                      const int* __restrict__ seq_len) {
   constexpr int TPR = D / 8;                           // threads per (token, head) row
   const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // (b * n_q + t) * h_q + h
   if (row >= nrows) return;
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict
   const int t = (int)(bt % n_q);
   const int g = h / G, hh = h % G;
   const int h_kv = h_q / G;
-  const int jl = (pos0 + t) / kBlock;
+  const int jl = (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + t) / kBlock;
   const int64_t unit0 = (bt * h_kv + g) * nslot;
   const int32_t* brow = blk ? blk + unit0 : nullptr;
   // One pass with a running maximum: slots go in batches of 8, each thread
@@ -424,7 +426,7 @@ hipError_t launch_merge_t(const Dims& d, const uint16_t* part_o, const float* pa
   {
     LaunchTimer timer("merge_partials", stream);
     hipLaunchKernelGGL(merge_partials<D>, dim3((unsigned)wgs), dim3(256), 0, stream, part_o, part_ml, blk, out, lse,
-                       nrows, d.n_q, d.pos0, d.h_q, d.group(), nslot, per);
+                       nrows, d.n_q, d.pos0, d.h_q, d.group(), nslot, per, d.n_kv, d.seq_len);
   }
   return hipGetLastError();
 }
@@ -486,7 +488,7 @@ hipError_t launch_decode_t(const Dims& d, const uint16_t* q, const uint16_t* k, 
   {
     LaunchTimer timer("sparse_decode_blocks", stream);
     hipLaunchKernelGGL((sparse_decode_blocks<D, G>), dim3((unsigned)wgs), dim3(kAttnThreads), 0, stream, q, k, v, blk,
-                       part_o, part_ml, d.n_kv, d.pos0, d.h_q, d.h_kv, d.topk, units, sl2);
+                       part_o, part_ml, d.n_kv, d.pos0, d.h_q, d.h_kv, d.topk, units, sl2, d.seq_len);
   }
   return launch_merge_t<D>(d, part_o, part_ml, blk, out, lse, d.topk, 1, stream);
 }

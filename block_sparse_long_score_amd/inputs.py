@@ -63,6 +63,8 @@ WORKLOADS = {
     "prefill_chunk_1m": (5, Shape(1, 8192, 1048576, 1040384, 64, 8, 128, 128)),
     # 8 single-token decode queries against 1,048,576-token caches
     "decode_1m_b8": (6, Shape(8, 1, 1048576, 1048575, 64, 8, 128, 128)),
+    # a whole 1,048,576-token causal prefill (run in chunks of 8,192 queries)
+    "prefill_1m_full": (7, Shape(1, 1048576, 1048576, 0, 64, 8, 128, 128)),
 }
 
 

@@ -45,6 +45,10 @@ EXPORTED = (
     "msa_dense_gqa",
     "msa_profile_begin",
     "msa_profile_end",
+    "msa_index_topk_varlen",
+    "msa_sparse_decode_varlen",
+    "msa_prefill_chunked_workspace_size",
+    "msa_prefill_chunked",
 )
 
 
@@ -91,10 +95,16 @@ def lib() -> ctypes.CDLL:
     L.msa_sparse_prefill.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
     L.msa_sparse_decode.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
     L.msa_dense_gqa.argtypes = [D, P, P, P, F, P, P, P, S, VP]
+    L.msa_index_topk_varlen.argtypes = [D, P, P, P, P, P, S, VP]
+    L.msa_sparse_decode_varlen.argtypes = [D, P, P, P, P, P, F, P, P, P, S, VP]
+    L.msa_prefill_chunked_workspace_size.argtypes = [D, ctypes.c_int32]
+    L.msa_prefill_chunked_workspace_size.restype = S
+    L.msa_prefill_chunked.argtypes = [D, ctypes.c_int32, P, P, P, P, P, F, P, P, P, P, S, VP]
     L.msa_profile_begin.argtypes = []
     L.msa_profile_end.argtypes = [ctypes.POINTER(MsaKernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     for fn in EXPORTED[2:]:
-        getattr(L, fn).restype = I32
+        if fn != "msa_prefill_chunked_workspace_size":
+            getattr(L, fn).restype = I32
     _lib = L
     return L
 
@@ -227,3 +237,63 @@ def msa_profile_end(capacity: int = 64) -> dict:
     n = ctypes.c_int32(0)
     _raise(lib().msa_profile_end(buf, capacity, ctypes.byref(n)), "msa_profile_end")
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n.value, capacity))}
+
+
+def _check_seq_len(s: Shape, seq_len) -> None:
+    _check(seq_len, "seq_len", torch.int32, (s.batch,))
+    if seq_len is None:
+        raise ValueError("seq_len: required")
+
+
+def msa_index_topk_varlen(s: Shape, seq_len, q_idx, k_idx, blk_idx, workspace, stream=None) -> None:
+    """msa_index_topk for a decode batch whose sequences hold seq_len[b] tokens of an s.n_kv-token cache."""
+    _check_seq_len(s, seq_len)
+    _check(q_idx, "q_idx", torch.bfloat16, (s.batch, 1, s.h_kv, s.d_idx))
+    _check(k_idx, "k_idx", torch.bfloat16, (s.batch, s.n_kv, s.d_idx))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, 1, s.h_kv, s.topk))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_index_topk_varlen(ctypes.byref(d), _ptr(seq_len), _ptr(q_idx), _ptr(k_idx), _ptr(blk_idx), wp, wb,
+                                     _stream(stream))
+    _raise(st, "msa_index_topk_varlen")
+
+
+def msa_sparse_decode_varlen(s: Shape, seq_len, q, k, v, blk_idx, out, lse=None, workspace=None, scale: float = 0.0,
+                             stream=None) -> None:
+    """msa_sparse_decode for a batch whose sequences hold seq_len[b] tokens of an s.n_kv-token cache."""
+    _check_seq_len(s, seq_len)
+    _check(q, "q", torch.bfloat16, (s.batch, 1, s.h_q, s.d))
+    _check(k, "k", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(v, "v", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, 1, s.h_kv, s.topk))
+    _check(out, "out", torch.bfloat16, (s.batch, 1, s.h_q, s.d))
+    _check(lse, "lse", torch.float32, (s.batch, 1, s.h_q))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_sparse_decode_varlen(ctypes.byref(d), _ptr(seq_len), _ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx),
+                                        ctypes.c_float(scale), _ptr(out), _ptr(lse), wp, wb, _stream(stream))
+    _raise(st, "msa_sparse_decode_varlen")
+
+
+def msa_prefill_chunked_workspace_size(s: Shape, chunk: int) -> int:
+    d = dims_of(s)
+    return int(lib().msa_prefill_chunked_workspace_size(ctypes.byref(d), chunk))
+
+
+def msa_prefill_chunked(s: Shape, chunk: int, q_idx, k_idx, q, k, v, blk_idx, out, lse=None, workspace=None,
+                        scale: float = 0.0, stream=None) -> None:
+    """Index branch + sparse prefill chunk by chunk (chunk query tokens each) over the whole call."""
+    _check(q_idx, "q_idx", torch.bfloat16, (s.batch, s.n_q, s.h_kv, s.d_idx))
+    _check(k_idx, "k_idx", torch.bfloat16, (s.batch, s.n_kv, s.d_idx))
+    _check(q, "q", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(k, "k", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(v, "v", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, s.n_q, s.h_kv, s.topk))
+    _check(out, "out", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(lse, "lse", torch.float32, (s.batch, s.n_q, s.h_q))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_prefill_chunked(ctypes.byref(d), chunk, _ptr(q_idx), _ptr(k_idx), _ptr(q), _ptr(k), _ptr(v),
+                                   ctypes.c_float(scale), _ptr(blk_idx), _ptr(out), _ptr(lse), wp, wb,
+                                   _stream(stream))
+    _raise(st, "msa_prefill_chunked")

@@ -149,6 +149,51 @@ msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint
                              const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
                              size_t workspace_bytes, msa_stream stream);
 
+/* Whole-sequence prefill in chunks of `chunk` query tokens: for each sequence
+ * and each chunk of its n_q queries (positions pos0 + t0 .. pos0 + t0 + chunk - 1,
+ * the last chunk possibly shorter) the index branch (scores, block max-pool,
+ * top-k) and the main branch (sparse attention) run on that chunk alone
+ * against the sequence's n_kv-token cache, as a serving system extends a
+ * context chunk by chunk (lefilia.fr article: 1M-token contexts; yhxrc.cn
+ * article, "第一步：索引分支" and "第二步：稀疏分支").  Every query row's
+ * result depends only on its own row, so the outputs equal those of
+ * msa_index_topk followed by msa_sparse_prefill on the whole call, while the
+ * workspace holds one chunk's pooled scores and partials: a 1,048,576-token
+ * prefill, whose one-shot pooled scores alone would take 256 GiB, runs in
+ * chunks of 8,192 queries (64 heads) in about 4.1 GiB.
+ *   q_idx, k_idx, q, k, v, blk_idx, out, lse   as for msa_index_topk and
+ *            msa_sparse_prefill (blk_idx is an output here, lse may be NULL)
+ *   chunk    >= 1 query tokens per chunk (MSA_ERR_SHAPE otherwise)
+ *   workspace >= msa_prefill_chunked_workspace_size(dims, chunk); reused by
+ *            every chunk, in stream order. */
+size_t msa_prefill_chunked_workspace_size(const msa_dims* dims, int32_t chunk);
+msa_status msa_prefill_chunked(const msa_dims* dims, int32_t chunk, const uint16_t* q_idx, const uint16_t* k_idx,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v, float scale,
+                               int32_t* blk_idx, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                               msa_stream stream);
+
+/* Variable-length decode (a batch of sequences of different lengths in one
+ * call): as msa_index_topk / msa_sparse_decode with n_q == 1, except that
+ * sequence b holds seq_len[b] tokens of its n_kv-token cache (k_idx, k, v keep
+ * the [batch][n_kv]... layout, n_kv being the capacity) and its query sits at
+ * p = seq_len[b] - 1; dims->pos0 is not used (it must still satisfy
+ * pos0 + 1 <= n_kv).  Blocks, the local block and the -1 padding follow from
+ * each sequence's own p; pooled-score rows in the index workspace are valid up
+ * to each sequence's local block.
+ *   seq_len  [batch] int32 device array, each in [1, n_kv]; the kernels clamp
+ *            values outside that range into it (no access leaves the cache),
+ *            the results for such a sequence are then those of the clamped
+ *            length.
+ * Same workspaces as msa_index_topk and msa_sparse_decode.  The index step
+ * supports n_q * h_kv <= 16 (MSA_ERR_UNSUPPORTED otherwise). */
+msa_status msa_index_topk_varlen(const msa_dims* dims, const int32_t* seq_len, const uint16_t* q_idx,
+                                 const uint16_t* k_idx, int32_t* blk_idx, void* workspace, size_t workspace_bytes,
+                                 msa_stream stream);
+msa_status msa_sparse_decode_varlen(const msa_dims* dims, const int32_t* seq_len, const uint16_t* q,
+                                    const uint16_t* k, const uint16_t* v, const int32_t* blk_idx, float scale,
+                                    uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                    msa_stream stream);
+
 /* Dense causal GQA, the comparator: as msa_sparse_prefill with every s <= p
  * visible (hamidun.com, "Como o MSA funciona": standard GQA attends every
  * key).  n_q == 1 takes a split-key decode path that needs workspace; n_q > 1

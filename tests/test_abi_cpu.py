@@ -141,3 +141,53 @@ def test_workspace_sizes_cover_their_buffers():
             assert n_pre >= s.batch * s.n_q * s.h_kv * s.topk * s.group * (s.d * 2 + 8), name
             assert M.msa_workspace_size(M.MSA_OP_DENSE_GQA, s) == 0
     assert M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, Shape(1, 10, 5, 0, 8, 2, 128, 128)) == 0   # rejected dims
+
+
+def varlen_index_call(d, lens=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, blk=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return M.lib().msa_index_topk_varlen(ctypes.byref(d), lens, a["q"], a["k"], a["blk"], a["ws"], a["wsb"], None)
+
+
+def varlen_decode_call(d, lens=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, blk=FAKE, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return M.lib().msa_sparse_decode_varlen(ctypes.byref(d), lens, a["q"], a["k"], a["v"], a["blk"],
+                                            ctypes.c_float(0.0), a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_varlen_argument_checks():
+    d1 = dims(n_q=1, pos0=4095)
+    assert varlen_index_call(d1, lens=None) == NULL
+    assert varlen_decode_call(d1, lens=None) == NULL
+    assert varlen_index_call(d1, blk=None) == NULL
+    assert varlen_decode_call(d1, out=None) == NULL
+    assert varlen_index_call(dims(n_q=2, pos0=4094)) == SHAPE           # one query per sequence
+    assert varlen_decode_call(dims(n_q=2, pos0=4094)) == SHAPE
+    assert varlen_index_call(dims(n_q=1, pos0=4095, h_q=64, h_kv=32)) == UNSUP   # > 16 index rows
+    assert varlen_index_call(d1, q=ODD) == ALIGN
+    assert varlen_decode_call(d1, lse=ODD) == ALIGN
+    need = M.lib().msa_workspace_size(M.MSA_OP_INDEX_TOPK, ctypes.byref(d1))
+    assert varlen_index_call(d1, wsb=need - 1) == WS
+    need_d = M.lib().msa_workspace_size(M.MSA_OP_SPARSE_DECODE, ctypes.byref(d1))
+    assert varlen_decode_call(d1, wsb=need_d - 1) == WS
+    assert varlen_index_call(dims(n_q=1, pos0=4095, batch=0), lens=None, q=None) == OK   # empty: no-op
+
+
+def test_chunked_prefill_argument_checks():
+    lib = M.lib()
+    d = dims()
+    call = lambda dd, chunk=64, ws=FAKE, wsb=1 << 40, **kw: lib.msa_prefill_chunked(
+        ctypes.byref(dd), chunk, kw.get("qi", FAKE), FAKE, kw.get("q", FAKE), FAKE, FAKE, ctypes.c_float(0.0),
+        kw.get("blk", FAKE), FAKE, kw.get("lse", None), ws, wsb, None)
+    assert call(d, chunk=0) == SHAPE
+    assert call(d, qi=None) == NULL
+    assert call(d, blk=None) == NULL
+    assert call(d, lse=ODD) == ALIGN
+    need = lib.msa_prefill_chunked_workspace_size(ctypes.byref(d), 64)
+    assert need > 0 and call(d, wsb=need - 1) == WS
+    assert lib.msa_prefill_chunked_workspace_size(ctypes.byref(d), 0) == 0
+    # the workspace grows with the chunk, not with the call
+    big = dims(n_q=4096, pos0=0)
+    assert lib.msa_prefill_chunked_workspace_size(ctypes.byref(big), 64) == need
+    assert call(dims(n_q=0), qi=None, q=None, blk=None, ws=None) == OK

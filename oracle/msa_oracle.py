@@ -38,6 +38,22 @@ Readings where the pages are silent (each also listed in the design notes):
   r8  a decode query sits at p = n_kv - 1 (its own K/V are already cached);
   r9  block j covers tokens [j*B, min((j+1)*B, n_kv)).
 
+Index-branch training target (forward only; Notion notes
+"Minimax-sparse-Attention", the "KL Loss Alignment" and "Detached Gradients"
+points: the main branch's attention distribution is the target the index branch
+is trained to imitate through a KL divergence, with no gradient flowing between
+the branches).  Readings:
+  r14 the main branch's distribution for one (query, group) lives on its
+      selected blocks: each head's softmax weights summed per block, then
+      averaged over the group's heads (the index branch has one query per
+      group, so one distribution per group);
+  r15 the index branch's distribution is a softmax of idx_scale times the
+      pooled block scores over the same selected blocks (the pages name no
+      temperature, so idx_scale is the caller's);
+  r16 the loss is KL(target || index) in nats, with 0 log 0 = 0;
+  r17 "detached": the target is returned as a plain value; nothing here
+      differentiates anything.
+
 Array conventions (all numpy, float64 inside):
   q_idx [batch][n_q][Hkv][d_idx]     k_idx [batch][n_kv][d_idx]
   q     [batch][n_q][Hq][d]          k, v  [batch][n_kv][Hkv][d]
@@ -266,3 +282,89 @@ def msa_forward(q_idx, k_idx, q, k, v, pos0: int, block: int, topk: int,
     bscore, blk = msa_index_topk(q_idx, k_idx, pos0, block, topk)
     out, lse = msa_sparse_attention(q, k, v, blk, pos0, block, scale)
     return out, lse, blk, bscore
+
+
+# ----------------------------------------------------------------------------
+# Index-branch training target (forward only)
+# ----------------------------------------------------------------------------
+
+def block_mass_row(q_heads: np.ndarray, keys_seq: np.ndarray, sel: np.ndarray, p: int,
+                   block: int, scale: float) -> np.ndarray:
+    """Main-branch attention mass per selected block for one (query, group).
+
+    Notion notes "Minimax-sparse-Attention", "KL Loss Alignment" (the main
+    branch's attention distribution is the target), readings r14 and r6.
+    q_heads [G][d] are the group's query heads, keys_seq [n_kv][d] the group's
+    keys.  For each head the softmax weights over the visible tokens are summed
+    per selected block; the result is the mean over heads, one value per slot
+    of `sel` (0 for -1 padding).
+    """
+    n_kv = keys_seq.shape[0]
+    pos = visible_positions(sel, p, block, n_kv)
+    q = np.asarray(q_heads, dtype=np.float64)
+    z = scale * (q @ np.asarray(keys_seq[pos], dtype=np.float64).T)     # [G][n]
+    w = np.exp(z - np.max(z, axis=1, keepdims=True))
+    w /= np.sum(w, axis=1, keepdims=True)
+    owner = pos // block
+    mass = np.zeros(len(sel), dtype=np.float64)
+    for slot, j in enumerate(sel):
+        if j >= 0:
+            mass[slot] = np.mean(np.sum(w[:, owner == j], axis=1))
+    return mass
+
+
+def msa_block_target(q: np.ndarray, k: np.ndarray, blk_idx: np.ndarray, pos0: int,
+                     block: int, scale: float | None = None) -> np.ndarray:
+    """The target distribution for every (batch, query, group).
+
+    Returns float64 [b][n_q][Hkv][topk]; each row sums to 1 over its selected
+    blocks and is 0 at padding (readings r14, r17).
+    """
+    b, n_q, h_q, d = q.shape
+    h_kv = k.shape[2]
+    group = h_q // h_kv
+    if scale is None:
+        scale = default_scale(d)
+    topk = blk_idx.shape[-1]
+    target = np.zeros((b, n_q, h_kv, topk), dtype=np.float64)
+    for bi in range(b):
+        for i in range(n_q):
+            for g in range(h_kv):
+                target[bi, i, g] = block_mass_row(q[bi, i, g * group:(g + 1) * group], k[bi, :, g],
+                                                  blk_idx[bi, i, g], pos0 + i, block, scale)
+    return target
+
+
+def index_kl_row(target_row: np.ndarray, pooled_row: np.ndarray, sel: np.ndarray,
+                 idx_scale: float) -> float:
+    """KL(target || index distribution) for one (query, group), in nats.
+
+    Readings r15 and r16: the index distribution is the softmax of
+    idx_scale * pooled[j] over the selected blocks j; slots with -1 padding
+    take no part; a zero target term contributes nothing.
+    """
+    live = [slot for slot, j in enumerate(sel) if j >= 0]
+    a = np.array([idx_scale * float(pooled_row[sel[slot]]) for slot in live], dtype=np.float64)
+    log_q = a - (np.max(a) + np.log(np.sum(np.exp(a - np.max(a)))))
+    kl = 0.0
+    for n, slot in enumerate(live):
+        t = float(target_row[slot])
+        if t > 0.0:
+            kl += t * (math.log(t) - log_q[n])
+    return kl
+
+
+def msa_index_kl(target: np.ndarray, bscore: np.ndarray, blk_idx: np.ndarray,
+                 idx_scale: float) -> np.ndarray:
+    """KL(target || index distribution) for every (batch, query, group).
+
+    target [b][n_q][Hkv][topk], bscore [b][n_q][Hkv][nblk] pooled index scores,
+    blk_idx [b][n_q][Hkv][topk].  Returns float64 [b][n_q][Hkv].
+    """
+    b, n_q, h_kv, _ = target.shape
+    kl = np.zeros((b, n_q, h_kv), dtype=np.float64)
+    for bi in range(b):
+        for i in range(n_q):
+            for g in range(h_kv):
+                kl[bi, i, g] = index_kl_row(target[bi, i, g], bscore[bi, i, g], blk_idx[bi, i, g], idx_scale)
+    return kl

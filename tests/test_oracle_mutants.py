@@ -124,3 +124,67 @@ def test_wrong_head_group_map_is_caught(monkeypatch):
 def test_missing_scale_is_caught(monkeypatch):
     monkeypatch.setattr(O, "softmax_attention", mut_attention_no_scale)
     assert fails(TA.test_dense_matches_torch_sdpa, 4, 1)
+
+
+# ---- index-branch training target ------------------------------------------
+
+from tests import test_oracle_target as TT   # noqa: E402
+
+ORIG_MASS_ROW = O.block_mass_row
+ORIG_KL_ROW = O.index_kl_row
+
+
+def mut_mass_summed_over_heads(q_heads, keys_seq, sel, p, block, scale):
+    return ORIG_MASS_ROW(q_heads, keys_seq, sel, p, block, scale) * len(q_heads)
+
+
+def mut_mass_ignores_causality(q_heads, keys_seq, sel, p, block, scale):
+    last = max(int(j) for j in sel)
+    return ORIG_MASS_ROW(q_heads, keys_seq, sel, max(p, (last + 1) * block - 1), block, scale)
+
+
+def mut_mass_first_head_only(q_heads, keys_seq, sel, p, block, scale):
+    return ORIG_MASS_ROW(q_heads[:1], keys_seq, sel, p, block, scale)
+
+
+def mut_kl_reversed(target_row, pooled_row, sel, idx_scale):
+    live = [s for s, j in enumerate(sel) if j >= 0]
+    a = np.array([idx_scale * pooled_row[sel[s]] for s in live])
+    qd = np.exp(a - a.max())
+    qd /= qd.sum()
+    t = np.array([target_row[s] for s in live])
+    return float(np.sum(qd * (np.log(qd) - np.log(np.maximum(t, 1e-300)))))
+
+
+def mut_kl_softmax_over_all_blocks(target_row, pooled_row, sel, idx_scale):
+    live = [s for s, j in enumerate(sel) if j >= 0]
+    jl = max(int(sel[s]) for s in live)
+    a = idx_scale * np.asarray(pooled_row[: jl + 1], dtype=np.float64)
+    log_q = a - (a.max() + np.log(np.sum(np.exp(a - a.max()))))
+    return float(sum(target_row[s] * (math.log(target_row[s]) - log_q[sel[s]]) for s in live if target_row[s] > 0))
+
+
+def test_target_summed_over_heads_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "block_mass_row", mut_mass_summed_over_heads)
+    assert fails(TT.test_target_rows_are_distributions_on_the_selection, 8, 2, 90, 4)
+
+
+def test_target_without_causal_mask_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "block_mass_row", mut_mass_ignores_causality)
+    assert fails(TT.test_zero_query_gives_share_of_visible_tokens)
+    assert fails(TT.test_target_matches_sdpa_with_block_indicator_values, 8, 2)
+
+
+def test_target_from_one_head_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "block_mass_row", mut_mass_first_head_only)
+    assert fails(TT.test_target_matches_sdpa_with_block_indicator_values, 8, 2)
+
+
+def test_reversed_kl_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "index_kl_row", mut_kl_reversed)
+    assert fails(TT.test_kl_matches_scipy_entropy)
+
+
+def test_index_softmax_over_all_blocks_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "index_kl_row", mut_kl_softmax_over_all_blocks)
+    assert fails(TT.test_kl_zero_when_index_matches_target_and_shift_invariant)

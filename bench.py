@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -48,6 +49,7 @@ def parse():
                     help="skip the whole 1M-token chunked prefill leg")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-topk-compare", action="store_true")
+    ap.add_argument("--no-target", action="store_true", help="skip the index-branch target (KL) leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -94,6 +96,17 @@ def topk_bytes(s) -> float:
     p = causal_positions(s)
     cand = (p // s.block).sum()
     return float(s.batch * s.h_kv * (cand * 4 + s.n_q * s.topk * 4))
+
+
+def target_bytes(s) -> float:
+    """Index-branch target: per (query, group) row, each live slot's partial
+    (m, l) for the G heads and its pooled index score; the row's selection read
+    and target written, and its KL."""
+    import numpy as np
+    p = causal_positions(s)
+    live = np.minimum(p // s.block + 1, s.topk).sum()
+    rows = s.n_q
+    return float(s.batch * s.h_kv * (live * (s.group * 8 + 4) + rows * (s.topk * 8 + 4)))
 
 
 def decode_bytes(s) -> float:
@@ -316,6 +329,25 @@ def main():
                                    "speedup": ms_torch / ms_topk,
                                    "note": "torch.topk over the full pooled rows, k-1 per row; timing only"}
         log(f"top-k: msa {ms_topk:.3f} ms vs torch.topk {ms_torch:.3f} ms")
+
+    if not args.no_target:
+        # Index-branch training target (forward only): msa_sparse_prefill plus
+        # block_target_kl on the same inputs; block_target_kl's own time from
+        # the library's event pairs.
+        target = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.float32, device=dev)
+        kl = torch.empty((s.batch, s.n_q, s.h_kv), dtype=torch.float32, device=dev)
+        idx_scale = 1.0 / math.sqrt(s.d_idx)
+        ms_t, _, kt = time_calls(torch, [lambda: M.msa_sparse_prefill_target(
+            s, inp["q"], inp["k"], inp["v"], blk, bscore, target, kl, out, lse, ws, idx_scale=idx_scale)], 3, 1, M)
+        n, tot = kt["block_target_kl"]
+        ms_k = tot / n
+        tb = target_bytes(s)
+        result["index_target"] = {"ms_call": ms_t, "block_target_kl_ms": ms_k, "algorithmic_bytes": tb,
+                                  "hbm_gbs": tb / (ms_k * 1e-3) / 1e9, "hbm_frac": tb / (ms_k * 1e-3) / PEAK_HBM_BYTES,
+                                  "extra_over_sparse_prefill_ms": ms_t - ms_sparse}
+        log(f"index target: call {ms_t:.3f} ms, block_target_kl {ms_k:.3f} ms "
+            f"({tb / (ms_k * 1e-3) / PEAK_HBM_BYTES:.1%} of HBM peak)")
+        del target, kl
 
     if not args.no_dense:
         dout = torch.empty_like(out)

@@ -169,6 +169,27 @@ msa_status msa_sparse_prefill(const msa_dims* dims, const uint16_t* q, const uin
                                                static_cast<hipStream_t>(stream)));
 }
 
+msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const int32_t* blk_idx, const float* bscore, float idx_scale, float scale,
+                                     uint16_t* out, float* lse, float* target, float* kl, void* workspace,
+                                     size_t workspace_bytes, msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_PREFILL));
+  if (st != MSA_OK) return st;
+  if (!std::isfinite(idx_scale)) return MSA_ERR_SHAPE;
+  if (empty(*dims)) return MSA_OK;
+  if (!q || !k || !v || !blk_idx || !bscore || !out || !target || !kl) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(blk_idx) || misaligned(bscore) ||
+      misaligned(out) || misaligned(target) || misaligned(kl) || (lse && misaligned(lse)))
+    return MSA_ERR_ALIGN;
+  const Dims d = to_dims(*dims);
+  const size_t need = msa::prefill_ws_layout(d).total;
+  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_sparse_prefill_target(d, q, k, v, blk_idx, resolve_scale(scale, d.d), bscore,
+                                                      idx_scale, out, lse, target, kl, workspace,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
                              size_t workspace_bytes, msa_stream stream) {

@@ -60,6 +60,11 @@ hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk_id
 hipError_t launch_sparse_prefill(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* ws,
                                  hipStream_t stream);
+// msa_sparse_prefill, then the index-branch target and its KL from the partials.
+hipError_t launch_sparse_prefill_target(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        const int32_t* blk, float scale, const float* bscore, float idx_scale,
+                                        uint16_t* out, float* lse, float* target, float* kl, void* ws,
+                                        hipStream_t stream);
 hipError_t launch_sparse_decode(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* ws,
                                 hipStream_t stream);

@@ -431,6 +431,109 @@ hipError_t launch_merge_t(const Dims& d, const uint16_t* part_o, const float* pa
   return hipGetLastError();
 }
 
+// ------------------------------------------------- index-branch target ------
+
+// Notion notes "Minimax-sparse-Attention", "KL Loss Alignment": the main
+// branch's attention distribution over blocks is the target the index branch
+// imitates.  For one (b, t, g) row, R lanes hold its slots.  Head h's mass on
+// slot s is w_hs / L_h with w_hs = exp2(m_hs - M_h) l_hs, M_h the largest
+// partial maximum and L_h = sum_s w_hs, read from the sparse prefill's
+// partials (m in log2 units, l the partial normaliser); the target is the mean
+// over the group's G heads.  The index distribution is a softmax of
+// idx_scale * bscore over the same live slots, and kl = sum_s target_s
+// (ln target_s - ln index_s), 0 ln 0 = 0.  A slot is live when blk holds a
+// block in [0, jl]; dead slots get target 0 and take no part.
+// Reductions over the R lanes of a row: DPP moves inside each row of 16 lanes
+// (swap neighbours, swap pairs, mirror within 8, mirror within 16; after each
+// step every lane holds the reduction of its group), then one cross-row swap
+// when R == 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+template <int R, typename Op>
+__device__ __forceinline__ float row_reduce(float v, Op op) {
+  v = op(v, dpp_f<0xb1>(v));                           // quad_perm [1,0,3,2]
+  v = op(v, dpp_f<0x4e>(v));                           // quad_perm [2,3,0,1]
+  v = op(v, dpp_f<0x141>(v));                          // row_half_mirror
+  v = op(v, dpp_f<0x140>(v));                          // row_mirror
+  if constexpr (R == 32) v = op(v, shfl_xor_f(v, 16));
+  return v;
+}
+
+template <int G, int R>
+__global__ __launch_bounds__(256) void block_target_kl(const float* __restrict__ part_ml,
+                                                       const int32_t* __restrict__ blk,
+                                                       const float* __restrict__ bscore, float* __restrict__ target,
+                                                       float* __restrict__ kl, int64_t nrows, int n_q, int h_kv,
+                                                       int pos0, int topk, int nblk, float idx_sl2) {
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / R;   // (b * n_q + t) * h_kv + g
+  const int s = threadIdx.x % R;
+  const int64_t rr = row < nrows ? row : nrows - 1;      // idle lanes of the last wave read a real row
+  const int t = (int)((rr / h_kv) % n_q);
+  const int jl = (pos0 + t) / kBlock;
+  const int sc = min(s, topk - 1);
+  const int j = blk[rr * topk + sc];
+  const bool on = s < topk && j >= 0 && j <= jl;
+  const auto fmax = [](float x, float y) { return vmax(x, y); };
+  const auto fadd = [](float x, float y) { return x + y; };
+  // (m, l) of the G heads of this slot: 8 G contiguous bytes
+  float mv[G], lv[G];
+  const float* ml = part_ml + (rr * topk + sc) * G * 2;
+  if constexpr (G == 1) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    const f32x2 v = *reinterpret_cast<const f32x2*>(ml);
+    mv[0] = v[0];
+    lv[0] = v[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; h += 2) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ml + 2 * h);
+      mv[h] = v[0];
+      lv[h] = v[1];
+      mv[h + 1] = v[2];
+      lv[h + 1] = v[3];
+    }
+  }
+  const float a = on ? bscore[rr * nblk + (on ? j : 0)] * idx_sl2 : -INFINITY;   // log2 units
+  float mass = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float m = on ? mv[h] : -INFINITY;
+    const float M = row_reduce<R>(m, fmax);
+    const float w = on ? __builtin_amdgcn_exp2f(m - M) * lv[h] : 0.f;
+    const float L = row_reduce<R>(w, fadd);
+    mass += L > 0.f ? w / L : 0.f;
+  }
+  const float tg = mass * (1.f / G);
+  const float A = row_reduce<R>(a, fmax);
+  const float e = on ? __builtin_amdgcn_exp2f(a - A) : 0.f;
+  const float Z = row_reduce<R>(e, fadd);
+  const float term = (on && tg > 0.f) ? tg * (__log2f(tg) - (a - A - __log2f(Z))) : 0.f;
+  const float k2 = row_reduce<R>(term, fadd);
+  if (row < nrows) {
+    if (s < topk) target[row * topk + s] = on ? tg : 0.f;
+    if (s == 0) kl[row] = k2 * kLn2;
+  }
+}
+
+template <int G>
+hipError_t launch_target_t(const Dims& d, const float* part_ml, const int32_t* blk, const float* bscore,
+                           float idx_scale, float* target, float* kl, hipStream_t stream) {
+  const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
+  const int R = d.topk > 16 ? 32 : 16;
+  const int64_t wgs = (nrows * R + 255) / 256;
+  LaunchTimer timer("block_target_kl", stream);
+  if (R == 16)
+    hipLaunchKernelGGL((block_target_kl<G, 16>), dim3((unsigned)wgs), dim3(256), 0, stream, part_ml, blk, bscore,
+                       target, kl, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale * kLog2e);
+  else
+    hipLaunchKernelGGL((block_target_kl<G, 32>), dim3((unsigned)wgs), dim3(256), 0, stream, part_ml, blk, bscore,
+                       target, kl, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale * kLog2e);
+  return hipGetLastError();
+}
+
 template <int D, int LOG2G>
 hipError_t launch_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const int32_t* blk, float sl2, uint16_t* out, float* lse, void* ws,
@@ -556,6 +659,22 @@ hipError_t launch_sparse_prefill(const Dims& d, const uint16_t* q, const uint16_
   const float sl2 = scale * kLog2e;
   if (d.d == 128) return prefill_by_group<128>(d, q, k, v, blk, sl2, out, lse, ws, stream);
   return prefill_by_group<64>(d, q, k, v, blk, sl2, out, lse, ws, stream);
+}
+
+hipError_t launch_sparse_prefill_target(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        const int32_t* blk, float scale, const float* bscore, float idx_scale,
+                                        uint16_t* out, float* lse, float* target, float* kl, void* ws,
+                                        hipStream_t stream) {
+  hipError_t e = launch_sparse_prefill(d, q, k, v, blk, scale, out, lse, ws, stream);
+  if (e != hipSuccess) return e;
+  const float* part_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + prefill_ws_layout(d).part_ml);
+  switch (d.group()) {
+    case 1: return launch_target_t<1>(d, part_ml, blk, bscore, idx_scale, target, kl, stream);
+    case 2: return launch_target_t<2>(d, part_ml, blk, bscore, idx_scale, target, kl, stream);
+    case 4: return launch_target_t<4>(d, part_ml, blk, bscore, idx_scale, target, kl, stream);
+    case 8: return launch_target_t<8>(d, part_ml, blk, bscore, idx_scale, target, kl, stream);
+    default: return launch_target_t<16>(d, part_ml, blk, bscore, idx_scale, target, kl, stream);
+  }
 }
 
 hipError_t launch_sparse_decode(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -49,6 +49,7 @@ EXPORTED = (
     "msa_sparse_decode_varlen",
     "msa_prefill_chunked_workspace_size",
     "msa_prefill_chunked",
+    "msa_sparse_prefill_target",
 )
 
 
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
     L.msa_block_topk.argtypes = [D, P, P, VP]
     L.msa_sparse_prefill.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
     L.msa_sparse_decode.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
+    L.msa_sparse_prefill_target.argtypes = [D, P, P, P, P, P, F, F, P, P, P, P, P, S, VP]
     L.msa_dense_gqa.argtypes = [D, P, P, P, F, P, P, P, S, VP]
     L.msa_index_topk_varlen.argtypes = [D, P, P, P, P, P, S, VP]
     L.msa_sparse_decode_varlen.argtypes = [D, P, P, P, P, P, F, P, P, P, S, VP]
@@ -196,6 +198,26 @@ def msa_sparse_prefill(s: Shape, q, k, v, blk_idx, out, lse=None, workspace=None
     st = lib().msa_sparse_prefill(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx), ctypes.c_float(scale),
                                   _ptr(out), _ptr(lse), wp, wb, _stream(stream))
     _raise(st, "msa_sparse_prefill")
+
+
+def msa_sparse_prefill_target(s: Shape, q, k, v, blk_idx, bscore, target, kl, out, lse=None, workspace=None,
+                              idx_scale: float = 1.0, scale: float = 0.0, stream=None) -> None:
+    """msa_sparse_prefill plus the index-branch target and its KL (forward only)."""
+    _check(q, "q", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(k, "k", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(v, "v", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, s.n_q, s.h_kv, s.topk))
+    _check(bscore, "bscore", torch.float32, (s.batch, s.n_q, s.h_kv, s.nblk))
+    _check(target, "target", torch.float32, (s.batch, s.n_q, s.h_kv, s.topk))
+    _check(kl, "kl", torch.float32, (s.batch, s.n_q, s.h_kv))
+    _check(out, "out", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(lse, "lse", torch.float32, (s.batch, s.n_q, s.h_q))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_sparse_prefill_target(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx), _ptr(bscore),
+                                         ctypes.c_float(idx_scale), ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                                         _ptr(target), _ptr(kl), wp, wb, _stream(stream))
+    _raise(st, "msa_sparse_prefill_target")
 
 
 def msa_sparse_decode(s: Shape, q, k, v, blk_idx, out, lse=None, workspace=None, scale: float = 0.0,

@@ -140,6 +140,32 @@ msa_status msa_sparse_prefill(const msa_dims* dims, const uint16_t* q, const uin
                               const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
                               size_t workspace_bytes, msa_stream stream);
 
+/* Index-branch training target, forward only (Notion notes
+ * "Minimax-sparse-Attention", "KL Loss Alignment" and "Detached Gradients":
+ * the main branch's attention distribution is what the index branch is
+ * trained to imitate through a KL divergence, and no gradient passes between
+ * the branches).  Runs msa_sparse_prefill (same outputs, same workspace) and
+ * then, for every (b, t, g) row and from the same partial results:
+ *   target[b][t][g][s] = mean over the group's heads h of the share of head h's
+ *            softmax weight that falls in block blk_idx[b][t][g][s]
+ *            (fp32; each row sums to 1 over its live slots; 0 at padding);
+ *   kl[b][t][g] = sum_s target_s * (ln target_s - ln index_s) in nats, where
+ *            index_s = softmax over the live slots of idx_scale * bscore at
+ *            the selected block (0 ln 0 = 0).
+ * A slot is live when it holds a block in [0, jl].  The target is a plain
+ * value: nothing here computes or carries gradients.
+ *   bscore   [batch][n_q][h_kv][nblk] fp32 pooled index scores, as written by
+ *            msa_index_scores (or at offset 0 of msa_index_topk's workspace);
+ *            only entries at live selected blocks are read.
+ *   idx_scale finite temperature of the index softmax (MSA_ERR_SHAPE if not
+ *            finite; the pages name none).
+ *   target   [batch][n_q][h_kv][topk] fp32, kl [batch][n_q][h_kv] fp32, outputs.
+ * Workspace: msa_workspace_size(MSA_OP_SPARSE_PREFILL, dims). */
+msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const int32_t* blk_idx, const float* bscore, float idx_scale, float scale,
+                                     uint16_t* out, float* lse, float* target, float* kl, void* workspace,
+                                     size_t workspace_bytes, msa_stream stream);
+
 /* Main branch, decode: msa_sparse_prefill with n_q == 1; each of the batch
  * sequences has its own cache of n_kv tokens and its query at p = pos0
  * (normally n_kv - 1).  Streams only the selected blocks (lefilia.fr: a fixed

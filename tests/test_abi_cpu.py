@@ -191,3 +191,26 @@ def test_chunked_prefill_argument_checks():
     big = dims(n_q=4096, pos0=0)
     assert lib.msa_prefill_chunked_workspace_size(ctypes.byref(big), 64) == need
     assert call(dims(n_q=0), qi=None, q=None, blk=None, ws=None) == OK
+
+
+def test_target_argument_checks():
+    lib = M.lib()
+    d = dims()
+
+    def call(dd, idx_scale=1.0, ws=FAKE, wsb=1 << 40, **kw):
+        return lib.msa_sparse_prefill_target(
+            ctypes.byref(dd), FAKE, FAKE, FAKE, kw.get("blk", FAKE), kw.get("bscore", FAKE),
+            ctypes.c_float(idx_scale), ctypes.c_float(0.0), FAKE, kw.get("lse", None), kw.get("target", FAKE),
+            kw.get("kl", FAKE), ws, wsb, None)
+
+    assert call(d, bscore=None) == NULL
+    assert call(d, target=None) == NULL
+    assert call(d, kl=None) == NULL
+    assert call(d, kl=ODD) == ALIGN
+    assert call(d, bscore=ODD) == ALIGN
+    assert call(d, idx_scale=float("nan")) == SHAPE
+    assert call(d, idx_scale=float("inf")) == SHAPE
+    assert call(dims(h_q=6, h_kv=2)) == UNSUP
+    need = lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d))
+    assert call(d, wsb=need - 1) == WS
+    assert call(dims(n_q=0), bscore=None, target=None, kl=None, ws=None) == OK

@@ -1,0 +1,126 @@
+"""GPU parity of the index-branch training target (msa_sparse_prefill_target)
+against the fp64 oracle.
+
+Tolerances: the target comes from fp32 partial maxima and normalisers of
+exactly represented bf16 products, so each mass is within 1e-5 of the fp64
+value; the KL adds fp32 log-softmax rounding of index logits up to a few
+hundred (log2 units): |kl - ref| <= 1e-4 + 1e-5 |ref|.  The attention outputs of
+the same call are held to the main branch's tolerances, and must be bit-identical
+to msa_sparse_prefill's.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_score_amd import msa as M
+from block_sparse_long_score_amd.inputs import WORKLOADS, Shape, make_inputs, sample_rows
+from oracle import msa_oracle as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+TARGET_ABS = 1e-5
+KL_ABS, KL_REL = 1e-4, 1e-5
+
+
+def run_target(s: Shape, inp, blk, bscore, idx_scale):
+    out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((s.batch, s.n_q, s.h_q), dtype=torch.float32, device="cuda")
+    target = torch.full((s.batch, s.n_q, s.h_kv, s.topk), float("nan"), dtype=torch.float32, device="cuda")
+    kl = torch.full((s.batch, s.n_q, s.h_kv), float("nan"), dtype=torch.float32, device="cuda")
+    ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
+    M.msa_sparse_prefill_target(s, inp["q"], inp["k"], inp["v"], blk, bscore, target, kl, out, lse, ws,
+                                idx_scale=idx_scale)
+    return out, lse, target, kl
+
+
+def check_target(target, kl, t_ref, kl_ref, what):
+    t_err = np.max(np.abs(target - t_ref))
+    assert t_err <= TARGET_ABS, f"{what}: target max |err| {t_err:.3g}"
+    k_err = np.abs(kl - kl_ref) - (KL_ABS + KL_REL * np.abs(kl_ref))
+    assert np.max(k_err) <= 0, f"{what}: kl max |err| {np.max(np.abs(kl - kl_ref)):.3g}"
+
+
+CASES = {
+    # MQA, G=4, d=64, every row of the 4096-token workload
+    "tiny_prefill_4k": (1, WORKLOADS["tiny_prefill_4k"][1], 1 / 8),
+    # G=8 at the real head shape, unaligned chunk, ragged tail
+    "g8_chunk": (31, Shape(1, 700, 6000, 5300, 64, 8, 128, 128, topk=16), 1 / math.sqrt(128)),
+    # two sequences, G=16, topk=3
+    "batch2_g16_d64": (12, Shape(2, 257, 600, 343, 16, 1, 64, 64, topk=3), 0.05),
+    # topk=32 (32 lanes per row), G=2, rows with fewer causal blocks than k
+    "g2_topk32": (14, Shape(1, 130, 2100, 1970, 16, 8, 64, 128, topk=32), 0.1),
+    # MHA, topk=1: the target is 1 on the local block and the KL 0
+    "mha_topk1": (15, Shape(1, 200, 3000, 2800, 8, 8, 128, 128, topk=1), 1 / math.sqrt(128)),
+    # idx_scale 0: KL = ln(live slots) - entropy(target)
+    "zero_idx_scale": (16, Shape(1, 300, 3000, 2700, 16, 4, 128, 128, topk=8), 0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_target_parity_every_row(name):
+    cid, s, idx_scale = CASES[name]
+    print(f"case {name}: {s} idx_scale={idx_scale}", flush=True)
+    inp = make_inputs(s, cid, device="cuda")
+    blk, bscore = U.run_index(s, inp["q_idx"], inp["k_idx"])
+    out, lse, target, kl = run_target(s, inp, blk, bscore, idx_scale)
+    o2, l2 = U.run_sparse_prefill_path(s, inp["q"], inp["k"], inp["v"], blk)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    bs_ref, blk_ref = O.msa_index_topk(U.to64(inp["q_idx"]), U.to64(inp["k_idx"]), s.pos0, s.block, s.topk)
+    assert np.array_equal(blk.cpu().numpy(), blk_ref.astype(np.int32))
+    t_ref = O.msa_block_target(U.to64(inp["q"]), U.to64(inp["k"]), blk_ref, s.pos0, s.block)
+    kl_ref = O.msa_index_kl(t_ref, bs_ref, blk_ref, idx_scale)
+    check_target(target.cpu().numpy(), kl.cpu().numpy(), t_ref, kl_ref, name)
+
+
+def test_target_caller_selection_with_padding():
+    """Hand-made selections: fewer blocks than k and -1 padding in any slot."""
+    s = Shape(1, 64, 2048, 1984, 8, 2, 128, 128, topk=6)
+    inp = make_inputs(s, 23, device="cuda")
+    rng = np.random.default_rng(7)
+    blk = np.full((1, s.n_q, s.h_kv, s.topk), -1, dtype=np.int32)
+    for t in range(s.n_q):
+        jl = (s.pos0 + t) // s.block
+        for g in range(s.h_kv):
+            n = int(rng.integers(1, s.topk))
+            chosen = sorted(rng.choice(jl, size=n - 1, replace=False).tolist() + [jl])
+            slots = sorted(rng.permutation(s.topk)[:n])
+            for sl, j in zip(slots, chosen):
+                blk[0, t, g, sl] = j
+    bscore = torch.from_numpy(rng.normal(size=(1, s.n_q, s.h_kv, s.nblk)).astype(np.float32) * 4).cuda()
+    _, _, target, kl = run_target(s, inp, torch.from_numpy(blk).cuda(), bscore, 0.5)
+    torch.cuda.synchronize()
+    t_ref = O.msa_block_target(U.to64(inp["q"]), U.to64(inp["k"]), blk, s.pos0, s.block)
+    kl_ref = O.msa_index_kl(t_ref, U.to64(bscore), blk, 0.5)
+    check_target(target.cpu().numpy(), kl.cpu().numpy(), t_ref, kl_ref, "caller selection")
+    assert np.all(target.cpu().numpy()[blk < 0] == 0.0)
+
+
+def test_target_full_size_prefill_128k_sampled_rows():
+    """The 131,072-token workload in the benchmark's launch configuration;
+    24 sampled rows (first, last and block-boundary rows included)."""
+    cid, s = WORKLOADS["prefill_128k"]
+    idx_scale = 1 / math.sqrt(s.d_idx)
+    inp = make_inputs(s, cid, device="cuda")
+    blk, bscore = U.run_index(s, inp["q_idx"], inp["k_idx"])
+    _, _, target, kl = run_target(s, inp, blk, bscore, idx_scale)
+    torch.cuda.synchronize()
+    print("  gpu done", flush=True)
+    boundary = [t for t in range(s.n_q) if (s.pos0 + t) % s.block in (0, s.block - 1)]
+    rows = [(0, t) for t in sample_rows(s.n_q, 24, 1000 * cid + 77, boundary[:: len(boundary) // 6][:6])]
+    kseq = U.to64(inp["k_idx"][0])
+    sels = U.check_index_rows(s, lambda b, t: U.to64(inp["q_idx"][b, t]), lambda b: kseq, blk, bscore, rows)
+    tg, kg = target.cpu().numpy(), kl.cpu().numpy()
+    for g in range(s.h_kv):
+        keys = U.to64(inp["k"][0, :, g])
+        for b, t in rows:
+            sel = sels[(b, t, g)]
+            qh = U.to64(inp["q"][b, t, g * s.group:(g + 1) * s.group])
+            t_ref = O.block_mass_row(qh, keys, sel, s.pos0 + t, s.block, O.default_scale(s.d))
+            pooled = bscore[b, t, g].cpu().numpy().astype(np.float64)
+            kl_ref = O.index_kl_row(t_ref, pooled, sel, idx_scale)
+            check_target(tg[b, t, g], kg[b, t, g], t_ref, kl_ref, f"128k b={b} t={t} g={g}")

@@ -54,6 +54,11 @@ the branches).  Readings:
   r17 "detached": the target is returned as a plain value; nothing here
       differentiates anything.
 
+Main-branch backward: the gradients of the selected-block softmax attention
+with respect to q, k and v for a fixed selection (the selection itself is
+discrete and carries none), written out from the derivative of softmax
+attention.
+
 Array conventions (all numpy, float64 inside):
   q_idx [batch][n_q][Hkv][d_idx]     k_idx [batch][n_kv][d_idx]
   q     [batch][n_q][Hq][d]          k, v  [batch][n_kv][Hkv][d]
@@ -368,3 +373,63 @@ def msa_index_kl(target: np.ndarray, bscore: np.ndarray, blk_idx: np.ndarray,
             for g in range(h_kv):
                 kl[bi, i, g] = index_kl_row(target[bi, i, g], bscore[bi, i, g], blk_idx[bi, i, g], idx_scale)
     return kl
+
+
+# ----------------------------------------------------------------------------
+# Main-branch backward (gradients of the selected-block softmax attention)
+# ----------------------------------------------------------------------------
+
+def softmax_attention_grad(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray,
+                           dout: np.ndarray, scale: float):
+    """Gradients of softmax attention of several heads over the given K/V rows.
+
+    The derivative of out = softmax(scale * q k^T) v, written out: with P the
+    softmax weights, dv = P^T dout, dP = dout v^T, dS = P * (dP - rowsum(dP * P)),
+    dq = scale dS k, dk = scale dS^T q.  q_heads, dout [G][d]; keys, values [n][d].
+    Returns (dq [G][d], dk [n][d], dv [n][d]) in float64.
+    """
+    q = np.asarray(q_heads, dtype=np.float64)
+    kk = np.asarray(keys, dtype=np.float64)
+    vv = np.asarray(values, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    z = scale * (q @ kk.T)
+    w = np.exp(z - np.max(z, axis=1, keepdims=True))
+    w /= np.sum(w, axis=1, keepdims=True)
+    dv = w.T @ do
+    dp = do @ vv.T
+    ds = w * (dp - np.sum(dp * w, axis=1, keepdims=True))
+    dq = scale * (ds @ kk)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def msa_sparse_attention_grad(q: np.ndarray, k: np.ndarray, v: np.ndarray, blk_idx: np.ndarray,
+                              dout: np.ndarray, pos0: int, block: int, scale: float | None = None):
+    """Gradients of the main branch for a fixed selection (the selection is
+    discrete and carries no gradient; the Notion notes' "Detached Gradients").
+
+    q, dout [b][n_q][Hq][d]; k, v [b][n_kv][Hkv][d]; blk_idx [b][n_q][Hkv][topk].
+    Every head of group g attends to the group's selected blocks (yhxrc.cn,
+    "第二步：稀疏分支"); keys and values collect the gradients of every query that
+    saw them.  Returns (dq, dk, dv) in float64, shaped like q, k, v.
+    """
+    b, n_q, h_q, d = q.shape
+    n_kv, h_kv = k.shape[1], k.shape[2]
+    group = h_q // h_kv
+    if scale is None:
+        scale = default_scale(d)
+    dq = np.zeros((b, n_q, h_q, d), dtype=np.float64)
+    dk = np.zeros((b, n_kv, h_kv, d), dtype=np.float64)
+    dv = np.zeros((b, n_kv, h_kv, d), dtype=np.float64)
+    for bi in range(b):
+        for i in range(n_q):
+            p = pos0 + i
+            for g in range(h_kv):
+                pos = visible_positions(blk_idx[bi, i, g], p, block, n_kv)
+                hs = slice(g * group, (g + 1) * group)
+                gq, gk, gv = softmax_attention_grad(q[bi, i, hs], k[bi, pos, g], v[bi, pos, g],
+                                                    dout[bi, i, hs], scale)
+                dq[bi, i, hs] = gq
+                dk[bi, pos, g] += gk
+                dv[bi, pos, g] += gv
+    return dq, dk, dv

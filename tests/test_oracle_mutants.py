@@ -188,3 +188,50 @@ def test_reversed_kl_is_caught(monkeypatch):
 def test_index_softmax_over_all_blocks_is_caught(monkeypatch):
     monkeypatch.setattr(O, "index_kl_row", mut_kl_softmax_over_all_blocks)
     assert fails(TT.test_kl_zero_when_index_matches_target_and_shift_invariant)
+
+
+# ---- main-branch backward ---------------------------------------------------
+
+from tests import test_oracle_backward as TB   # noqa: E402
+
+
+def _grad_parts(q_heads, keys, values, dout, scale):
+    q, kk, vv, do = (np.asarray(a, dtype=np.float64) for a in (q_heads, keys, values, dout))
+    z = scale * (q @ kk.T)
+    w = np.exp(z - z.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    return q, kk, vv, do, w, do @ vv.T
+
+
+def mut_grad_no_rowsum(q_heads, keys, values, dout, scale):
+    q, kk, vv, do, w, dp = _grad_parts(q_heads, keys, values, dout, scale)
+    ds = w * dp                                             # the rowsum term dropped
+    return scale * ds @ kk, scale * ds.T @ q, w.T @ do
+
+
+def mut_grad_dk_unscaled(q_heads, keys, values, dout, scale):
+    q, kk, vv, do, w, dp = _grad_parts(q_heads, keys, values, dout, scale)
+    ds = w * (dp - np.sum(dp * w, axis=1, keepdims=True))
+    return scale * ds @ kk, ds.T @ q, w.T @ do
+
+
+def mut_grad_rowsum_of_dp(q_heads, keys, values, dout, scale):
+    q, kk, vv, do, w, dp = _grad_parts(q_heads, keys, values, dout, scale)
+    ds = w * (dp - np.mean(dp, axis=1, keepdims=True))       # unweighted row mean
+    return scale * ds @ kk, scale * ds.T @ q, w.T @ do
+
+
+def test_backward_without_rowsum_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "softmax_attention_grad", mut_grad_no_rowsum)
+    assert fails(TB.test_value_and_key_gradient_sums)
+    assert fails(TB.test_grads_match_torch_autograd, 8, 2, 1)
+
+
+def test_backward_unscaled_key_gradient_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "softmax_attention_grad", mut_grad_dk_unscaled)
+    assert fails(TB.test_grads_match_central_differences)
+
+
+def test_backward_unweighted_rowsum_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "softmax_attention_grad", mut_grad_rowsum_of_dp)
+    assert fails(TB.test_grads_match_torch_autograd, 4, 1, 2)

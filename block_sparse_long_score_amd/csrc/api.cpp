@@ -190,6 +190,28 @@ msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, co
                                                       static_cast<hipStream_t>(stream)));
 }
 
+msa_status msa_sparse_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t* k,
+                                       const uint16_t* v, const int32_t* blk_idx, const uint16_t* out,
+                                       const float* lse, const uint16_t* dout, float scale, uint16_t* dq,
+                                       uint16_t* dk, uint16_t* dv, void* workspace, size_t workspace_bytes,
+                                       msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_PREFILL));
+  if (st != MSA_OK) return st;
+  if (dims->batch == 0 || dims->n_kv == 0) return MSA_OK;
+  if (!k || !v || !dk || !dv) return MSA_ERR_NULL;
+  if (dims->n_q > 0 && (!q || !blk_idx || !out || !lse || !dout || !dq)) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(blk_idx) || misaligned(out) ||
+      misaligned(lse) || misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv))
+    return MSA_ERR_ALIGN;
+  const Dims d = to_dims(*dims);
+  const size_t need = msa::prefill_ws_layout(d).total;
+  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_sparse_prefill_backward(d, q, k, v, blk_idx, out, lse, dout,
+                                                        resolve_scale(scale, d.d), dq, dk, dv, workspace,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
 msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
                              size_t workspace_bytes, msa_stream stream) {

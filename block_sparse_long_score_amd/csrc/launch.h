@@ -45,6 +45,8 @@ struct PrefillWs {
   int64_t lists, chunks, entries_max;
 };
 PrefillWs prefill_ws_layout(const Dims& d);
+// Builds the per-(b, g, block) lists of (t, slot) entries in the workspace.
+hipError_t launch_csr(const Dims& d, const int32_t* blk, void* ws, hipStream_t stream);
 
 // Decode / dense-decode partials.
 struct DecodeWs {
@@ -65,6 +67,12 @@ hipError_t launch_sparse_prefill_target(const Dims& d, const uint16_t* q, const 
                                         const int32_t* blk, float scale, const float* bscore, float idx_scale,
                                         uint16_t* out, float* lse, float* target, float* kl, void* ws,
                                         hipStream_t stream);
+// Gradients of msa_sparse_prefill: dq, dk, dv from dout, the forward's output
+// and lse; same workspace layout (partial dq in part_o, row dots in part_ml).
+hipError_t launch_sparse_prefill_backward(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                          const int32_t* blk, const uint16_t* out, const float* lse,
+                                          const uint16_t* dout, float scale, uint16_t* dq, uint16_t* dk,
+                                          uint16_t* dv, void* ws, hipStream_t stream);
 hipError_t launch_sparse_decode(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* ws,
                                 hipStream_t stream);

@@ -40,14 +40,16 @@ int64_t prefill_entries_max(const Dims& d) { return (int64_t)d.batch * d.n_q * d
 
 constexpr int kCsrThreads = 256;
 constexpr int kCsrMaxBlocks = 8192;                    // nblk <= 8192 (n_kv <= 1M)
-constexpr int kCsrTargetWgs = 1024;
+constexpr int kCsrTargetChunks = 4096;
+constexpr int kCsrMinTokens = 64;
 
-// Token chunks per (b, g): enough workgroups to fill the chip.
+// Token chunks per (b, g): enough to fill the chip with the one-wave fill
+// kernel, each of at least kCsrMinTokens tokens.
 int csr_chunks(const Dims& d) {
   const int64_t bg = (int64_t)d.batch * d.h_kv;
   if (bg <= 0 || d.n_q <= 0) return 1;
-  int64_t c = (kCsrTargetWgs + bg - 1) / bg;
-  c = std::max<int64_t>(1, std::min<int64_t>(c, d.n_q));
+  int64_t c = (kCsrTargetChunks + bg - 1) / bg;
+  c = std::max<int64_t>(1, std::min<int64_t>(c, (d.n_q + kCsrMinTokens - 1) / kCsrMinTokens));
   const int64_t tc = (d.n_q + c - 1) / c;
   return (int)((d.n_q + tc - 1) / tc);
 }
@@ -88,10 +90,15 @@ __global__ void csr_chunk_scan(int* __restrict__ ccnt, int* __restrict__ cnt, in
   const int bg = list / nblk, j = list % nblk;
   int* col = ccnt + (int64_t)bg * chunks * nblk + j;
   int run = 0;
-  for (int c = 0; c < chunks; ++c) {
-    const int v = col[(int64_t)c * nblk];
-    col[(int64_t)c * nblk] = run;
-    run += v;
+  for (int c0 = 0; c0 < chunks; c0 += 8) {             // eight loads in flight
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = c0 + i < chunks ? col[(int64_t)(c0 + i) * nblk] : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (c0 + i < chunks) col[(int64_t)(c0 + i) * nblk] = run;
+      run += v[i];
+    }
   }
   cnt[list] = run;
 }
@@ -122,26 +129,69 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan(const int* __restrict__
   if (tid == kScanThreads - 1) off[lists] = s_e[tid];
 }
 
-// Entries of chunk c go to off[list] + (prefix of earlier chunks) + a rank
-// taken from an LDS cursor, so lists are ordered by chunk (ranks inside a
-// chunk follow the LDS atomics and do not affect any result).
-__global__ __launch_bounds__(kCsrThreads) void csr_fill_chunks(const int32_t* __restrict__ blk,
-                                                               const int* __restrict__ off,
-                                                               const int* __restrict__ ccnt,
-                                                               int* __restrict__ entries, int n_q, int h_kv, int topk,
-                                                               int nblk, int pos0, int tc, int chunks) {
-  __shared__ int cur[kCsrMaxBlocks];
+// Entries of chunk c go to off[list] + (prefix of earlier chunks) + their rank
+// among the chunk's entries of that list in (token, slot) order.  One wave per
+// chunk: its lanes take the chunk's items in rounds of 64 (64 / T tokens, T =
+// topk rounded up to a power of two, lane = token * T + slot); an entry's
+// position is the list cursor plus the number of the round's entries before it
+// with the same block, and the round's last such entry advances the cursor.
+// A single wave's LDS operations complete in issue order, so no barrier is
+// needed; the selections of four rounds are loaded together.  Every list is therefore ordered by token and slot whatever the
+// scheduling, so a kernel that accumulates over a list in list order gives the
+// same bits on every run.
+constexpr int kFillThreads = 64;
+constexpr int kFillBatch = 4;
+__global__ __launch_bounds__(kFillThreads) void csr_fill_chunks(const int32_t* __restrict__ blk,
+                                                                const int* __restrict__ off,
+                                                                const int* __restrict__ ccnt,
+                                                                int* __restrict__ entries, int n_q, int h_kv,
+                                                                int topk, int nblk, int pos0, int tc, int chunks) {
+  extern __shared__ int cur[];                         // [nblk]
+  __shared__ __attribute__((aligned(16))) int sel[kFillThreads];
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
   const int t0 = c * tc, t1 = min(n_q, t0 + tc);
   const int* pre = ccnt + (((int64_t)b * h_kv + g) * chunks + c) * nblk;
   const int* loff = off + ((int64_t)b * h_kv + g) * nblk;
-  for (int j = threadIdx.x; j < nblk; j += kCsrThreads) cur[j] = loff[j] + pre[j];
-  __syncthreads();
-  const int n = (t1 - t0) * topk;
-  for (int k = threadIdx.x; k < n; k += kCsrThreads) {
-    const int t = t0 + k / topk, slot = k % topk;
-    const int j = entry_block(blk, ((int64_t)b * n_q + t) * h_kv + g, slot, topk, t, pos0);
-    if (j >= 0) entries[atomicAdd(&cur[j], 1)] = (t << 5) | slot;   // slot < 32, t < 2^26
+  for (int j = lane; j < nblk; j += kFillThreads) cur[j] = loff[j] + pre[j];
+  int T = 1;
+  while (T < topk) T <<= 1;
+  const int tpr = kFillThreads / T, tl = lane / T, slot = lane % T;
+  auto load_j = [&](int tb) {
+    const int t = tb + tl;
+    return (t < t1 && slot < topk) ? entry_block(blk, ((int64_t)b * n_q + t) * h_kv + g, slot, topk, t, pos0) : -1;
+  };
+  // Rounds go in batches of kFillBatch whose selections are loaded together:
+  // one wait per batch (the wait also covers the batch's entry stores).
+  for (int tb0 = t0; tb0 < t1; tb0 += kFillBatch * tpr) {
+    int jb[kFillBatch];
+#pragma unroll
+    for (int r = 0; r < kFillBatch; ++r) jb[r] = load_j(tb0 + r * tpr);
+#pragma unroll
+    for (int r = 0; r < kFillBatch; ++r) {
+      const int tb = tb0 + r * tpr, j = jb[r];
+      sel[lane] = j;
+      int rank = 0;
+      bool last = true;
+#pragma unroll
+      for (int q = 0; q < kFillThreads / 4; ++q) {
+        const int4 r4 = reinterpret_cast<const int4*>(sel)[q];
+        const int v[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool same = v[e] == j;
+          rank += (same && 4 * q + e < lane) ? 1 : 0;
+          last = last && !(same && 4 * q + e > lane);
+        }
+      }
+      if (j >= 0) {
+        const int pos = cur[j] + rank;
+        entries[pos] = ((tb + tl) << 5) | slot;        // slot < 32, t < 2^26
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (j >= 0 && last) cur[j] += rank + 1;          // after every lane has read its cursor
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
@@ -540,36 +590,14 @@ hipError_t launch_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k,
                             hipStream_t stream) {
   const PrefillWs L = prefill_ws_layout(d);
   char* base = static_cast<char*>(ws);
-  int* cnt = reinterpret_cast<int*>(base + L.cnt);
-  int* off = reinterpret_cast<int*>(base + L.off);
-  int* ccnt = reinterpret_cast<int*>(base + L.ccnt);
-  int* entries = reinterpret_cast<int*>(base + L.entries);
+  const int* off = reinterpret_cast<const int*>(base + L.off);
+  const int* entries = reinterpret_cast<const int*>(base + L.entries);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
   const int nblk = d.nblk();
   const int lists = (int)L.lists;
-  const int chunks = (int)L.chunks;
-  const int tc = (d.n_q + chunks - 1) / chunks;
-  const dim3 cgrid((unsigned)chunks, (unsigned)d.h_kv, (unsigned)d.batch);
-  {
-    LaunchTimer timer("csr_count_chunks", stream);
-    hipLaunchKernelGGL(csr_count_chunks, cgrid, dim3(kCsrThreads), 0, stream, blk, ccnt, d.n_q, d.h_kv, d.topk, nblk,
-                       d.pos0, tc, chunks);
-  }
-  {
-    LaunchTimer timer("csr_chunk_scan", stream);
-    hipLaunchKernelGGL(csr_chunk_scan, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream, ccnt, cnt, lists,
-                       chunks, nblk);
-  }
-  {
-    LaunchTimer timer("csr_scan", stream);
-    hipLaunchKernelGGL(csr_scan, dim3(1), dim3(kScanThreads), 0, stream, cnt, off, lists);
-  }
-  {
-    LaunchTimer timer("csr_fill_chunks", stream);
-    hipLaunchKernelGGL(csr_fill_chunks, cgrid, dim3(kCsrThreads), 0, stream, blk, off, ccnt, entries, d.n_q, d.h_kv,
-                       d.topk, nblk, d.pos0, tc, chunks);
-  }
+  hipError_t e = launch_csr(d, blk, ws, stream);
+  if (e != hipSuccess) return e;
   {
     LaunchTimer timer("sparse_kv_outer", stream);
     hipLaunchKernelGGL((sparse_kv_outer<D, LOG2G>), dim3((unsigned)device_cu_count()), dim3(kKvThreads), 0, stream,
@@ -621,6 +649,40 @@ hipError_t decode_by_group(const Dims& d, const uint16_t* q, const uint16_t* k, 
 }
 
 }  // namespace
+
+hipError_t launch_csr(const Dims& d, const int32_t* blk, void* ws, hipStream_t stream) {
+  const PrefillWs L = prefill_ws_layout(d);
+  char* base = static_cast<char*>(ws);
+  int* cnt = reinterpret_cast<int*>(base + L.cnt);
+  int* off = reinterpret_cast<int*>(base + L.off);
+  int* ccnt = reinterpret_cast<int*>(base + L.ccnt);
+  int* entries = reinterpret_cast<int*>(base + L.entries);
+  const int nblk = d.nblk();
+  const int lists = (int)L.lists;
+  const int chunks = (int)L.chunks;
+  const int tc = (d.n_q + chunks - 1) / chunks;
+  const dim3 cgrid((unsigned)chunks, (unsigned)d.h_kv, (unsigned)d.batch);
+  {
+    LaunchTimer timer("csr_count_chunks", stream);
+    hipLaunchKernelGGL(csr_count_chunks, cgrid, dim3(kCsrThreads), 0, stream, blk, ccnt, d.n_q, d.h_kv, d.topk, nblk,
+                       d.pos0, tc, chunks);
+  }
+  {
+    LaunchTimer timer("csr_chunk_scan", stream);
+    hipLaunchKernelGGL(csr_chunk_scan, dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream, ccnt, cnt, lists,
+                       chunks, nblk);
+  }
+  {
+    LaunchTimer timer("csr_scan", stream);
+    hipLaunchKernelGGL(csr_scan, dim3(1), dim3(kScanThreads), 0, stream, cnt, off, lists);
+  }
+  {
+    LaunchTimer timer("csr_fill_chunks", stream);
+    hipLaunchKernelGGL(csr_fill_chunks, cgrid, dim3(kFillThreads), (unsigned)(nblk * sizeof(int)), stream, blk, off,
+                       ccnt, entries, d.n_q, d.h_kv, d.topk, nblk, d.pos0, tc, chunks);
+  }
+  return hipGetLastError();
+}
 
 PrefillWs prefill_ws_layout(const Dims& d) {
   PrefillWs L{};

@@ -1,0 +1,371 @@
+// Main branch, backward: gradients of the selected-block softmax attention with
+// respect to q, k and v for a fixed selection (the selection is discrete and
+// carries no gradient; Notion notes "Minimax-sparse-Attention", "Detached
+// Gradients").  With P the softmax weights of a (query, head) over its visible
+// keys, D = rowsum(dout * out):
+//   dv[s] = sum P dout,   dP = dout . v[s],   dS = P (dP - D),
+//   dq    = scale sum_s dS k[s],   dk[s] = scale sum dS q.
+//
+// KV-outer, like the forward (lumi-systems summary: KV-outer sparse attention):
+// one workgroup per (b, g, block) list of the CSR inversion.  Its eight waves
+// each own 16 keys of the block: they keep those keys' K and V rows as MFMA
+// operands in registers, and their dk / dv rows as fp32 accumulators for the
+// whole list, so every key gradient is summed inside one workgroup in a fixed
+// order (no atomics).  For each group of 32 (entry x group head) columns the
+// columns' q and dout rows are staged in LDS row-major and transposed; each
+// wave computes S^T and dP^T for its keys, P and dS, and adds P * dout and
+// dS * q into its rows.  dS goes through LDS so that each wave can then form
+// one 16-wide d slice of dq over all 128 keys of the block; dq leaves as one
+// bf16 partial per (t, g, slot, head), summed per (t, head) by a second kernel.
+#include "launch.h"
+#include "msa_device.h"
+
+namespace msa {
+namespace {
+
+constexpr int kBwdThreads = 512;
+constexpr int kBwdCols = 32;                           // (entry x head) columns per group
+
+// [row][d] tiles (K/V rows of the block, q/dout rows of the columns): 16-byte
+// chunk c of row r sits at c ^ row_swz(r), so 16 rows read at the same chunk
+// hit 16 different bank groups.
+template <int D>
+__device__ __forceinline__ int row_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int rt_off(int r, int chunk) { return r * D + 8 * (chunk ^ row_swz<D>(r)); }
+// [d][column] tiles (q and dout transposed): units of 4 columns, unit u of row
+// d at u ^ ((d >> 2) & 7).
+__device__ __forceinline__ int tt_off(int d, int col) {
+  return d * kBwdCols + 4 * (((col >> 2) ^ (d >> 2)) & 7) + (col & 3);
+}
+// dS tile [column][key]: 8-key chunk c of row col at c ^ (col & 15).
+__device__ __forceinline__ int ds_off(int col, int key) {
+  return col * kBlock + 8 * (((key >> 3) ^ col) & 15) + (key & 7);
+}
+
+template <int D>
+struct BwdLds {
+  union {
+    struct {
+      uint16_t k[kBlock * D];
+      uint16_t v[kBlock * D];
+    } kv;                                              // the block, while its operands are loaded
+    struct {
+      uint16_t qr[kBwdCols * D], dor[kBwdCols * D];    // [column][d]
+      uint16_t qt[D * kBwdCols], dot[D * kBwdCols];    // [d][column]
+      uint16_t ds[kBwdCols * kBlock];                  // [column][key]
+      float lse2[kBwdCols], dcol[kBwdCols];
+      int plim[kBwdCols];                              // last visible key position, -1 for an empty column
+    } g;
+  };
+};
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16x2(x, 0.f) & 0xffffu; }
+
+// D = rowsum(dout * out) per (b, t, head) row, from the forward's bf16 output.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_row_dot(const uint16_t* __restrict__ out,
+                                                   const uint16_t* __restrict__ dout, float* __restrict__ dcol,
+                                                   int64_t nrows) {
+  constexpr int TPR = D / 8;
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int64_t rr = row < nrows ? row : nrows - 1;
+  const int dl = threadIdx.x % TPR;
+  const u32x4 a = ld16(out + rr * D + dl * 8), c = ld16(dout + rr * D + dl * 8);
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sum = fmaf(bf16_to_f32(a[e] & 0xffffu), bf16_to_f32(c[e] & 0xffffu), sum);
+    sum = fmaf(bf16_to_f32(a[e] >> 16), bf16_to_f32(c[e] >> 16), sum);
+  }
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) sum += shfl_xor_f(sum, m);
+  if (row < nrows && dl == 0) dcol[row] = sum;
+}
+
+template <int D, int LOG2G>
+__global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dcol,
+    const int* __restrict__ off, const int* __restrict__ entries, uint16_t* __restrict__ part_dq,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int batch, int n_q, int n_kv, int pos0, int h_q, int h_kv,
+    int nblk, int topk, float sl2, float scale) {
+  constexpr int G = 1 << LOG2G;
+  constexpr int DC = D / 8;                            // 16-byte chunks per row
+  constexpr int DT = D / 16;                           // 16-wide d tiles
+  constexpr int CTW = D / 64;                          // column tiles of dq per wave
+  __shared__ BwdLds<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int m16 = lane & 15, q4 = lane >> 4;
+  // Grid order: block index outermost, so the earliest blocks (candidates for
+  // the most queries) start first.
+  const int bgs = batch * h_kv;
+  const int j = blockIdx.x / bgs, bg = blockIdx.x % bgs;
+  const int g = bg % h_kv, b = bg / h_kv;
+  const int list = bg * nblk + j;
+  const int e0 = off[list], e1 = off[list + 1];
+  const int ncols = (e1 - e0) << LOG2G;
+  const int s0 = j * kBlock;
+  const int64_t rs = (int64_t)h_kv * D;
+  const uint16_t* kb = k + ((int64_t)b * n_kv * h_kv + g) * D;
+  const uint16_t* vb = v + ((int64_t)b * n_kv * h_kv + g) * D;
+
+  for (int it = tid; it < kBlock * DC; it += kBwdThreads) {
+    const int key = it / DC, ch = it % DC, s = s0 + key;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    st16(&sm.kv.k[rt_off<D>(key, ch)], s < n_kv ? ld16(kb + s * rs + ch * 8) : z);
+    st16(&sm.kv.v[rt_off<D>(key, ch)], s < n_kv ? ld16(vb + s * rs + ch * 8) : z);
+  }
+  __syncthreads();
+  // B operands of S^T and dP^T: column (MFMA n) = this lane's key, contraction
+  // slots 8*q4 + i = d 32*c + 8*q4 + i.
+  const int mykey = 16 * w + m16;
+  u32x4 kop[D / 32], vop[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    kop[c] = ld16(&sm.kv.k[rt_off<D>(mykey, 4 * c + q4)]);
+    vop[c] = ld16(&sm.kv.v[rt_off<D>(mykey, 4 * c + q4)]);
+  }
+  // A operand of dq: row (MFMA m) = d 16*dtw + m16, contraction slots = keys
+  // 32*kc + 8*q4 + i.
+  const int dtw = w % DT, ct0 = (w / DT) * CTW;
+  u32x4 ktop[4];
+  {
+    const int d = 16 * dtw + m16;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 32 * kc + 8 * q4 + 2 * i;
+        const uint32_t lo = sm.kv.k[rt_off<D>(key, d >> 3) + (d & 7)];
+        const uint32_t hi = sm.kv.k[rt_off<D>(key + 1, d >> 3) + (d & 7)];
+        ktop[kc][i] = lo | (hi << 16);
+      }
+  }
+  __syncthreads();                                     // the LDS now holds column groups
+
+  f32x4 dka[DT], dva[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dka[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int skey = s0 + mykey;
+  for (int c0 = 0; c0 < ncols; c0 += kBwdCols) {
+    if (tid < kBwdCols) {
+      const int gc = c0 + tid;
+      int pl = -1;
+      float l2 = 0.f, dc = 0.f;
+      if (gc < ncols) {
+        const int en = entries[e0 + (gc >> LOG2G)];
+        const int t = en >> 5;
+        const int64_t row = ((int64_t)b * n_q + t) * h_q + g * G + (gc & (G - 1));
+        pl = pos0 + t;
+        l2 = lse[row] * kLog2e;
+        dc = dcol[row];
+      }
+      sm.g.plim[tid] = pl;
+      sm.g.lse2[tid] = l2;
+      sm.g.dcol[tid] = dc;
+    }
+    for (int it = tid; it < 2 * kBwdCols * DC; it += kBwdThreads) {
+      const int which = it / (kBwdCols * DC), rem = it % (kBwdCols * DC), col = rem / DC, ch = rem % DC;
+      const int gc = c0 + col;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (gc < ncols) {
+        const int en = entries[e0 + (gc >> LOG2G)];
+        const int64_t row = ((int64_t)b * n_q + (en >> 5)) * h_q + g * G + (gc & (G - 1));
+        val = ld16((which ? dout : q) + row * D + ch * 8);
+      }
+      st16(&(which ? sm.g.dor : sm.g.qr)[rt_off<D>(col, ch)], val);
+      uint16_t* tt = which ? sm.g.dot : sm.g.qt;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tt[tt_off(8 * ch + e, col)] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();
+
+    // S^T and dP^T for this wave's 16 keys and the 32 columns: lane holds
+    // column 16*ct + 4*q4 + r, key mykey.
+    f32x4 st[2], dpt[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      st[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dpt[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        st[ct] = mfma_16x16x32(ld16(&sm.g.qr[rt_off<D>(16 * ct + m16, 4 * c + q4)]), kop[c], st[ct]);
+        dpt[ct] = mfma_16x16x32(ld16(&sm.g.dor[rt_off<D>(16 * ct + m16, 4 * c + q4)]), vop[c], dpt[ct]);
+      }
+    }
+    float p[2][4], ds[2][4];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = 16 * ct + 4 * q4 + r;
+        const float pv = skey <= sm.g.plim[col]
+                             ? __builtin_amdgcn_exp2f(fmaf(st[ct][r], sl2, -sm.g.lse2[col]))
+                             : 0.f;
+        p[ct][r] = pv;
+        ds[ct][r] = pv * (dpt[ct][r] - sm.g.dcol[col]);
+      }
+    // A operands (row = this lane's key) with contraction slot 8*q4 + i <->
+    // column 4*q4 + i (i < 4) or 16 + 4*q4 + i - 4 (i >= 4).
+    const u32x4 pa = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
+                      pack_bf16x2(p[1][2], p[1][3])};
+    const u32x4 dsa = {pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
+                       pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 16 * dt + m16;
+      const u32x2 dlo = *reinterpret_cast<const u32x2*>(&sm.g.dot[tt_off(d, 4 * q4)]);
+      const u32x2 dhi = *reinterpret_cast<const u32x2*>(&sm.g.dot[tt_off(d, 16 + 4 * q4)]);
+      dva[dt] = mfma_16x16x32(pa, u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, dva[dt]);
+      const u32x2 qlo = *reinterpret_cast<const u32x2*>(&sm.g.qt[tt_off(d, 4 * q4)]);
+      const u32x2 qhi = *reinterpret_cast<const u32x2*>(&sm.g.qt[tt_off(d, 16 + 4 * q4)]);
+      dka[dt] = mfma_16x16x32(dsa, u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dka[dt]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sm.g.ds[ds_off(16 * ct + 4 * q4 + r, mykey)] =
+            (uint16_t)((r & 1) ? (dsa[2 * ct + (r >> 1)] >> 16) : (dsa[2 * ct + (r >> 1)] & 0xffffu));
+    __syncthreads();
+
+    // dq slice: rows d 16*dtw + 4*q4 + r of column 16*ct + m16.
+#pragma unroll
+    for (int i = 0; i < CTW; ++i) {
+      const int ct = ct0 + i;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        acc = mfma_16x16x32(ktop[kc], ld16(&sm.g.ds[ds_off(16 * ct + m16, 32 * kc + 8 * q4)]), acc);
+      const int gc = c0 + 16 * ct + m16;
+      if (gc < ncols) {
+        const int en = entries[e0 + (gc >> LOG2G)];
+        const int64_t prow = ((((int64_t)b * n_q + (en >> 5)) * h_kv + g) * topk + (en & 31)) * G + (gc & (G - 1));
+        u32x2 o;
+        o[0] = pack_bf16x2(acc[0] * scale, acc[1] * scale);
+        o[1] = pack_bf16x2(acc[2] * scale, acc[3] * scale);
+        *reinterpret_cast<u32x2*>(part_dq + prow * D + 16 * dtw + 4 * q4) = o;
+      }
+    }
+    __syncthreads();                                   // before the next group is staged
+  }
+  // Rows 16*w + 4*q4 + r, d 16*dt + m16.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int s = s0 + 16 * w + 4 * q4 + r;
+    if (s >= n_kv) continue;
+    const int64_t base = ((int64_t)b * n_kv + s) * rs + (int64_t)g * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dk[base + 16 * dt + m16] = (uint16_t)bf16_bits(dka[dt][r] * scale);
+      dv[base + 16 * dt + m16] = (uint16_t)bf16_bits(dva[dt][r]);
+    }
+  }
+}
+
+// dq[t, h] = sum over the live slots of the row's partials.  Every slot is
+// loaded from an in-row address and dead ones are dropped with selects.
+template <int D, int G>
+__global__ __launch_bounds__(256) void sum_dq_partials(const uint16_t* __restrict__ part_dq,
+                                                       const int32_t* __restrict__ blk, uint16_t* __restrict__ dq,
+                                                       int64_t nrows, int n_q, int pos0, int h_q, int topk) {
+  constexpr int TPR = D / 8;
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // (b * n_q + t) * h_q + h
+  if (row >= nrows) return;
+  const int dl = threadIdx.x % TPR;
+  const int h = (int)(row % h_q);
+  const int64_t bt = row / h_q;
+  const int t = (int)(bt % n_q);
+  const int g = h / G, hh = h % G, h_kv = h_q / G;
+  const int jl = (pos0 + t) / kBlock;
+  const int64_t unit0 = (bt * h_kv + g) * topk;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < topk; s0 += 8) {
+    u32x4 o[8];
+    bool on[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = min(s0 + i, topk - 1);
+      const int jb = blk[unit0 + s];
+      on[i] = (s0 + i < topk) && jb >= 0 && jb <= jl;
+      o[i] = ld16(part_dq + ((unit0 + s) * G + hh) * D + dl * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t ov = on[i] ? o[i][e] : 0u;
+        acc[2 * e] += bf16_to_f32(ov & 0xffffu);
+        acc[2 * e + 1] += bf16_to_f32(ov >> 16);
+      }
+  }
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+  st16(dq + row * D + dl * 8, r);
+}
+
+template <int D, int LOG2G>
+hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const int32_t* blk, const uint16_t* out, const float* lse, const uint16_t* dout,
+                        float scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, void* ws, hipStream_t stream) {
+  constexpr int G = 1 << LOG2G;
+  constexpr int TPR = D / 8;
+  const PrefillWs L = prefill_ws_layout(d);
+  char* base = static_cast<char*>(ws);
+  const int* off = reinterpret_cast<const int*>(base + L.off);
+  const int* entries = reinterpret_cast<const int*>(base + L.entries);
+  uint16_t* part_dq = reinterpret_cast<uint16_t*>(base + L.part_o);
+  float* dcol = reinterpret_cast<float*>(base + L.part_ml);
+  const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_q;
+  const int64_t row_wgs = (nrows + 256 / TPR - 1) / (256 / TPR);
+  if (nrows > 0) {
+    LaunchTimer timer("bwd_row_dot", stream);
+    hipLaunchKernelGGL(bwd_row_dot<D>, dim3((unsigned)row_wgs), dim3(256), 0, stream, out, dout, dcol, nrows);
+  }
+  hipError_t e = launch_csr(d, blk, ws, stream);
+  if (e != hipSuccess) return e;
+  {
+    LaunchTimer timer("sparse_bwd_kv", stream);
+    hipLaunchKernelGGL((sparse_bwd_kv<D, LOG2G>), dim3((unsigned)L.lists), dim3(kBwdThreads), 0, stream, q, k, v,
+                       dout, lse, dcol, off, entries, part_dq, dk, dv, d.batch, d.n_q, d.n_kv, d.pos0, d.h_q, d.h_kv,
+                       d.nblk(), d.topk, scale * kLog2e, scale);
+  }
+  if (nrows > 0) {
+    LaunchTimer timer("sum_dq_partials", stream);
+    hipLaunchKernelGGL((sum_dq_partials<D, G>), dim3((unsigned)row_wgs), dim3(256), 0, stream, part_dq, blk, dq,
+                       nrows, d.n_q, d.pos0, d.h_q, d.topk);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t bwd_by_group(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* blk,
+                        const uint16_t* out, const float* lse, const uint16_t* dout, float scale, uint16_t* dq,
+                        uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+  switch (d.group()) {
+    case 1: return launch_bwd_t<D, 0>(d, q, k, v, blk, out, lse, dout, scale, dq, dk, dv, ws, s);
+    case 2: return launch_bwd_t<D, 1>(d, q, k, v, blk, out, lse, dout, scale, dq, dk, dv, ws, s);
+    case 4: return launch_bwd_t<D, 2>(d, q, k, v, blk, out, lse, dout, scale, dq, dk, dv, ws, s);
+    case 8: return launch_bwd_t<D, 3>(d, q, k, v, blk, out, lse, dout, scale, dq, dk, dv, ws, s);
+    default: return launch_bwd_t<D, 4>(d, q, k, v, blk, out, lse, dout, scale, dq, dk, dv, ws, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sparse_prefill_backward(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                          const int32_t* blk, const uint16_t* out, const float* lse,
+                                          const uint16_t* dout, float scale, uint16_t* dq, uint16_t* dk,
+                                          uint16_t* dv, void* ws, hipStream_t stream) {
+  if (d.d == 128) return bwd_by_group<128>(d, q, k, v, blk, out, lse, dout, scale, dq, dk, dv, ws, stream);
+  return bwd_by_group<64>(d, q, k, v, blk, out, lse, dout, scale, dq, dk, dv, ws, stream);
+}
+
+}  // namespace msa

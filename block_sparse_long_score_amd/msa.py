@@ -50,6 +50,7 @@ EXPORTED = (
     "msa_prefill_chunked_workspace_size",
     "msa_prefill_chunked",
     "msa_sparse_prefill_target",
+    "msa_sparse_prefill_backward",
 )
 
 
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
     L.msa_block_topk.argtypes = [D, P, P, VP]
     L.msa_sparse_prefill.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
     L.msa_sparse_decode.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
+    L.msa_sparse_prefill_backward.argtypes = [D, P, P, P, P, P, P, P, F, P, P, P, P, S, VP]
     L.msa_sparse_prefill_target.argtypes = [D, P, P, P, P, P, F, F, P, P, P, P, P, S, VP]
     L.msa_dense_gqa.argtypes = [D, P, P, P, F, P, P, P, S, VP]
     L.msa_index_topk_varlen.argtypes = [D, P, P, P, P, P, S, VP]
@@ -218,6 +220,27 @@ def msa_sparse_prefill_target(s: Shape, q, k, v, blk_idx, bscore, target, kl, ou
                                          ctypes.c_float(idx_scale), ctypes.c_float(scale), _ptr(out), _ptr(lse),
                                          _ptr(target), _ptr(kl), wp, wb, _stream(stream))
     _raise(st, "msa_sparse_prefill_target")
+
+
+def msa_sparse_prefill_backward(s: Shape, q, k, v, blk_idx, out, lse, dout, dq, dk, dv, workspace=None,
+                                scale: float = 0.0, stream=None) -> None:
+    """Gradients of msa_sparse_prefill's output w.r.t. q, k and v."""
+    _check(q, "q", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(k, "k", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(v, "v", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, s.n_q, s.h_kv, s.topk))
+    _check(out, "out", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(lse, "lse", torch.float32, (s.batch, s.n_q, s.h_q))
+    _check(dout, "dout", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(dq, "dq", torch.bfloat16, (s.batch, s.n_q, s.h_q, s.d))
+    _check(dk, "dk", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    _check(dv, "dv", torch.bfloat16, (s.batch, s.n_kv, s.h_kv, s.d))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_sparse_prefill_backward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx), _ptr(out),
+                                           _ptr(lse), _ptr(dout), ctypes.c_float(scale), _ptr(dq), _ptr(dk),
+                                           _ptr(dv), wp, wb, _stream(stream))
+    _raise(st, "msa_sparse_prefill_backward")
 
 
 def msa_sparse_decode(s: Shape, q, k, v, blk_idx, out, lse=None, workspace=None, scale: float = 0.0,

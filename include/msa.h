@@ -166,6 +166,29 @@ msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, co
                                      uint16_t* out, float* lse, float* target, float* kl, void* workspace,
                                      size_t workspace_bytes, msa_stream stream);
 
+/* Main branch, backward: gradients of msa_sparse_prefill's output with
+ * respect to q, k and v for the given selection (the selection is discrete
+ * and carries no gradient; Notion notes "Minimax-sparse-Attention",
+ * "Detached Gradients").  With P the softmax weights of a (query, head) over
+ * its visible keys and D = sum_d dout * out:
+ *   dv[s] = sum P dout,  dS = P (dout . v[s] - D),  dq = scale sum_s dS k[s],
+ *   dk[s] = scale sum dS q  (sums over the (query, head) pairs that see s).
+ *   q, k, v, blk_idx, scale   as given to msa_sparse_prefill;
+ *   out, lse  that call's outputs (lse is required here);
+ *   dout      [batch][n_q][h_q][d] bf16, the gradient of the loss w.r.t. out;
+ *   dq        [batch][n_q][h_q][d] bf16, output;
+ *   dk, dv    [batch][n_kv][h_kv][d] bf16, outputs, fully written (0 for keys
+ *             no query saw, and for every key when n_q == 0).
+ * Every key gradient is summed in one fixed order inside one workgroup, so the
+ * results are deterministic.  Workspace: msa_workspace_size(
+ * MSA_OP_SPARSE_PREFILL, dims); do not share one workspace between this call
+ * and a forward call in flight on another stream. */
+msa_status msa_sparse_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t* k,
+                                       const uint16_t* v, const int32_t* blk_idx, const uint16_t* out,
+                                       const float* lse, const uint16_t* dout, float scale, uint16_t* dq,
+                                       uint16_t* dk, uint16_t* dv, void* workspace, size_t workspace_bytes,
+                                       msa_stream stream);
+
 /* Main branch, decode: msa_sparse_prefill with n_q == 1; each of the batch
  * sequences has its own cache of n_kv tokens and its query at p = pos0
  * (normally n_kv - 1).  Streams only the selected blocks (lefilia.fr: a fixed

@@ -214,3 +214,28 @@ def test_target_argument_checks():
     need = lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d))
     assert call(d, wsb=need - 1) == WS
     assert call(dims(n_q=0), bscore=None, target=None, kl=None, ws=None) == OK
+
+
+def test_backward_argument_checks():
+    lib = M.lib()
+    d = dims()
+
+    def call(dd, ws=FAKE, wsb=1 << 40, **kw):
+        p = {n: kw.get(n, FAKE) for n in ("q", "k", "v", "blk", "out", "lse", "dout", "dq", "dk", "dv")}
+        return lib.msa_sparse_prefill_backward(ctypes.byref(dd), p["q"], p["k"], p["v"], p["blk"], p["out"],
+                                               p["lse"], p["dout"], ctypes.c_float(0.0), p["dq"], p["dk"],
+                                               p["dv"], ws, wsb, None)
+
+    for n in ("q", "k", "v", "blk", "out", "lse", "dout", "dq", "dk", "dv"):
+        assert call(d, **{n: None}) == NULL, n
+        assert call(d, **{n: ODD}) == ALIGN, n
+    assert call(dims(h_q=6, h_kv=2)) == UNSUP
+    assert call(dims(d=96)) == UNSUP
+    need = lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d))
+    assert call(d, wsb=need - 1) == WS
+    assert call(d, ws=None) == WS
+    # no queries: only the key gradients (zeros) are written, query-side pointers may be NULL
+    d0 = dims(n_q=0)
+    assert call(d0, q=None, blk=None, out=None, lse=None, dout=None, dq=None, wsb=0) == WS
+    assert call(d0, dk=None) == NULL
+    assert call(dims(batch=0), q=None, k=None, v=None, dk=None, dv=None, ws=None) == OK

@@ -1,0 +1,139 @@
+"""GPU parity of the main-branch backward (msa_sparse_prefill_backward) against
+the fp64 oracle.
+
+Tolerances, from the arithmetic: products are exact bf16 x bf16 in fp32; P and
+dS enter the dv, dk and dq contractions rounded to bf16 (relative 2^-9 per
+term), dq leaves the key-outer kernel as one bf16 partial per selected block,
+D = rowsum(dout * out) uses the forward's bf16 output, and every gradient is
+rounded to bf16 once.  The bound per tensor is
+    ||err||_2 / ||ref||_2 <= 1e-2   and   max |err| <= 2e-2 * max |ref|,
+plus, per row of dq (one (token, head)) and per key row of dk / dv with a norm
+of at least a tenth of the largest row, ||err|| / ||ref|| <= 5e-2: a dq row is a
+sum of terms whose dS add up to zero, so its cancellation can lift the 2^-9
+per-term rounding to a few percent of the row (3.2e-2 seen at most).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_score_amd import msa as M
+from block_sparse_long_score_amd.inputs import WORKLOADS, Shape, make_inputs
+from oracle import msa_oracle as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-2
+MAX_REL = 2e-2
+ROW_REL = 5e-2
+
+
+def make_dout(s: Shape, seed: int):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn((s.batch, s.n_q, s.h_q, s.d), generator=g).to(torch.bfloat16).cuda()
+
+
+def run_backward(s: Shape, inp, blk, dout):
+    ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
+    out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((s.batch, s.n_q, s.h_q), dtype=torch.float32, device="cuda")
+    M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws)
+    dq = torch.full((s.batch, s.n_q, s.h_q, s.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dk = torch.full((s.batch, s.n_kv, s.h_kv, s.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dv = torch.full_like(dk, float("nan"))
+    M.msa_sparse_prefill_backward(s, inp["q"], inp["k"], inp["v"], blk, out, lse, dout, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
+def check_grad(got: np.ndarray, ref: np.ndarray, what: str):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = got - ref
+    rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30)
+    mx = np.max(np.abs(err)) / max(np.max(np.abs(ref)), 1e-30)
+    rows_ref = np.linalg.norm(ref.reshape(-1, ref.shape[-1]), axis=1)
+    rows_err = np.linalg.norm(err.reshape(-1, ref.shape[-1]), axis=1)
+    big = rows_ref >= 0.1 * rows_ref.max() if rows_ref.size else rows_ref > 0
+    row_rel = float(np.max(rows_err[big] / rows_ref[big])) if np.any(big) else 0.0
+    print(f"  {what}: rel L2 {rel:.2e}, max {mx:.2e}, worst row {row_rel:.2e}", flush=True)
+    assert rel <= REL_L2 and mx <= MAX_REL and row_rel <= ROW_REL, what
+    if np.max(np.abs(ref)) == 0.0:
+        assert np.max(np.abs(got)) == 0.0, what
+
+
+CASES = {
+    # the 4096-token MQA workload, G = 4, d = 64
+    "tiny_prefill_4k": (1, WORKLOADS["tiny_prefill_4k"][1]),
+    # unaligned chunk, ragged n_q, partial last block (1000 % 128 = 104), G = 4
+    "chunk_ragged_g4": (11, Shape(1, 300, 1000, 700, 8, 2, 128, 128, topk=4)),
+    # two sequences, G = 16, d = 64, topk 3
+    "batch2_g16_d64": (12, Shape(2, 257, 600, 343, 16, 1, 64, 64, topk=3)),
+    # MHA, topk 2
+    "mha_d128": (13, Shape(1, 520, 520, 0, 8, 8, 128, 64, topk=2)),
+    # G = 2, topk 32 >= every causal block
+    "g2_topk32_all_blocks": (14, Shape(1, 130, 2100, 1970, 16, 8, 64, 128, topk=32)),
+    # G = 8 at the real head shape
+    "g8_chunk": (31, Shape(1, 700, 6000, 5300, 64, 8, 128, 128, topk=16)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_parity_every_row(name):
+    cid, s = CASES[name]
+    print(f"case {name}: {s}", flush=True)
+    inp = make_inputs(s, cid, device="cuda")
+    blk, _ = U.run_index(s, inp["q_idx"], inp["k_idx"])
+    dout = make_dout(s, 100 + cid)
+    dq, dk, dv = run_backward(s, inp, blk, dout)
+    dq2, dk2, dv2 = run_backward(s, inp, blk, dout)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2), "not deterministic"
+    blk_np = blk.cpu().numpy()
+    _, blk_ref = O.msa_index_topk(U.to64(inp["q_idx"]), U.to64(inp["k_idx"]), s.pos0, s.block, s.topk)
+    assert np.array_equal(blk_np, blk_ref.astype(np.int32))
+    rq, rk, rv = O.msa_sparse_attention_grad(U.to64(inp["q"]), U.to64(inp["k"]), U.to64(inp["v"]), blk_ref,
+                                             U.to64(dout), s.pos0, s.block)
+    check_grad(U.to64(dq), rq, f"{name} dq")
+    check_grad(U.to64(dk), rk, f"{name} dk")
+    check_grad(U.to64(dv), rv, f"{name} dv")
+
+
+def test_backward_caller_selection_with_padding():
+    """Hand-made selections: fewer blocks than k, -1 padding in any slot; keys
+    nobody selected must come back exactly 0."""
+    s = Shape(1, 64, 2048, 1984, 8, 2, 128, 128, topk=6)
+    inp = make_inputs(s, 23, device="cuda")
+    rng = np.random.default_rng(9)
+    blk = np.full((1, s.n_q, s.h_kv, s.topk), -1, dtype=np.int32)
+    for t in range(s.n_q):
+        jl = (s.pos0 + t) // s.block
+        for g in range(s.h_kv):
+            n = int(rng.integers(1, 4))
+            chosen = sorted(rng.choice(np.arange(2, jl), size=n - 1, replace=False).tolist() + [jl])
+            slots = sorted(rng.permutation(s.topk)[:n])
+            for sl, j in zip(slots, chosen):
+                blk[0, t, g, sl] = j
+    dout = make_dout(s, 77)
+    dq, dk, dv = run_backward(s, inp, torch.from_numpy(blk).cuda(), dout)
+    torch.cuda.synchronize()
+    rq, rk, rv = O.msa_sparse_attention_grad(U.to64(inp["q"]), U.to64(inp["k"]), U.to64(inp["v"]), blk,
+                                             U.to64(dout), s.pos0, s.block)
+    check_grad(U.to64(dq), rq, "caller dq")
+    check_grad(U.to64(dk), rk, "caller dk")
+    check_grad(U.to64(dv), rv, "caller dv")
+    assert float(dk[0, : 2 * s.block].abs().max()) == 0.0 and float(dv[0, : 2 * s.block].abs().max()) == 0.0
+
+
+def test_backward_without_queries_zeroes_key_gradients():
+    s = Shape(1, 0, 1000, 0, 8, 2, 64, 64, topk=4)
+    k = torch.randn((1, 1000, 2, 64)).to(torch.bfloat16).cuda()
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(k, float("nan"))
+    e = torch.empty((1, 0, 8, 64), dtype=torch.bfloat16, device="cuda")
+    ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
+    M.msa_sparse_prefill_backward(s, e, k, k, torch.empty((1, 0, 2, 4), dtype=torch.int32, device="cuda"), e,
+                                  torch.empty((1, 0, 8), dtype=torch.float32, device="cuda"), e, e, dk, dv, ws)
+    torch.cuda.synchronize()
+    assert float(dk.abs().max()) == 0.0 and float(dv.abs().max()) == 0.0

@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-topk-compare", action="store_true")
     ap.add_argument("--no-target", action="store_true", help="skip the index-branch target (KL) leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the main-branch backward leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -348,6 +349,30 @@ def main():
         log(f"index target: call {ms_t:.3f} ms, block_target_kl {ms_k:.3f} ms "
             f"({tb / (ms_k * 1e-3) / PEAK_HBM_BYTES:.1%} of HBM peak)")
         del target, kl
+
+    if not args.no_backward:
+        # Main-branch backward on the same selection: dq, dk, dv from a seeded
+        # output gradient; algorithmic work 10 d flops per (query head, visible
+        # key) (S, dP, dV, dK, dQ), i.e. 2.5x the forward's S4 count.
+        g = torch.Generator().manual_seed(7)
+        dout_b = torch.randn((s.batch, s.n_q, s.h_q, s.d), generator=g).to(torch.bfloat16).to(dev)
+        dq_b = torch.empty_like(dout_b)
+        dk_b = torch.empty_like(inp["k"])
+        dv_b = torch.empty_like(inp["v"])
+        M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws)
+        ms_b, _, kb = time_calls(torch, [lambda: M.msa_sparse_prefill_backward(
+            s, inp["q"], inp["k"], inp["v"], blk, out, lse, dout_b, dq_b, dk_b, dv_b, ws)], 3, 1, M)
+        fb = 2.5 * f_sp
+        n, tot = kb["sparse_bwd_kv"]
+        ms_kv = tot / n
+        result["backward"] = {"ms": ms_b, "tok_s": tokens / (ms_b * 1e-3), "algorithmic_flops": fb,
+                              "mfma_frac": fb / (ms_b * 1e-3) / PEAK_BF16_FLOPS,
+                              "sparse_bwd_kv_ms": ms_kv,
+                              "sparse_bwd_kv_mfma_frac": fb / (ms_kv * 1e-3) / PEAK_BF16_FLOPS,
+                              "kernels": {name: {"launches": c, "avg_ms": t / c} for name, (c, t) in kb.items()}}
+        log(f"backward {ms_b:.2f} ms (sparse_bwd_kv {ms_kv:.2f} ms, "
+            f"{fb / (ms_kv * 1e-3) / PEAK_BF16_FLOPS:.1%} of MFMA peak)")
+        del dout_b, dq_b, dk_b, dv_b
 
     if not args.no_dense:
         dout = torch.empty_like(out)

@@ -56,6 +56,10 @@ struct BwdLds {
       uint16_t ds[kBwdCols * kBlock];                  // [column][key]
       float lse2[kBwdCols], dcol[kBwdCols];
       int plim[kBwdCols];                              // last visible key position, -1 for an empty column
+      // Partial dq row of each column (the sink when empty), by group parity:
+      // the dq phase of one group reads it while faster waves already stage
+      // the next group.
+      int64_t prow[2][kBwdCols];
     } g;
   };
 };
@@ -83,17 +87,29 @@ __global__ __launch_bounds__(256) void bwd_row_dot(const uint16_t* __restrict__ 
   if (row < nrows && dl == 0) dcol[row] = sum;
 }
 
+// Registers of one column group in flight: this thread's 16-byte chunk of its
+// column's q and dout rows, the column's lse (log2 units), D and last visible
+// position, and the entry of the group that this buffer loads next (two groups
+// later).
+struct BwdStage {
+  u32x4 q, dout;
+  int64_t prow;
+  float lse2, dcol;
+  int plim, en_next;
+};
+
 template <int D, int LOG2G>
 __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dcol,
     const int* __restrict__ off, const int* __restrict__ entries, uint16_t* __restrict__ part_dq,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int batch, int n_q, int n_kv, int pos0, int h_q, int h_kv,
-    int nblk, int topk, float sl2, float scale) {
+    int64_t sink_row, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int batch, int n_q, int n_kv, int pos0,
+    int h_q, int h_kv, int nblk, int topk, float sl2, float scale) {
   constexpr int G = 1 << LOG2G;
   constexpr int DC = D / 8;                            // 16-byte chunks per row
   constexpr int DT = D / 16;                           // 16-wide d tiles
   constexpr int CTW = D / 64;                          // column tiles of dq per wave
+  constexpr int NST = kBwdCols * DC;                   // staging threads (one q and one dout chunk each)
   __shared__ BwdLds<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m16 = lane & 15, q4 = lane >> 4;
@@ -150,108 +166,138 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
     dka[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     dva[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int skey = s0 + mykey;
-  for (int c0 = 0; c0 < ncols; c0 += kBwdCols) {
-    if (tid < kBwdCols) {
-      const int gc = c0 + tid;
-      int pl = -1;
-      float l2 = 0.f, dc = 0.f;
-      if (gc < ncols) {
-        const int en = entries[e0 + (gc >> LOG2G)];
-        const int t = en >> 5;
-        const int64_t row = ((int64_t)b * n_q + t) * h_q + g * G + (gc & (G - 1));
-        pl = pos0 + t;
-        l2 = lse[row] * kLog2e;
-        dc = dcol[row];
-      }
-      sm.g.plim[tid] = pl;
-      sm.g.lse2[tid] = l2;
-      sm.g.dcol[tid] = dc;
+  const int ngroups = (ncols + kBwdCols - 1) / kBwdCols;
+  if (ngroups > 0) {
+    const int skey = s0 + mykey;
+    // Staging role: column scol of each group, chunk sch of its rows.  Threads
+    // beyond NST (d = 64) mirror the first NST and write the same values.
+    const int st_id = tid % NST, scol = st_id / DC, sch = st_id % DC;
+    // Every load of the loop reads a real row (the column index is clamped), so
+    // the loop body has no memory operation behind a branch and the compiler's
+    // wait counts stay exact across iterations; columns past the list end are
+    // masked through plim = -1 and their dq goes to the sink row.
+    auto entry_at = [&](int grp) {
+      const int gc = min(grp * kBwdCols + scol, ncols - 1);
+      return entries[e0 + (gc >> LOG2G)];
+    };
+    auto fetch = [&](BwdStage& st, int grp, int en) {
+      const int gc = grp * kBwdCols + scol;
+      const int hh = min(gc, ncols - 1) & (G - 1);
+      const int t = en >> 5;
+      const int64_t row = ((int64_t)b * n_q + t) * h_q + g * G + hh;
+      st.q = ld16(q + row * D + sch * 8);
+      st.dout = ld16(dout + row * D + sch * 8);
+      st.lse2 = lse[row] * kLog2e;
+      st.dcol = dcol[row];
+      // Selects by mask, not a ternary: a branch here would make the
+      // compiler's wait counts at the loop head conservative.
+      const int64_t live = -(int64_t)(gc < ncols);
+      const int64_t pr = ((((int64_t)b * n_q + t) * h_kv + g) * topk + (en & 31)) * G + hh;
+      st.plim = (int)(((int64_t)(pos0 + t) & live) | (-1 & ~live));
+      st.prow = (pr & live) | (sink_row & ~live);
+    };
+    BwdStage sx, sy;
+    {
+      const int en0 = entry_at(0), en1 = entry_at(1);
+      fetch(sx, 0, en0);
+      fetch(sy, 1, en1);
+      sx.en_next = entry_at(2);
+      sy.en_next = entry_at(3);
     }
-    for (int it = tid; it < 2 * kBwdCols * DC; it += kBwdThreads) {
-      const int which = it / (kBwdCols * DC), rem = it % (kBwdCols * DC), col = rem / DC, ch = rem % DC;
-      const int gc = c0 + col;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (gc < ncols) {
-        const int en = entries[e0 + (gc >> LOG2G)];
-        const int64_t row = ((int64_t)b * n_q + (en >> 5)) * h_q + g * G + (gc & (G - 1));
-        val = ld16((which ? dout : q) + row * D + ch * 8);
-      }
-      st16(&(which ? sm.g.dor : sm.g.qr)[rt_off<D>(col, ch)], val);
-      uint16_t* tt = which ? sm.g.dot : sm.g.qt;
+    auto step = [&](BwdStage& st, int grp) {
+      // No branch here: every thread of a column writes the same meta values.
+      st16(&sm.g.qr[rt_off<D>(scol, sch)], st.q);
+      st16(&sm.g.dor[rt_off<D>(scol, sch)], st.dout);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tt[tt_off(8 * ch + e, col)] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
-    }
-    __syncthreads();
+      for (int e = 0; e < 8; ++e) {
+        sm.g.qt[tt_off(8 * sch + e, scol)] = (uint16_t)(st.q[e >> 1] >> (16 * (e & 1)));
+        sm.g.dot[tt_off(8 * sch + e, scol)] = (uint16_t)(st.dout[e >> 1] >> (16 * (e & 1)));
+      }
+      sm.g.plim[scol] = st.plim;
+      sm.g.lse2[scol] = st.lse2;
+      sm.g.dcol[scol] = st.dcol;
+      sm.g.prow[grp & 1][scol] = st.prow;
+      __syncthreads();
+      // Refill this buffer with the group two ahead, and its entry with the
+      // group four ahead.
+      {
+        const int en = st.en_next;
+        fetch(st, grp + 2, en);
+        st.en_next = entry_at(grp + 4);
+      }
+      // S^T and dP^T for this wave's 16 keys and the 32 columns: lane holds
+      // column 16*ct + 4*q4 + r, key mykey.
+      f32x4 sacc[2], dpacc[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dpacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          sacc[ct] = mfma_16x16x32(ld16(&sm.g.qr[rt_off<D>(16 * ct + m16, 4 * c + q4)]), kop[c], sacc[ct]);
+          dpacc[ct] = mfma_16x16x32(ld16(&sm.g.dor[rt_off<D>(16 * ct + m16, 4 * c + q4)]), vop[c], dpacc[ct]);
+        }
+      }
+      float p[2][4], ds[2][4];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int col = 16 * ct + 4 * q4 + r;
+          const float x = fmaf(sacc[ct][r], sl2, -sm.g.lse2[col]);
+          const float pv = __builtin_amdgcn_exp2f(skey <= sm.g.plim[col] ? x : -INFINITY);
+          p[ct][r] = pv;
+          ds[ct][r] = pv * (dpacc[ct][r] - sm.g.dcol[col]);
+        }
+      // A operands (row = this lane's key) with contraction slot 8*q4 + i <->
+      // column 4*q4 + i (i < 4) or 16 + 4*q4 + i - 4 (i >= 4).
+      const u32x4 pa = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                        pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+      const u32x4 dsa = {pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
+                         pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + m16;
+        const u32x2 dlo = *reinterpret_cast<const u32x2*>(&sm.g.dot[tt_off(d, 4 * q4)]);
+        const u32x2 dhi = *reinterpret_cast<const u32x2*>(&sm.g.dot[tt_off(d, 16 + 4 * q4)]);
+        dva[dt] = mfma_16x16x32(pa, u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, dva[dt]);
+        const u32x2 qlo = *reinterpret_cast<const u32x2*>(&sm.g.qt[tt_off(d, 4 * q4)]);
+        const u32x2 qhi = *reinterpret_cast<const u32x2*>(&sm.g.qt[tt_off(d, 16 + 4 * q4)]);
+        dka[dt] = mfma_16x16x32(dsa, u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dka[dt]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sm.g.ds[ds_off(16 * ct + 4 * q4 + r, mykey)] =
+              (uint16_t)((r & 1) ? (dsa[2 * ct + (r >> 1)] >> 16) : (dsa[2 * ct + (r >> 1)] & 0xffffu));
+      __syncthreads();
 
-    // S^T and dP^T for this wave's 16 keys and the 32 columns: lane holds
-    // column 16*ct + 4*q4 + r, key mykey.
-    f32x4 st[2], dpt[2];
+      // dq slice: rows d 16*dtw + 4*q4 + r of column 16*ct + m16.
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      st[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dpt[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < CTW; ++i) {
+        const int ct = ct0 + i;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        st[ct] = mfma_16x16x32(ld16(&sm.g.qr[rt_off<D>(16 * ct + m16, 4 * c + q4)]), kop[c], st[ct]);
-        dpt[ct] = mfma_16x16x32(ld16(&sm.g.dor[rt_off<D>(16 * ct + m16, 4 * c + q4)]), vop[c], dpt[ct]);
-      }
-    }
-    float p[2][4], ds[2][4];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = 16 * ct + 4 * q4 + r;
-        const float pv = skey <= sm.g.plim[col]
-                             ? __builtin_amdgcn_exp2f(fmaf(st[ct][r], sl2, -sm.g.lse2[col]))
-                             : 0.f;
-        p[ct][r] = pv;
-        ds[ct][r] = pv * (dpt[ct][r] - sm.g.dcol[col]);
-      }
-    // A operands (row = this lane's key) with contraction slot 8*q4 + i <->
-    // column 4*q4 + i (i < 4) or 16 + 4*q4 + i - 4 (i >= 4).
-    const u32x4 pa = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
-                      pack_bf16x2(p[1][2], p[1][3])};
-    const u32x4 dsa = {pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
-                       pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])};
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 16 * dt + m16;
-      const u32x2 dlo = *reinterpret_cast<const u32x2*>(&sm.g.dot[tt_off(d, 4 * q4)]);
-      const u32x2 dhi = *reinterpret_cast<const u32x2*>(&sm.g.dot[tt_off(d, 16 + 4 * q4)]);
-      dva[dt] = mfma_16x16x32(pa, u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, dva[dt]);
-      const u32x2 qlo = *reinterpret_cast<const u32x2*>(&sm.g.qt[tt_off(d, 4 * q4)]);
-      const u32x2 qhi = *reinterpret_cast<const u32x2*>(&sm.g.qt[tt_off(d, 16 + 4 * q4)]);
-      dka[dt] = mfma_16x16x32(dsa, u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dka[dt]);
-    }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sm.g.ds[ds_off(16 * ct + 4 * q4 + r, mykey)] =
-            (uint16_t)((r & 1) ? (dsa[2 * ct + (r >> 1)] >> 16) : (dsa[2 * ct + (r >> 1)] & 0xffffu));
-    __syncthreads();
-
-    // dq slice: rows d 16*dtw + 4*q4 + r of column 16*ct + m16.
-#pragma unroll
-    for (int i = 0; i < CTW; ++i) {
-      const int ct = ct0 + i;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        acc = mfma_16x16x32(ktop[kc], ld16(&sm.g.ds[ds_off(16 * ct + m16, 32 * kc + 8 * q4)]), acc);
-      const int gc = c0 + 16 * ct + m16;
-      if (gc < ncols) {
-        const int en = entries[e0 + (gc >> LOG2G)];
-        const int64_t prow = ((((int64_t)b * n_q + (en >> 5)) * h_kv + g) * topk + (en & 31)) * G + (gc & (G - 1));
+        for (int kc = 0; kc < 4; ++kc)
+          acc = mfma_16x16x32(ktop[kc], ld16(&sm.g.ds[ds_off(16 * ct + m16, 32 * kc + 8 * q4)]), acc);
+        const int64_t prow = sm.g.prow[grp & 1][16 * ct + m16];
         u32x2 o;
         o[0] = pack_bf16x2(acc[0] * scale, acc[1] * scale);
         o[1] = pack_bf16x2(acc[2] * scale, acc[3] * scale);
         *reinterpret_cast<u32x2*>(part_dq + prow * D + 16 * dtw + 4 * q4) = o;
       }
+    };
+    // Drain the prologue's loads: the wait counts at the loop head are the
+    // merge of the entry and back-edge states, and an empty entry state keeps
+    // them those of the loop itself (which waits only for the buffer in use).
+    __builtin_amdgcn_s_waitcnt(0);
+    // Groups go in pairs so that each buffer's role is fixed in the code; an
+    // odd last group is followed by one fully masked group.
+    for (int grp = 0; grp < ngroups; grp += 2) {
+      step(sx, grp);
+      step(sy, grp + 1);
     }
-    __syncthreads();                                   // before the next group is staged
   }
   // Rows 16*w + 4*q4 + r, d 16*dt + m16.
 #pragma unroll
@@ -334,8 +380,8 @@ hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, const uint16_t* k, con
   {
     LaunchTimer timer("sparse_bwd_kv", stream);
     hipLaunchKernelGGL((sparse_bwd_kv<D, LOG2G>), dim3((unsigned)L.lists), dim3(kBwdThreads), 0, stream, q, k, v,
-                       dout, lse, dcol, off, entries, part_dq, dk, dv, d.batch, d.n_q, d.n_kv, d.pos0, d.h_q, d.h_kv,
-                       d.nblk(), d.topk, scale * kLog2e, scale);
+                       dout, lse, dcol, off, entries, part_dq, L.entries_max * G, dk, dv, d.batch, d.n_q, d.n_kv,
+                       d.pos0, d.h_q, d.h_kv, d.nblk(), d.topk, scale * kLog2e, scale);
   }
   if (nrows > 0) {
     LaunchTimer timer("sum_dq_partials", stream);

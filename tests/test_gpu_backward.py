@@ -137,3 +137,49 @@ def test_backward_without_queries_zeroes_key_gradients():
                                   torch.empty((1, 0, 8), dtype=torch.float32, device="cuda"), e, e, dk, dv, ws)
     torch.cuda.synchronize()
     assert float(dk.abs().max()) == 0.0 and float(dv.abs().max()) == 0.0
+
+
+def test_backward_full_size_prefill_128k_sampled():
+    """The 131,072-token workload in the benchmark's launch configuration: dq on
+    sampled (token, group) rows, dk and dv on every key of two whole blocks of
+    one group (one selected by ~1,300 queries, one near the end)."""
+    from block_sparse_long_score_amd.inputs import sample_rows
+    cid, s = WORKLOADS["prefill_128k"]
+    inp = make_inputs(s, cid, device="cuda")
+    blk, bscore = U.run_index(s, inp["q_idx"], inp["k_idx"])
+    dout = make_dout(s, 4242)
+    dq, dk, dv = run_backward(s, inp, blk, dout)
+    torch.cuda.synchronize()
+    print("  gpu done", flush=True)
+    scale = O.default_scale(s.d)
+    G = s.group
+    rows = [(0, t) for t in sample_rows(s.n_q, 6, 1000 * cid + 55, [0, s.n_q - 1])]
+    kseq = U.to64(inp["k_idx"][0])
+    sels = U.check_index_rows(s, lambda b, t: U.to64(inp["q_idx"][b, t]), lambda b: kseq, blk, bscore, rows)
+    g_dk = 5
+    keys64 = {g: U.to64(inp["k"][0, :, g]) for g in range(s.h_kv)}
+    vals64 = {g: U.to64(inp["v"][0, :, g]) for g in range(s.h_kv)}
+    ref_dq, got_dq = [], []
+    for (b, t, g), sel in sels.items():
+        pos = O.visible_positions(sel, s.pos0 + t, s.block, s.n_kv)
+        gq, _, _ = O.softmax_attention_grad(U.to64(inp["q"][b, t, g * G:(g + 1) * G]), keys64[g][pos],
+                                            vals64[g][pos], U.to64(dout[b, t, g * G:(g + 1) * G]), scale)
+        ref_dq.append(gq)
+        got_dq.append(U.to64(dq[b, t, g * G:(g + 1) * G]))
+    check_grad(np.stack(got_dq), np.stack(ref_dq), "128k dq rows")
+    blk_g = blk[0, :, g_dk].cpu().numpy()
+    for j in (512, s.nblk - 3):
+        ts = np.nonzero((blk_g == j).any(axis=1))[0]
+        print(f"  block {j}: {len(ts)} queries", flush=True)
+        rk = np.zeros((s.block, s.d))
+        rv = np.zeros((s.block, s.d))
+        for t in ts:
+            pos = O.visible_positions(blk_g[t], s.pos0 + t, s.block, s.n_kv)
+            _, gk, gv = O.softmax_attention_grad(U.to64(inp["q"][0, t, g_dk * G:(g_dk + 1) * G]), keys64[g_dk][pos],
+                                                 vals64[g_dk][pos], U.to64(dout[0, t, g_dk * G:(g_dk + 1) * G]),
+                                                 scale)
+            inb = (pos >= j * s.block) & (pos < (j + 1) * s.block)
+            rk[pos[inb] - j * s.block] += gk[inb]
+            rv[pos[inb] - j * s.block] += gv[inb]
+        check_grad(U.to64(dk[0, j * s.block:(j + 1) * s.block, g_dk]), rk, f"128k dk block {j}")
+        check_grad(U.to64(dv[0, j * s.block:(j + 1) * s.block, g_dk]), rv, f"128k dv block {j}")

@@ -51,8 +51,12 @@ the branches).  Readings:
       pooled block scores over the same selected blocks (the pages name no
       temperature, so idx_scale is the caller's);
   r16 the loss is KL(target || index) in nats, with 0 log 0 = 0;
-  r17 "detached": the target is returned as a plain value; nothing here
-      differentiates anything.
+  r17 "detached": the target is returned as a plain value, and every
+      gradient below treats it as a constant;
+  r18 the index-branch gradient of the KL loss treats the target as a
+      constant and the selection as fixed; the block max-pool passes the
+      gradient of a pooled score to its argmax token, the lowest position
+      among equal maxima.
 
 Main-branch backward: the gradients of the selected-block softmax attention
 with respect to q, k and v for a fixed selection (the selection itself is
@@ -433,3 +437,56 @@ def msa_sparse_attention_grad(q: np.ndarray, k: np.ndarray, v: np.ndarray, blk_i
                 dk[bi, pos, g] += gk
                 dv[bi, pos, g] += gv
     return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# Index-branch backward (gradient of the KL loss; target detached)
+# ----------------------------------------------------------------------------
+
+def block_argmax(scores: np.ndarray, j: int, p: int, block: int) -> int:
+    """Position of the largest causal token score in block j (reading r18:
+    the max-pool passes its gradient to one token, the lowest position among
+    equal maxima)."""
+    lo, hi = j * block, min((j + 1) * block, p + 1)
+    return lo + int(np.argmax(scores[lo:hi]))
+
+
+def index_kl_grad(q_idx: np.ndarray, k_idx: np.ndarray, blk_idx: np.ndarray, target: np.ndarray,
+                  idx_scale: float, dkl: np.ndarray, pos0: int, block: int):
+    """Gradient of sum_rows dkl[row] * KL(target || index distribution) with
+    respect to q_idx and k_idx, for a fixed selection and a detached target
+    (Notion notes "Minimax-sparse-Attention": "KL Loss Alignment" trains the
+    index branch to imitate the main branch, "Detached Gradients" keeps the
+    target out of the gradient).
+
+    For a row with live slots s: a_s = idx_scale * pooled[j_s], index_s =
+    softmax(a)_s, dKL/da_s = index_s - target_s; the pooled score is a max over
+    the block's causal tokens, so its gradient goes to the argmax token s*:
+    dq_idx += idx_scale (index_s - target_s) k_idx[s*], dk_idx[s*] += the same
+    coefficient times q_idx (times dkl[row]).  Returns float64 (dq_idx, dk_idx)
+    shaped like q_idx and k_idx.
+    """
+    b, n_q, h_kv, _ = q_idx.shape
+    dq = np.zeros(q_idx.shape, dtype=np.float64)
+    dk = np.zeros(k_idx.shape, dtype=np.float64)
+    for bi in range(b):
+        kseq = np.asarray(k_idx[bi], dtype=np.float64)
+        for i in range(n_q):
+            p = pos0 + i
+            for g in range(h_kv):
+                qrow = np.asarray(q_idx[bi, i, g], dtype=np.float64)
+                sc = token_scores(qrow, kseq, p)
+                sel = blk_idx[bi, i, g]
+                live = [s for s, j in enumerate(sel) if j >= 0]
+                if not live:
+                    continue
+                pooled = block_max_pool(sc, p, block)
+                a = np.array([idx_scale * pooled[sel[s]] for s in live])
+                e = np.exp(a - a.max())
+                qd = e / e.sum()
+                for n, s in enumerate(live):
+                    coef = dkl[bi, i, g] * idx_scale * (qd[n] - target[bi, i, g, s])
+                    star = block_argmax(sc, int(sel[s]), p, block)
+                    dq[bi, i, g] += coef * kseq[star]
+                    dk[bi, star] += coef * qrow
+    return dq, dk

@@ -235,3 +235,42 @@ def test_backward_unscaled_key_gradient_is_caught(monkeypatch):
 def test_backward_unweighted_rowsum_is_caught(monkeypatch):
     monkeypatch.setattr(O, "softmax_attention_grad", mut_grad_rowsum_of_dp)
     assert fails(TB.test_grads_match_torch_autograd, 4, 1, 2)
+
+
+# ---- index-branch backward --------------------------------------------------
+
+from tests import test_oracle_index_grad as TG   # noqa: E402
+
+
+def mut_argmax_last(scores, j, p, block):
+    lo, hi = j * block, min((j + 1) * block, p + 1)
+    seg = scores[lo:hi]
+    return lo + int(len(seg) - 1 - np.argmax(seg[::-1]))
+
+
+ORIG_KL_GRAD = O.index_kl_grad
+
+
+def mut_kl_grad_sign(q_idx, k_idx, blk, target, idx_scale, dkl, pos0, block):
+    dq, dk = ORIG_KL_GRAD(q_idx, k_idx, blk, target, idx_scale, dkl, pos0, block)
+    return -dq, -dk
+
+
+def mut_kl_grad_no_scale(q_idx, k_idx, blk, target, idx_scale, dkl, pos0, block):
+    dq, dk = ORIG_KL_GRAD(q_idx, k_idx, blk, target, idx_scale, dkl, pos0, block)
+    return dq / idx_scale, dk / idx_scale
+
+
+def test_index_grad_tie_to_last_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "block_argmax", mut_argmax_last)
+    assert fails(TG.test_tied_maxima_send_the_key_gradient_to_the_lower_position)
+
+
+def test_index_grad_sign_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "index_kl_grad", mut_kl_grad_sign)
+    assert fails(TG.test_grad_matches_central_differences, 0.7)
+
+
+def test_index_grad_missing_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "index_kl_grad", mut_kl_grad_no_scale)
+    assert fails(TG.test_grad_matches_torch_autograd)

@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-topk-compare", action="store_true")
     ap.add_argument("--no-target", action="store_true", help="skip the index-branch target (KL) leg")
-    ap.add_argument("--no-backward", action="store_true", help="skip the main-branch backward leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the main-branch and index-branch backward legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -373,6 +373,22 @@ def main():
         log(f"backward {ms_b:.2f} ms (sparse_bwd_kv {ms_kv:.2f} ms, "
             f"{fb / (ms_kv * 1e-3) / PEAK_BF16_FLOPS:.1%} of MFMA peak)")
         del dout_b, dq_b, dk_b, dv_b
+        # Index-branch backward (gradient of the KL alignment loss) on the
+        # same selection, with the target of msa_sparse_prefill_target.
+        target = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.float32, device=dev)
+        kl = torch.empty((s.batch, s.n_q, s.h_kv), dtype=torch.float32, device=dev)
+        idx_scale = 1.0 / math.sqrt(s.d_idx)
+        M.msa_sparse_prefill_target(s, inp["q"], inp["k"], inp["v"], blk, bscore, target, kl, out, lse, ws,
+                                    idx_scale=idx_scale)
+        dkl = torch.ones_like(kl)
+        dqi = torch.empty((s.batch, s.n_q, s.h_kv, s.d_idx), dtype=torch.float32, device=dev)
+        dki = torch.empty((s.batch, s.n_kv, s.d_idx), dtype=torch.float32, device=dev)
+        ms_i, _, ki = time_calls(torch, [lambda: M.msa_index_backward(
+            s, inp["q_idx"], inp["k_idx"], blk, bscore, target, dkl, dqi, dki, ws, idx_scale=idx_scale)], 3, 1, M)
+        result["index_backward"] = {"ms": ms_i, "kernels": {name: {"launches": c, "avg_ms": t / c}
+                                                            for name, (c, t) in ki.items()}}
+        log(f"index backward {ms_i:.2f} ms")
+        del target, kl, dkl, dqi, dki
 
     if not args.no_dense:
         dout = torch.empty_like(out)

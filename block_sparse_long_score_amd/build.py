@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
 
-SOURCES = ["api.cpp", "profile.cpp", "index_score.hip", "block_topk.hip", "sparse_attn.hip", "sparse_bwd.hip", "dense_attn.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "index_score.hip", "block_topk.hip", "sparse_attn.hip", "sparse_bwd.hip", "index_bwd.hip", "dense_attn.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -212,6 +212,27 @@ msa_status msa_sparse_prefill_backward(const msa_dims* dims, const uint16_t* q, 
                                                         static_cast<hipStream_t>(stream)));
 }
 
+msa_status msa_index_backward(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
+                              const int32_t* blk_idx, const float* bscore, const float* target, const float* dkl,
+                              float idx_scale, float* dq_idx, float* dk_idx, void* workspace, size_t workspace_bytes,
+                              msa_stream stream) {
+  msa_status st = check_dims(dims, kNeedDIdx | kCsr);
+  if (st != MSA_OK) return st;
+  if (!std::isfinite(idx_scale)) return MSA_ERR_SHAPE;
+  if (dims->batch == 0) return MSA_OK;
+  if (!k_idx || !dk_idx) return MSA_ERR_NULL;
+  if (dims->n_q > 0 && (!q_idx || !blk_idx || !bscore || !target || !dkl || !dq_idx)) return MSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(k_idx) || misaligned(blk_idx) || misaligned(bscore) || misaligned(target) ||
+      misaligned(dkl) || misaligned(dq_idx) || misaligned(dk_idx))
+    return MSA_ERR_ALIGN;
+  const Dims d = to_dims(*dims);
+  const size_t need = msa::prefill_ws_layout(d).total;
+  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_index_backward(d, q_idx, k_idx, blk_idx, bscore, target, dkl, idx_scale, dq_idx,
+                                               dk_idx, workspace, static_cast<hipStream_t>(stream)));
+}
+
 msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
                              size_t workspace_bytes, msa_stream stream) {

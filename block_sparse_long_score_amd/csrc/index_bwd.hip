@@ -1,0 +1,288 @@
+// Index branch, backward: gradient of the KL alignment loss with respect to the
+// index queries and keys (Notion notes "Minimax-sparse-Attention": "KL Loss
+// Alignment" trains the index branch to imitate the main branch's attention
+// distribution; "Detached Gradients": the target is a constant and nothing
+// flows into the main branch).  For a (b, t, g) row with live slots s:
+//   a_s = idx_scale * pooled[j_s],  index = softmax(a),
+//   coef_s = dkl[row] * idx_scale * (index_s - target_s),
+// and the pooled score is a max over the block's causal tokens, so the
+// gradient goes to its argmax token s* (the lowest position among equal
+// maxima):  dq_idx[row] += coef_s k_idx[s*],  dk_idx[s*] += coef_s q_idx[row].
+//
+// Three kernels: the per-row coefficients; a KV-outer pass, one workgroup per
+// (b, block), that recomputes the scores of every entry of the block's lists
+// (all groups share the index key) by MFMA, takes each entry's argmax and
+// accumulates dk_idx for the block's keys in LDS in list order (deterministic,
+// no atomics); and a per-row gather for dq_idx.
+#include "launch.h"
+#include "msa_device.h"
+
+namespace msa {
+namespace {
+
+constexpr int kIbThreads = 512;
+constexpr int kIbCols = 32;                            // entries per group
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+
+// Min over the 16 lanes of a row (the same DPP pattern as row_reduce).
+__device__ __forceinline__ int row_min16(int v) {
+  v = min(v, dpp_i<0xb1>(v));
+  v = min(v, dpp_i<0x4e>(v));
+  v = min(v, dpp_i<0x141>(v));
+  v = min(v, dpp_i<0x140>(v));
+  return v;
+}
+
+// coef[row][s] for the live slots, 0 for the others; R lanes per row.
+template <int R>
+__global__ __launch_bounds__(256) void index_kl_coef(const int32_t* __restrict__ blk,
+                                                     const float* __restrict__ bscore,
+                                                     const float* __restrict__ target,
+                                                     const float* __restrict__ dkl, float* __restrict__ coef,
+                                                     int64_t nrows, int n_q, int h_kv, int pos0, int topk, int nblk,
+                                                     float idx_scale) {
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / R;   // (b * n_q + t) * h_kv + g
+  const int s = threadIdx.x % R;
+  const int64_t rr = row < nrows ? row : nrows - 1;
+  const int t = (int)((rr / h_kv) % n_q);
+  const int jl = (pos0 + t) / kBlock;
+  const int sc = min(s, topk - 1);
+  const int j = blk[rr * topk + sc];
+  const bool on = s < topk && j >= 0 && j <= jl;
+  const auto fmax = [](float x, float y) { return vmax(x, y); };
+  const auto fadd = [](float x, float y) { return x + y; };
+  const float sl2 = idx_scale * kLog2e;
+  const float a = on ? bscore[rr * nblk + (on ? j : 0)] * sl2 : -INFINITY;
+  const float A = row_reduce<R>(a, fmax);
+  const float e = on ? __builtin_amdgcn_exp2f(a - A) : 0.f;
+  const float Z = row_reduce<R>(e, fadd);
+  const float tg = target[rr * topk + sc];
+  const float c = on ? dkl[rr] * idx_scale * (e / Z - tg) : 0.f;
+  if (row < nrows && s < topk) coef[row * topk + s] = c;
+}
+
+template <int DI>
+struct IbLds {
+  float dk[kBlock * DI];                               // dk_idx of the block's keys
+  union {
+    uint16_t k[kBlock * DI];                           // the block's index keys, while loaded
+    struct {
+      uint16_t qr[kIbCols * DI];                       // [entry][d] index queries
+      float coef[kIbCols];
+      int plim[kIbCols];                               // last visible position, -1 for an empty column
+      int slot_row[kIbCols];                           // (b * n_q + t) * h_kv + g) * topk + slot, -1 if empty
+      float wmax[8][kIbCols];
+      int wkey[8][kIbCols];
+      int amax[kIbCols];                               // argmax key in the block, -1 if empty
+    } g;
+  };
+};
+
+template <int DI>
+__global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const int* __restrict__ off,
+    const int* __restrict__ entries, const float* __restrict__ coef, int* __restrict__ amax_out,
+    float* __restrict__ dk_idx, int batch, int n_q, int n_kv, int pos0, int h_kv, int nblk, int topk) {
+  constexpr int DC = DI / 8;
+  __shared__ IbLds<DI> sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int m16 = lane & 15, q4 = lane >> 4;
+  const int j = blockIdx.x / batch, b = blockIdx.x % batch;   // early blocks (most entries) first
+  const int s0 = j * kBlock;
+  const uint16_t* kb = k_idx + (int64_t)b * n_kv * DI;
+
+  for (int i = tid; i < kBlock * DI; i += kIbThreads) sm.dk[i] = 0.f;
+  for (int it = tid; it < kBlock * DC; it += kIbThreads) {
+    const int key = it / DC, ch = it % DC, s = s0 + key;
+    st16(&sm.k[rt_off<DI>(key, ch)], s < n_kv ? ld16(kb + (int64_t)s * DI + ch * 8) : u32x4{0u, 0u, 0u, 0u});
+  }
+  __syncthreads();
+  // B operands of S^T: column (MFMA n) = this lane's key, contraction slots
+  // 8*q4 + i = d 32*c + 8*q4 + i.
+  const int mykey = 16 * w + m16;
+  u32x4 kop[DI / 32];
+#pragma unroll
+  for (int c = 0; c < DI / 32; ++c) kop[c] = ld16(&sm.k[rt_off<DI>(mykey, 4 * c + q4)]);
+  __syncthreads();                                     // the LDS now holds entry groups
+  const int skey = s0 + mykey;
+
+  for (int g = 0; g < h_kv; ++g) {
+    const int list = (b * h_kv + g) * nblk + j;
+    const int e0 = off[list], e1 = off[list + 1];
+    for (int c0 = e0; c0 < e1; c0 += kIbCols) {
+      // Stage the entries' index queries and per-column values.
+      for (int it = tid; it < kIbCols * DC; it += kIbThreads) {
+        const int col = it / DC, ch = it % DC, e = c0 + col;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (e < e1) {
+          const int t = entries[e] >> 5;
+          val = ld16(q_idx + (((int64_t)b * n_q + t) * h_kv + g) * DI + ch * 8);
+        }
+        st16(&sm.g.qr[rt_off<DI>(col, ch)], val);
+      }
+      if (tid < kIbCols) {
+        const int e = c0 + tid;
+        int pl = -1, sr = -1;
+        float cf = 0.f;
+        if (e < e1) {
+          const int en = entries[e], t = en >> 5;
+          sr = (int)((((int64_t)b * n_q + t) * h_kv + g) * topk + (en & 31));
+          pl = pos0 + t;
+          cf = coef[sr];
+        }
+        sm.g.plim[tid] = pl;
+        sm.g.slot_row[tid] = sr;
+        sm.g.coef[tid] = cf;
+      }
+      __syncthreads();
+      // S^T for this wave's 16 keys: lane holds column 16*ct + 4*q4 + r.
+      f32x4 sacc[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < DI / 32; ++c)
+          sacc[ct] = mfma_16x16x32(ld16(&sm.g.qr[rt_off<DI>(16 * ct + m16, 4 * c + q4)]), kop[c], sacc[ct]);
+      }
+      // Per column: the wave's max over its keys and the lowest key that has it.
+      const auto fmax = [](float x, float y) { return vmax(x, y); };
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int col = 16 * ct + 4 * q4 + r;
+          const float v = skey <= sm.g.plim[col] ? sacc[ct][r] : -INFINITY;
+          const float m = row_reduce<16>(v, fmax);
+          const int kk = row_min16(v == m && m > -INFINITY ? mykey : 1 << 20);
+          if (m16 == 0) {
+            sm.g.wmax[w][col] = m;
+            sm.g.wkey[w][col] = kk;
+          }
+        }
+      __syncthreads();
+      // Across waves (ascending key ranges): the first wave that reaches the
+      // column's maximum holds its lowest argmax.
+      if (tid < kIbCols) {
+        float best = -INFINITY;
+        int key = -1;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) {
+          const float m = sm.g.wmax[ww][tid];
+          if (m > best) {
+            best = m;
+            key = sm.g.wkey[ww][tid];
+          }
+        }
+        const int sr = sm.g.slot_row[tid];
+        if (sr < 0) key = -1;
+        sm.g.amax[tid] = key;
+        if (sr >= 0) amax_out[sr] = key < 0 ? -1 : s0 + key;
+      }
+      __syncthreads();
+      // dk_idx rows of this wave's keys, columns in list order.
+      for (int col = 0; col < kIbCols; ++col) {
+        const int key = sm.g.amax[col];
+        if ((key >> 4) != w) continue;                 // wave-uniform
+        const float cf = sm.g.coef[col];
+        for (int d = lane; d < DI; d += 64) {
+          const int ch = d >> 3;
+          const float qv = bf16_to_f32(sm.g.qr[rt_off<DI>(col, ch) + (d & 7)]);
+          sm.dk[key * DI + d] = fmaf(cf, qv, sm.dk[key * DI + d]);
+        }
+      }
+      __syncthreads();                                 // before the next group is staged
+    }
+  }
+  for (int i = tid; i < kBlock * DI; i += kIbThreads) {
+    const int s = s0 + i / DI;
+    if (s < n_kv) dk_idx[((int64_t)b * n_kv + s) * DI + (i % DI)] = sm.dk[i];
+  }
+}
+
+// dq_idx[row] = sum over the live slots of coef * k_idx[argmax]; DI / 8
+// threads per row, 8 values each.
+template <int DI>
+__global__ __launch_bounds__(256) void index_dq_gather(const float* __restrict__ coef,
+                                                       const int* __restrict__ amax,
+                                                       const uint16_t* __restrict__ k_idx,
+                                                       float* __restrict__ dq_idx, int64_t nrows, int n_q,
+                                                       int h_kv, int n_kv, int topk) {
+  constexpr int TPR = DI / 8;
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  if (row >= nrows) return;
+  const int dl = threadIdx.x % TPR;
+  const int b = (int)(row / ((int64_t)n_q * h_kv));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < topk; ++s) {
+    const float cf = coef[row * topk + s];
+    // Dead slots carry coef 0 and an unwritten argmax: clamp the address.
+    const int pos = amax[row * topk + s];
+    const int ps = min(max(pos, 0), n_kv - 1);
+    const u32x4 kv = ld16(k_idx + ((int64_t)b * n_kv + ps) * DI + dl * 8);
+    const float c = pos >= 0 ? cf : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(c, bf16_to_f32(kv[e] & 0xffffu), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(c, bf16_to_f32(kv[e] >> 16), acc[2 * e + 1]);
+    }
+  }
+  float* dst = dq_idx + row * DI + dl * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = acc[e];
+}
+
+template <int DI>
+hipError_t launch_index_bwd_t(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* blk,
+                              const float* bscore, const float* target, const float* dkl, float idx_scale,
+                              float* dq_idx, float* dk_idx, void* ws, hipStream_t stream) {
+  const PrefillWs L = prefill_ws_layout(d);
+  char* base = static_cast<char*>(ws);
+  const int* off = reinterpret_cast<const int*>(base + L.off);
+  const int* entries = reinterpret_cast<const int*>(base + L.entries);
+  float* coef = reinterpret_cast<float*>(base + L.part_ml);
+  int* amax = reinterpret_cast<int*>(base + L.part_o);
+  const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
+  if (nrows > 0) {
+    const int R = d.topk > 16 ? 32 : 16;
+    const int64_t wgs = (nrows * R + 255) / 256;
+    LaunchTimer timer("index_kl_coef", stream);
+    if (R == 16)
+      hipLaunchKernelGGL(index_kl_coef<16>, dim3((unsigned)wgs), dim3(256), 0, stream, blk, bscore, target, dkl,
+                         coef, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale);
+    else
+      hipLaunchKernelGGL(index_kl_coef<32>, dim3((unsigned)wgs), dim3(256), 0, stream, blk, bscore, target, dkl,
+                         coef, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale);
+  }
+  hipError_t e = launch_csr(d, blk, ws, stream);
+  if (e != hipSuccess) return e;
+  {
+    LaunchTimer timer("index_bwd_kv", stream);
+    hipLaunchKernelGGL(index_bwd_kv<DI>, dim3((unsigned)(d.batch * d.nblk())), dim3(kIbThreads), 0, stream, q_idx,
+                       k_idx, off, entries, coef, amax, dk_idx, d.batch, d.n_q, d.n_kv, d.pos0, d.h_kv, d.nblk(),
+                       d.topk);
+  }
+  if (nrows > 0) {
+    constexpr int TPR = DI / 8;
+    const int64_t wgs = (nrows + 256 / TPR - 1) / (256 / TPR);
+    LaunchTimer timer("index_dq_gather", stream);
+    hipLaunchKernelGGL(index_dq_gather<DI>, dim3((unsigned)wgs), dim3(256), 0, stream, coef, amax, k_idx, dq_idx,
+                       nrows, d.n_q, d.h_kv, d.n_kv, d.topk);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_backward(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* blk,
+                                 const float* bscore, const float* target, const float* dkl, float idx_scale,
+                                 float* dq_idx, float* dk_idx, void* ws, hipStream_t stream) {
+  if (d.d_idx == 128)
+    return launch_index_bwd_t<128>(d, q_idx, k_idx, blk, bscore, target, dkl, idx_scale, dq_idx, dk_idx, ws, stream);
+  return launch_index_bwd_t<64>(d, q_idx, k_idx, blk, bscore, target, dkl, idx_scale, dq_idx, dk_idx, ws, stream);
+}
+
+}  // namespace msa

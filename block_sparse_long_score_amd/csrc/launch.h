@@ -73,6 +73,10 @@ hipError_t launch_sparse_prefill_backward(const Dims& d, const uint16_t* q, cons
                                           const int32_t* blk, const uint16_t* out, const float* lse,
                                           const uint16_t* dout, float scale, uint16_t* dq, uint16_t* dk,
                                           uint16_t* dv, void* ws, hipStream_t stream);
+// Gradient of the KL alignment loss w.r.t. q_idx and k_idx (fp32 outputs).
+hipError_t launch_index_backward(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* blk,
+                                 const float* bscore, const float* target, const float* dkl, float idx_scale,
+                                 float* dq_idx, float* dk_idx, void* ws, hipStream_t stream);
 hipError_t launch_sparse_decode(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* ws,
                                 hipStream_t stream);

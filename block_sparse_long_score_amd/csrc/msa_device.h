@@ -89,6 +89,35 @@ __device__ __forceinline__ float colgroup_sum(float v) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Reductions over the R lanes of a row: DPP moves inside each row of 16 lanes
+// (swap neighbours, swap pairs, mirror within 8, mirror within 16; after each
+// step every lane holds the reduction of its group), then one cross-row swap
+// when R == 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+template <int R, typename Op>
+__device__ __forceinline__ float row_reduce(float v, Op op) {
+  v = op(v, dpp_f<0xb1>(v));                           // quad_perm [1,0,3,2]
+  v = op(v, dpp_f<0x4e>(v));                           // quad_perm [2,3,0,1]
+  v = op(v, dpp_f<0x141>(v));                          // row_half_mirror
+  v = op(v, dpp_f<0x140>(v));                          // row_mirror
+  if constexpr (R == 32) v = op(v, shfl_xor_f(v, 16));
+  return v;
+}
+
+// [row][d] tiles in LDS (rows of D bf16): 16-byte chunk c of row r sits at
+// c ^ row_swz(r), so 16 consecutive rows read at the same chunk hit 16
+// different bank groups.
+template <int D>
+__device__ __forceinline__ int row_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int rt_off(int r, int chunk) { return r * D + 8 * (chunk ^ row_swz<D>(r)); }
+
+
+
 // Number of set bits of `mask` in lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

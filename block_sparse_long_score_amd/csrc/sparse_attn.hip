@@ -493,25 +493,6 @@ hipError_t launch_merge_t(const Dims& d, const uint16_t* part_o, const float* pa
 // idx_scale * bscore over the same live slots, and kl = sum_s target_s
 // (ln target_s - ln index_s), 0 ln 0 = 0.  A slot is live when blk holds a
 // block in [0, jl]; dead slots get target 0 and take no part.
-// Reductions over the R lanes of a row: DPP moves inside each row of 16 lanes
-// (swap neighbours, swap pairs, mirror within 8, mirror within 16; after each
-// step every lane holds the reduction of its group), then one cross-row swap
-// when R == 32.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-
-template <int R, typename Op>
-__device__ __forceinline__ float row_reduce(float v, Op op) {
-  v = op(v, dpp_f<0xb1>(v));                           // quad_perm [1,0,3,2]
-  v = op(v, dpp_f<0x4e>(v));                           // quad_perm [2,3,0,1]
-  v = op(v, dpp_f<0x141>(v));                          // row_half_mirror
-  v = op(v, dpp_f<0x140>(v));                          // row_mirror
-  if constexpr (R == 32) v = op(v, shfl_xor_f(v, 16));
-  return v;
-}
-
 template <int G, int R>
 __global__ __launch_bounds__(256) void block_target_kl(const float* __restrict__ part_ml,
                                                        const int32_t* __restrict__ blk,

@@ -26,13 +26,6 @@ namespace {
 constexpr int kBwdThreads = 512;
 constexpr int kBwdCols = 32;                           // (entry x head) columns per group
 
-// [row][d] tiles (K/V rows of the block, q/dout rows of the columns): 16-byte
-// chunk c of row r sits at c ^ row_swz(r), so 16 rows read at the same chunk
-// hit 16 different bank groups.
-template <int D>
-__device__ __forceinline__ int row_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int rt_off(int r, int chunk) { return r * D + 8 * (chunk ^ row_swz<D>(r)); }
 // [d][column] tiles (q and dout transposed): units of 4 columns, unit u of row
 // d at u ^ ((d >> 2) & 7).
 __device__ __forceinline__ int tt_off(int d, int col) {

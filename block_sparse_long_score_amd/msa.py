@@ -51,6 +51,7 @@ EXPORTED = (
     "msa_prefill_chunked",
     "msa_sparse_prefill_target",
     "msa_sparse_prefill_backward",
+    "msa_index_backward",
 )
 
 
@@ -96,6 +97,7 @@ def lib() -> ctypes.CDLL:
     L.msa_block_topk.argtypes = [D, P, P, VP]
     L.msa_sparse_prefill.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
     L.msa_sparse_decode.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
+    L.msa_index_backward.argtypes = [D, P, P, P, P, P, P, F, P, P, P, S, VP]
     L.msa_sparse_prefill_backward.argtypes = [D, P, P, P, P, P, P, P, F, P, P, P, P, S, VP]
     L.msa_sparse_prefill_target.argtypes = [D, P, P, P, P, P, F, F, P, P, P, P, P, S, VP]
     L.msa_dense_gqa.argtypes = [D, P, P, P, F, P, P, P, S, VP]
@@ -241,6 +243,25 @@ def msa_sparse_prefill_backward(s: Shape, q, k, v, blk_idx, out, lse, dout, dq, 
                                            _ptr(lse), _ptr(dout), ctypes.c_float(scale), _ptr(dq), _ptr(dk),
                                            _ptr(dv), wp, wb, _stream(stream))
     _raise(st, "msa_sparse_prefill_backward")
+
+
+def msa_index_backward(s: Shape, q_idx, k_idx, blk_idx, bscore, target, dkl, dq_idx, dk_idx, workspace=None,
+                       idx_scale: float = 1.0, stream=None) -> None:
+    """Gradient of the KL alignment loss w.r.t. q_idx and k_idx (fp32)."""
+    _check(q_idx, "q_idx", torch.bfloat16, (s.batch, s.n_q, s.h_kv, s.d_idx))
+    _check(k_idx, "k_idx", torch.bfloat16, (s.batch, s.n_kv, s.d_idx))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, s.n_q, s.h_kv, s.topk))
+    _check(bscore, "bscore", torch.float32, (s.batch, s.n_q, s.h_kv, s.nblk))
+    _check(target, "target", torch.float32, (s.batch, s.n_q, s.h_kv, s.topk))
+    _check(dkl, "dkl", torch.float32, (s.batch, s.n_q, s.h_kv))
+    _check(dq_idx, "dq_idx", torch.float32, (s.batch, s.n_q, s.h_kv, s.d_idx))
+    _check(dk_idx, "dk_idx", torch.float32, (s.batch, s.n_kv, s.d_idx))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_index_backward(ctypes.byref(d), _ptr(q_idx), _ptr(k_idx), _ptr(blk_idx), _ptr(bscore),
+                                  _ptr(target), _ptr(dkl), ctypes.c_float(idx_scale), _ptr(dq_idx), _ptr(dk_idx),
+                                  wp, wb, _stream(stream))
+    _raise(st, "msa_index_backward")
 
 
 def msa_sparse_decode(s: Shape, q, k, v, blk_idx, out, lse=None, workspace=None, scale: float = 0.0,

@@ -189,6 +189,34 @@ msa_status msa_sparse_prefill_backward(const msa_dims* dims, const uint16_t* q, 
                                        uint16_t* dk, uint16_t* dv, void* workspace, size_t workspace_bytes,
                                        msa_stream stream);
 
+/* Index branch, backward: gradient of sum_rows dkl[row] * KL(target ||
+ * index distribution) with respect to q_idx and k_idx (Notion notes
+ * "Minimax-sparse-Attention": "KL Loss Alignment" trains the index branch to
+ * imitate the main branch's attention distribution; "Detached Gradients": the
+ * target is a constant and no gradient reaches the main branch).  With the
+ * selection fixed and, per (b, t, g) row and live slot s,
+ *   coef_s = dkl[row] * idx_scale * (softmax_s(idx_scale * bscore[j_s]) - target_s),
+ *   dq_idx[row] = sum_s coef_s k_idx[s*],   dk_idx[s*] += coef_s q_idx[row],
+ * where s* is the position of the largest causal token score in block j_s
+ * (the lowest position among equal maxima): the block max-pool passes its
+ * gradient to that token alone.  The argmax is taken on scores recomputed
+ * with the index scorer's arithmetic (bf16 products, fp32 sums).
+ *   q_idx, k_idx, blk_idx   as for msa_index_topk / msa_sparse_prefill_target;
+ *   bscore  [batch][n_q][h_kv][nblk] fp32 pooled index scores (read at the
+ *           live selected blocks);
+ *   target  [batch][n_q][h_kv][topk] fp32, msa_sparse_prefill_target's output;
+ *   dkl     [batch][n_q][h_kv] fp32, the loss gradient w.r.t. each row's KL;
+ *   idx_scale  as given to msa_sparse_prefill_target (finite);
+ *   dq_idx  [batch][n_q][h_kv][d_idx] fp32, output;
+ *   dk_idx  [batch][n_kv][d_idx] fp32, output, fully written (0 for keys that
+ *           are no row's argmax).
+ * Deterministic (every sum in a fixed order).  Workspace:
+ * msa_workspace_size(MSA_OP_SPARSE_PREFILL, dims). */
+msa_status msa_index_backward(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
+                              const int32_t* blk_idx, const float* bscore, const float* target, const float* dkl,
+                              float idx_scale, float* dq_idx, float* dk_idx, void* workspace, size_t workspace_bytes,
+                              msa_stream stream);
+
 /* Main branch, decode: msa_sparse_prefill with n_q == 1; each of the batch
  * sequences has its own cache of n_kv tokens and its query at p = pos0
  * (normally n_kv - 1).  Streams only the selected blocks (lefilia.fr: a fixed

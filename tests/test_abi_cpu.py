@@ -239,3 +239,23 @@ def test_backward_argument_checks():
     assert call(d0, q=None, blk=None, out=None, lse=None, dout=None, dq=None, wsb=0) == WS
     assert call(d0, dk=None) == NULL
     assert call(dims(batch=0), q=None, k=None, v=None, dk=None, dv=None, ws=None) == OK
+
+
+def test_index_backward_argument_checks():
+    lib = M.lib()
+    d = dims()
+    names = ("qi", "ki", "blk", "bscore", "target", "dkl", "dqi", "dki")
+
+    def call(dd, idx_scale=1.0, ws=FAKE, wsb=1 << 40, **kw):
+        p = {n: kw.get(n, FAKE) for n in names}
+        return lib.msa_index_backward(ctypes.byref(dd), p["qi"], p["ki"], p["blk"], p["bscore"], p["target"],
+                                      p["dkl"], ctypes.c_float(idx_scale), p["dqi"], p["dki"], ws, wsb, None)
+
+    for n in names:
+        assert call(d, **{n: None}) == NULL, n
+        assert call(d, **{n: ODD}) == ALIGN, n
+    assert call(d, idx_scale=float("nan")) == SHAPE
+    assert call(dims(d_idx=96)) == UNSUP
+    need = lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d))
+    assert call(d, wsb=need - 1) == WS
+    assert call(dims(batch=0), qi=None, ki=None, dki=None, ws=None) == OK

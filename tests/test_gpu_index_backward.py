@@ -1,0 +1,124 @@
+"""GPU parity of the index-branch backward (msa_index_backward) against the fp64
+oracle.
+
+The index inputs are integers in [-3, 3] (exact in bf16), so every token score
+is an exact integer in fp32 and the argmax positions (lowest position on ties)
+must agree bit for bit.  The coefficients come from an fp32 softmax of the
+pooled scores, and the gradients are fp32 sums of at most k * n_q terms:
+||err|| / ||ref|| <= 1e-5 per tensor, and |err| <= 1e-5 max |ref| + 1e-7 per
+element.  The target is the GPU's own msa_sparse_prefill_target output, fed
+to both sides (it is an input of the backward).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_score_amd import msa as M
+from block_sparse_long_score_amd.inputs import WORKLOADS, Shape, make_inputs
+from oracle import msa_oracle as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(s: Shape, cid: int, idx_scale: float):
+    inp = make_inputs(s, cid, device="cuda")
+    blk, bscore = U.run_index(s, inp["q_idx"], inp["k_idx"])
+    bscore = bscore.clone()
+    ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
+    out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
+    target = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.float32, device="cuda")
+    kl = torch.empty((s.batch, s.n_q, s.h_kv), dtype=torch.float32, device="cuda")
+    M.msa_sparse_prefill_target(s, inp["q"], inp["k"], inp["v"], blk, bscore, target, kl, out, None, ws,
+                                idx_scale=idx_scale)
+    g = torch.Generator().manual_seed(500 + cid)
+    dkl = (torch.rand((s.batch, s.n_q, s.h_kv), generator=g) + 0.5).cuda()
+    dqi = torch.full((s.batch, s.n_q, s.h_kv, s.d_idx), float("nan"), dtype=torch.float32, device="cuda")
+    dki = torch.full((s.batch, s.n_kv, s.d_idx), float("nan"), dtype=torch.float32, device="cuda")
+    M.msa_index_backward(s, inp["q_idx"], inp["k_idx"], blk, bscore, target, dkl, dqi, dki, ws, idx_scale=idx_scale)
+    dqi2 = torch.empty_like(dqi)
+    dki2 = torch.empty_like(dki)
+    M.msa_index_backward(s, inp["q_idx"], inp["k_idx"], blk, bscore, target, dkl, dqi2, dki2, ws,
+                         idx_scale=idx_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dqi, dqi2) and torch.equal(dki, dki2), "not deterministic"
+    rq, rk = O.index_kl_grad(U.to64(inp["q_idx"]), U.to64(inp["k_idx"]), blk.cpu().numpy(),
+                             target.cpu().numpy().astype(np.float64), idx_scale,
+                             dkl.cpu().numpy().astype(np.float64), s.pos0, s.block)
+    for got, ref, what in ((dqi, rq, "dq_idx"), (dki, rk, "dk_idx")):
+        got = got.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), what
+        err = np.abs(got - ref)
+        rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+        print(f"  {what}: rel L2 {rel:.2e}, max {err.max():.2e} (max |ref| {np.abs(ref).max():.2e})", flush=True)
+        assert rel <= 1e-5, what
+        assert np.all(err <= 1e-5 * np.abs(ref).max() + 1e-7), what
+
+
+CASES = {
+    "tiny_prefill_4k": (1, WORKLOADS["tiny_prefill_4k"][1], 1 / 8),
+    "chunk_ragged_g4": (11, Shape(1, 300, 1000, 700, 8, 2, 128, 128, topk=4), 0.1),
+    "batch2_g16_d64": (12, Shape(2, 257, 600, 343, 16, 1, 64, 64, topk=3), 0.05),
+    "g2_topk32_all_blocks": (14, Shape(1, 130, 2100, 1970, 16, 8, 64, 128, topk=32), 0.1),
+    "g8_chunk": (31, Shape(1, 700, 6000, 5300, 64, 8, 128, 128, topk=16), 1 / math.sqrt(128)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_index_backward_parity(name):
+    cid, s, idx_scale = CASES[name]
+    print(f"case {name}: {s}", flush=True)
+    run_case(s, cid, idx_scale)
+
+
+def test_index_backward_full_size_prefill_128k_sampled():
+    """The 131,072-token workload: dq_idx on sampled (token, group) rows and
+    dk_idx on every key of the second-to-last block (the sum over all rows that
+    selected it), each against the oracle run on those rows alone."""
+    from block_sparse_long_score_amd.inputs import sample_rows
+    cid, s = WORKLOADS["prefill_128k"]
+    idx_scale = 1 / math.sqrt(s.d_idx)
+    inp = make_inputs(s, cid, device="cuda")
+    blk, bscore = U.run_index(s, inp["q_idx"], inp["k_idx"])
+    bscore = bscore.clone()
+    ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
+    out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
+    target = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.float32, device="cuda")
+    kl = torch.empty((s.batch, s.n_q, s.h_kv), dtype=torch.float32, device="cuda")
+    M.msa_sparse_prefill_target(s, inp["q"], inp["k"], inp["v"], blk, bscore, target, kl, out, None, ws,
+                                idx_scale=idx_scale)
+    dkl = torch.full((s.batch, s.n_q, s.h_kv), 0.75, dtype=torch.float32, device="cuda")
+    dqi = torch.empty((s.batch, s.n_q, s.h_kv, s.d_idx), dtype=torch.float32, device="cuda")
+    dki = torch.empty((s.batch, s.n_kv, s.d_idx), dtype=torch.float32, device="cuda")
+    M.msa_index_backward(s, inp["q_idx"], inp["k_idx"], blk, bscore, target, dkl, dqi, dki, ws, idx_scale=idx_scale)
+    torch.cuda.synchronize()
+    print("  gpu done", flush=True)
+    kseq = U.to64(inp["k_idx"][:1])
+    blk_np, tg, dk_np = blk.cpu().numpy(), target.cpu().numpy().astype(np.float64), dkl.cpu().numpy()
+    dq_np = dqi.cpu().numpy()
+
+    def row_grad(t, g):
+        return O.index_kl_grad(U.to64(inp["q_idx"][:1, t:t + 1, g:g + 1]), kseq, blk_np[:1, t:t + 1, g:g + 1],
+                               tg[:1, t:t + 1, g:g + 1], idx_scale, dk_np[:1, t:t + 1, g:g + 1].astype(np.float64),
+                               t, s.block)
+
+    for t in sample_rows(s.n_q, 4, 1000 * cid + 66, [s.n_q - 1]):
+        for g in range(s.h_kv):
+            rq, _ = row_grad(t, g)
+            err = np.abs(dq_np[0, t, g] - rq[0, 0, 0])
+            assert np.all(err <= 1e-5 * np.abs(rq).max() + 1e-7), f"dq_idx t={t} g={g}"
+    j = s.nblk - 2
+    ref = np.zeros((s.block, s.d_idx))
+    rows = [(t, g) for t in range(j * s.block, s.n_q) for g in range(s.h_kv) if j in blk_np[0, t, g]]
+    rows += [(t, g) for t in range(0, j * s.block) for g in range(s.h_kv) if j in blk_np[0, t, g]]
+    print(f"  block {j}: {len(rows)} rows", flush=True)
+    for t, g in rows:
+        _, rk = row_grad(t, g)
+        ref += rk[0, j * s.block:(j + 1) * s.block]
+    got = dki[0, j * s.block:(j + 1) * s.block].cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    print(f"  dk_idx block {j}: rel L2 {rel:.2e}", flush=True)
+    assert rel <= 1e-5 and np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref).max() + 1e-7)

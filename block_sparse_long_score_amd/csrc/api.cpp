@@ -218,6 +218,7 @@ msa_status msa_index_backward(const msa_dims* dims, const uint16_t* q_idx, const
                               msa_stream stream) {
   msa_status st = check_dims(dims, kNeedDIdx | kCsr);
   if (st != MSA_OK) return st;
+  if (dims->h_kv > 128) return MSA_ERR_UNSUPPORTED;
   if (!std::isfinite(idx_scale)) return MSA_ERR_SHAPE;
   if (dims->batch == 0) return MSA_OK;
   if (!k_idx || !dk_idx) return MSA_ERR_NULL;

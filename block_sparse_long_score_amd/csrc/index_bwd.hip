@@ -65,29 +65,45 @@ __global__ __launch_bounds__(256) void index_kl_coef(const int32_t* __restrict__
   if (row < nrows && s < topk) coef[row * topk + s] = c;
 }
 
+constexpr int kIbMaxLists = 128;                       // h_kv <= 128
+
 template <int DI>
 struct IbLds {
   float dk[kBlock * DI];                               // dk_idx of the block's keys
   union {
     uint16_t k[kBlock * DI];                           // the block's index keys, while loaded
     struct {
-      uint16_t qr[kIbCols * DI];                       // [entry][d] index queries
-      float coef[kIbCols];
+      // q rows and coefficients by group parity: the dk phase of one group
+      // reads them while faster waves already stage the next group.
+      uint16_t qr[2][kIbCols * DI];                    // [entry][d] index queries
+      float coef[2][kIbCols];
       int plim[kIbCols];                               // last visible position, -1 for an empty column
-      int slot_row[kIbCols];                           // (b * n_q + t) * h_kv + g) * topk + slot, -1 if empty
+      int slot_row[kIbCols];                           // ((b * n_q + t) * h_kv + g) * topk + slot, -1 if empty
       float wmax[8][kIbCols];
       int wkey[8][kIbCols];
       int amax[kIbCols];                               // argmax key in the block, -1 if empty
     } g;
   };
+  int lstart[kIbMaxLists + 1];                         // flat column where group g's list starts
+  int lbase[kIbMaxLists];                              // its first entry
+};
+
+// One column group in flight: this thread's 16-byte chunk of its column's
+// index query, the column's coefficient, last visible position and slot row,
+// and the entry (value and group) that this buffer loads next.
+struct IbStage {
+  u32x4 q;
+  float coef;
+  int plim, srow, en_next, g_next;
 };
 
 template <int DI>
 __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const int* __restrict__ off,
-    const int* __restrict__ entries, const float* __restrict__ coef, int* __restrict__ amax_out,
+    const int* __restrict__ entries, const float* __restrict__ coef, int* __restrict__ amax_out, int sink,
     float* __restrict__ dk_idx, int batch, int n_q, int n_kv, int pos0, int h_kv, int nblk, int topk) {
   constexpr int DC = DI / 8;
+  constexpr int NST = kIbCols * DC;                    // staging threads (one chunk each)
   __shared__ IbLds<DI> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m16 = lane & 15, q4 = lane >> 4;
@@ -100,6 +116,16 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
     const int key = it / DC, ch = it % DC, s = s0 + key;
     st16(&sm.k[rt_off<DI>(key, ch)], s < n_kv ? ld16(kb + (int64_t)s * DI + ch * 8) : u32x4{0u, 0u, 0u, 0u});
   }
+  if (tid == 0) {                                      // the block's lists of all groups, back to back
+    int run = 0;
+    for (int g = 0; g < h_kv; ++g) {
+      const int list = (b * h_kv + g) * nblk + j;
+      sm.lstart[g] = run;
+      sm.lbase[g] = off[list];
+      run += off[list + 1] - off[list];
+    }
+    sm.lstart[h_kv] = run;
+  }
   __syncthreads();
   // B operands of S^T: column (MFMA n) = this lane's key, contraction slots
   // 8*q4 + i = d 32*c + 8*q4 + i.
@@ -107,38 +133,65 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
   u32x4 kop[DI / 32];
 #pragma unroll
   for (int c = 0; c < DI / 32; ++c) kop[c] = ld16(&sm.k[rt_off<DI>(mykey, 4 * c + q4)]);
+  const int ncols = sm.lstart[h_kv];
   __syncthreads();                                     // the LDS now holds entry groups
   const int skey = s0 + mykey;
+  const int ngroups = (ncols + kIbCols - 1) / kIbCols;
 
-  for (int g = 0; g < h_kv; ++g) {
-    const int list = (b * h_kv + g) * nblk + j;
-    const int e0 = off[list], e1 = off[list + 1];
-    for (int c0 = e0; c0 < e1; c0 += kIbCols) {
-      // Stage the entries' index queries and per-column values.
-      for (int it = tid; it < kIbCols * DC; it += kIbThreads) {
-        const int col = it / DC, ch = it % DC, e = c0 + col;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (e < e1) {
-          const int t = entries[e] >> 5;
-          val = ld16(q_idx + (((int64_t)b * n_q + t) * h_kv + g) * DI + ch * 8);
-        }
-        st16(&sm.g.qr[rt_off<DI>(col, ch)], val);
+  if (ngroups > 0) {
+    // Staging role: column scol of each group, chunk sch of its query.
+    // Threads beyond NST (d_idx = 64) mirror the first NST.
+    const int st_id = tid % NST, scol = st_id / DC, sch = st_id % DC;
+    // Flat column f -> (entry value, group); f is clamped to a real column,
+    // so no load of the loop sits behind a branch.
+    auto entry_at = [&](int grp, int& gout) {
+      const int f = min(grp * kIbCols + scol, ncols - 1);
+      int lo = 0, hi = h_kv;                           // largest g with lstart[g] <= f
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sm.lstart[mid] <= f) lo = mid;
+        else hi = mid;
       }
-      if (tid < kIbCols) {
-        const int e = c0 + tid;
-        int pl = -1, sr = -1;
-        float cf = 0.f;
-        if (e < e1) {
-          const int en = entries[e], t = en >> 5;
-          sr = (int)((((int64_t)b * n_q + t) * h_kv + g) * topk + (en & 31));
-          pl = pos0 + t;
-          cf = coef[sr];
-        }
-        sm.g.plim[tid] = pl;
-        sm.g.slot_row[tid] = sr;
-        sm.g.coef[tid] = cf;
-      }
+      gout = lo;
+      return entries[sm.lbase[lo] + f - sm.lstart[lo]];
+    };
+    auto fetch = [&](IbStage& st, int grp, int en, int gc) {
+      const int t = en >> 5;
+      const bool live = grp * kIbCols + scol < ncols;
+      const int64_t qrow = ((int64_t)b * n_q + t) * h_kv + gc;
+      const int sr = (int)(qrow * topk + (en & 31));
+      st.q = ld16(q_idx + qrow * DI + sch * 8);
+      st.coef = coef[sr];
+      st.plim = live ? pos0 + t : -1;
+      st.srow = live ? sr : -1;
+    };
+    IbStage sx, sy;
+    {
+      int g0, g1, g2, g3;
+      const int en0 = entry_at(0, g0), en1 = entry_at(1, g1);
+      fetch(sx, 0, en0, g0);
+      fetch(sy, 1, en1, g1);
+      sx.en_next = entry_at(2, g2);
+      sx.g_next = g2;
+      sy.en_next = entry_at(3, g3);
+      sy.g_next = g3;
+    }
+    const auto fmax = [](float x, float y) { return vmax(x, y); };
+    auto step = [&](IbStage& st, int grp) {
+      const int par = grp & 1;
+      // Every thread of a column writes the same per-column values.
+      st16(&sm.g.qr[par][rt_off<DI>(scol, sch)], st.q);
+      sm.g.coef[par][scol] = st.coef;
+      sm.g.plim[scol] = st.plim;
+      sm.g.slot_row[scol] = st.srow;
       __syncthreads();
+      {
+        const int en = st.en_next, gn = st.g_next;
+        fetch(st, grp + 2, en, gn);
+        int g4;
+        st.en_next = entry_at(grp + 4, g4);
+        st.g_next = g4;
+      }
       // S^T for this wave's 16 keys: lane holds column 16*ct + 4*q4 + r.
       f32x4 sacc[2];
 #pragma unroll
@@ -146,10 +199,9 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
         sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < DI / 32; ++c)
-          sacc[ct] = mfma_16x16x32(ld16(&sm.g.qr[rt_off<DI>(16 * ct + m16, 4 * c + q4)]), kop[c], sacc[ct]);
+          sacc[ct] = mfma_16x16x32(ld16(&sm.g.qr[par][rt_off<DI>(16 * ct + m16, 4 * c + q4)]), kop[c], sacc[ct]);
       }
       // Per column: the wave's max over its keys and the lowest key that has it.
-      const auto fmax = [](float x, float y) { return vmax(x, y); };
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -165,38 +217,50 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
         }
       __syncthreads();
       // Across waves (ascending key ranges): the first wave that reaches the
-      // column's maximum holds its lowest argmax.
-      if (tid < kIbCols) {
+      // column's maximum holds its lowest argmax.  Wave 0 publishes it; its
+      // upper half stores to the sink slot.
+      if (w == 0) {
+        const int col = lane & 31;
         float best = -INFINITY;
         int key = -1;
 #pragma unroll
         for (int ww = 0; ww < 8; ++ww) {
-          const float m = sm.g.wmax[ww][tid];
-          if (m > best) {
-            best = m;
-            key = sm.g.wkey[ww][tid];
-          }
+          const float m = sm.g.wmax[ww][col];
+          key = m > best ? sm.g.wkey[ww][col] : key;
+          best = vmax(best, m);
         }
-        const int sr = sm.g.slot_row[tid];
-        if (sr < 0) key = -1;
-        sm.g.amax[tid] = key;
-        if (sr >= 0) amax_out[sr] = key < 0 ? -1 : s0 + key;
+        const int sr = sm.g.slot_row[col];
+        key = sr < 0 ? -1 : key;
+        sm.g.amax[col] = key;
+        amax_out[(lane < 32 && sr >= 0) ? sr : sink] = key < 0 ? -1 : s0 + key;
       }
       __syncthreads();
-      // dk_idx rows of this wave's keys, columns in list order.
-      for (int col = 0; col < kIbCols; ++col) {
-        const int key = sm.g.amax[col];
-        if ((key >> 4) != w) continue;                 // wave-uniform
-        const float cf = sm.g.coef[col];
-        for (int d = lane; d < DI; d += 64) {
-          const int ch = d >> 3;
-          const float qv = bf16_to_f32(sm.g.qr[rt_off<DI>(col, ch) + (d & 7)]);
-          sm.dk[key * DI + d] = fmaf(cf, qv, sm.dk[key * DI + d]);
+      // dk_idx rows of this wave's keys, columns in list order: a ballot over
+      // the 32 argmax keys picks this wave's columns.
+      {
+        const int mine = sm.g.amax[lane & 31];
+        uint64_t hits = ballot(lane < kIbCols && (mine >> 4) == w);
+        while (hits) {
+          const int col = __builtin_ctzll(hits);
+          hits &= hits - 1;
+          const int key = __builtin_amdgcn_readfirstlane(sm.g.amax[col]);
+          const float cf = sm.g.coef[par][col];
+#pragma unroll
+          for (int d0 = 0; d0 < DI; d0 += 64) {
+            const int d = d0 + lane;
+            const float qv = bf16_to_f32(sm.g.qr[par][rt_off<DI>(col, d >> 3) + (d & 7)]);
+            sm.dk[key * DI + d] = fmaf(cf, qv, sm.dk[key * DI + d]);
+          }
         }
       }
-      __syncthreads();                                 // before the next group is staged
+    };
+    __builtin_amdgcn_s_waitcnt(0);                     // drain the prologue (exact waits in the loop)
+    for (int grp = 0; grp < ngroups; grp += 2) {
+      step(sx, grp);
+      step(sy, grp + 1);
     }
   }
+  __syncthreads();
   for (int i = tid; i < kBlock * DI; i += kIbThreads) {
     const int s = s0 + i / DI;
     if (s < n_kv) dk_idx[((int64_t)b * n_kv + s) * DI + (i % DI)] = sm.dk[i];
@@ -262,8 +326,8 @@ hipError_t launch_index_bwd_t(const Dims& d, const uint16_t* q_idx, const uint16
   {
     LaunchTimer timer("index_bwd_kv", stream);
     hipLaunchKernelGGL(index_bwd_kv<DI>, dim3((unsigned)(d.batch * d.nblk())), dim3(kIbThreads), 0, stream, q_idx,
-                       k_idx, off, entries, coef, amax, dk_idx, d.batch, d.n_q, d.n_kv, d.pos0, d.h_kv, d.nblk(),
-                       d.topk);
+                       k_idx, off, entries, coef, amax, (int)(nrows * d.topk), dk_idx, d.batch, d.n_q, d.n_kv,
+                       d.pos0, d.h_kv, d.nblk(), d.topk);
   }
   if (nrows > 0) {
     constexpr int TPR = DI / 8;

@@ -210,7 +210,8 @@ msa_status msa_sparse_prefill_backward(const msa_dims* dims, const uint16_t* q, 
  *   dq_idx  [batch][n_q][h_kv][d_idx] fp32, output;
  *   dk_idx  [batch][n_kv][d_idx] fp32, output, fully written (0 for keys that
  *           are no row's argmax).
- * Deterministic (every sum in a fixed order).  Workspace:
+ * Deterministic (every sum in a fixed order).  h_kv <= 128
+ * (MSA_ERR_UNSUPPORTED otherwise).  Workspace:
  * msa_workspace_size(MSA_OP_SPARSE_PREFILL, dims). */
 msa_status msa_index_backward(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
                               const int32_t* blk_idx, const float* bscore, const float* target, const float* dkl,

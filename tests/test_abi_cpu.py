@@ -256,6 +256,7 @@ def test_index_backward_argument_checks():
         assert call(d, **{n: ODD}) == ALIGN, n
     assert call(d, idx_scale=float("nan")) == SHAPE
     assert call(dims(d_idx=96)) == UNSUP
+    assert call(dims(h_q=256, h_kv=256)) == UNSUP
     need = lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d))
     assert call(d, wsb=need - 1) == WS
     assert call(dims(batch=0), qi=None, ki=None, dki=None, ws=None) == OK

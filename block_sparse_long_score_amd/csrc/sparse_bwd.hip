@@ -28,8 +28,12 @@ constexpr int kBwdCols = 32;                           // (entry x head) columns
 
 // [d][column] tiles (q and dout transposed): units of 4 columns, unit u of row
 // d at u ^ ((d >> 2) & 7).
+// Rows are padded to kTtStride elements and the unit is XOR'd with (d >> 3) & 7:
+// the dk / dv operand reads (16 rows x 4 units per wave) then hit every bank
+// pair once, and the staging writes (8-byte words of 4 columns) at most twice.
+constexpr int kTtStride = 40;
 __device__ __forceinline__ int tt_off(int d, int col) {
-  return d * kBwdCols + 4 * (((col >> 2) ^ (d >> 2)) & 7) + (col & 3);
+  return d * kTtStride + 4 * (((col >> 2) ^ (d >> 3)) & 7) + (col & 3);
 }
 // dS tile [column][key]: 8-key chunk c of row col at c ^ (col & 15).
 __device__ __forceinline__ int ds_off(int col, int key) {
@@ -45,7 +49,7 @@ struct BwdLds {
     } kv;                                              // the block, while its operands are loaded
     struct {
       uint16_t qr[kBwdCols * D], dor[kBwdCols * D];    // [column][d]
-      uint16_t qt[D * kBwdCols], dot[D * kBwdCols];    // [d][column]
+      uint16_t qt[D * kTtStride], dot[D * kTtStride];  // [d][column], padded rows
       uint16_t ds[kBwdCols * kBlock];                  // [column][key]
       float lse2[kBwdCols], dcol[kBwdCols];
       int plim[kBwdCols];                              // last visible key position, -1 for an empty column
@@ -80,15 +84,16 @@ __global__ __launch_bounds__(256) void bwd_row_dot(const uint16_t* __restrict__ 
   if (row < nrows && dl == 0) dcol[row] = sum;
 }
 
-// Registers of one column group in flight: this thread's 16-byte chunk of its
-// column's q and dout rows, the column's lse (log2 units), D and last visible
-// position, and the entry of the group that this buffer loads next (two groups
-// later).
+// Registers of the next column group: this thread's staging tile (4 columns x
+// one 16-byte chunk of q or dout), the values of its meta column (tid & 31),
+// and the entries of the group after it (the 4 staging columns and the meta
+// column).
 struct BwdStage {
-  u32x4 q, dout;
+  u32x4 v[4];
   int64_t prow;
   float lse2, dcol;
-  int plim, en_next;
+  int plim;
+  int en[4], men;
 };
 
 template <int D, int LOG2G>
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
   constexpr int DC = D / 8;                            // 16-byte chunks per row
   constexpr int DT = D / 16;                           // 16-wide d tiles
   constexpr int CTW = D / 64;                          // column tiles of dq per wave
-  constexpr int NST = kBwdCols * DC;                   // staging threads (one q and one dout chunk each)
+  constexpr int NST = 2 * 8 * DC;                      // staging threads: 4-column tiles of q and dout
   __shared__ BwdLds<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m16 = lane & 15, q4 = lane >> 4;
@@ -162,62 +167,80 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
   const int ngroups = (ncols + kBwdCols - 1) / kBwdCols;
   if (ngroups > 0) {
     const int skey = s0 + mykey;
-    // Staging role: column scol of each group, chunk sch of its rows.  Threads
-    // beyond NST (d = 64) mirror the first NST and write the same values.
-    const int st_id = tid % NST, scol = st_id / DC, sch = st_id % DC;
+    // Staging role: tensor `which` (q or dout), columns 4*scg .. 4*scg + 3,
+    // chunk sch.  Threads beyond NST mirror the first NST and write nothing;
+    // every thread also carries the meta values of column tid & 31.
+    const int st_id = tid % NST, which = st_id / (8 * DC), scg = (st_id % (8 * DC)) / DC, sch = st_id % DC;
+    const int mcol = tid & 31;
+    const uint16_t* src = which ? dout : q;
     // Every load of the loop reads a real row (the column index is clamped), so
     // the loop body has no memory operation behind a branch and the compiler's
     // wait counts stay exact across iterations; columns past the list end are
     // masked through plim = -1 and their dq goes to the sink row.
-    auto entry_at = [&](int grp) {
-      const int gc = min(grp * kBwdCols + scol, ncols - 1);
+    auto entry_at = [&](int grp, int col) {
+      const int gc = min(grp * kBwdCols + col, ncols - 1);
       return entries[e0 + (gc >> LOG2G)];
     };
-    auto fetch = [&](BwdStage& st, int grp, int en) {
-      const int gc = grp * kBwdCols + scol;
+    auto fetch = [&](BwdStage& st, int grp) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int gc = min(grp * kBwdCols + 4 * scg + kk, ncols - 1);
+        const int64_t row = ((int64_t)b * n_q + (st.en[kk] >> 5)) * h_q + g * G + (gc & (G - 1));
+        st.v[kk] = ld16(src + row * D + sch * 8);
+      }
+      const int gc = grp * kBwdCols + mcol;
       const int hh = min(gc, ncols - 1) & (G - 1);
-      const int t = en >> 5;
+      const int t = st.men >> 5;
       const int64_t row = ((int64_t)b * n_q + t) * h_q + g * G + hh;
-      st.q = ld16(q + row * D + sch * 8);
-      st.dout = ld16(dout + row * D + sch * 8);
       st.lse2 = lse[row] * kLog2e;
       st.dcol = dcol[row];
       // Selects by mask, not a ternary: a branch here would make the
       // compiler's wait counts at the loop head conservative.
       const int64_t live = -(int64_t)(gc < ncols);
-      const int64_t pr = ((((int64_t)b * n_q + t) * h_kv + g) * topk + (en & 31)) * G + hh;
+      const int64_t pr = ((((int64_t)b * n_q + t) * h_kv + g) * topk + (st.men & 31)) * G + hh;
       st.plim = (int)(((int64_t)(pos0 + t) & live) | (-1 & ~live));
       st.prow = (pr & live) | (sink_row & ~live);
     };
-    BwdStage sx, sy;
-    {
-      const int en0 = entry_at(0), en1 = entry_at(1);
-      fetch(sx, 0, en0);
-      fetch(sy, 1, en1);
-      sx.en_next = entry_at(2);
-      sy.en_next = entry_at(3);
-    }
-    auto step = [&](BwdStage& st, int grp) {
-      // No branch here: every thread of a column writes the same meta values.
-      st16(&sm.g.qr[rt_off<D>(scol, sch)], st.q);
-      st16(&sm.g.dor[rt_off<D>(scol, sch)], st.dout);
+    auto load_entries = [&](BwdStage& st, int grp) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) st.en[kk] = entry_at(grp, 4 * scg + kk);
+      st.men = entry_at(grp, mcol);
+    };
+    BwdStage st;
+    load_entries(st, 0);
+    fetch(st, 0);
+    load_entries(st, 1);
+    // Drain the prologue's loads: the wait counts at the loop head are the
+    // merge of the entry and back-edge states, and an empty entry state keeps
+    // them those of the loop itself.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int grp = 0; grp < ngroups; ++grp) {
+      // Transpose the staging tile in registers (4 columns per 8-byte word),
+      // outside the writer branch so the waits for the loads stay outside too.
+      u32x2 tw[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        sm.g.qt[tt_off(8 * sch + e, scol)] = (uint16_t)(st.q[e >> 1] >> (16 * (e & 1)));
-        sm.g.dot[tt_off(8 * sch + e, scol)] = (uint16_t)(st.dout[e >> 1] >> (16 * (e & 1)));
+        const int wd = e >> 1, sh = 16 * (e & 1);
+        tw[e][0] = ((st.v[0][wd] >> sh) & 0xffffu) | (((st.v[1][wd] >> sh) & 0xffffu) << 16);
+        tw[e][1] = ((st.v[2][wd] >> sh) & 0xffffu) | (((st.v[3][wd] >> sh) & 0xffffu) << 16);
       }
-      sm.g.plim[scol] = st.plim;
-      sm.g.lse2[scol] = st.lse2;
-      sm.g.dcol[scol] = st.dcol;
-      sm.g.prow[grp & 1][scol] = st.prow;
+      if (tid < NST) {                                 // wave-uniform
+        uint16_t* rt = which ? sm.g.dor : sm.g.qr;
+        uint16_t* tt = which ? sm.g.dot : sm.g.qt;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) st16(&rt[rt_off<D>(4 * scg + kk, sch)], st.v[kk]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x2*>(&tt[tt_off(8 * sch + e, 4 * scg)]) = tw[e];
+      }
+      // Every thread of a meta column writes the same values.
+      sm.g.plim[mcol] = st.plim;
+      sm.g.lse2[mcol] = st.lse2;
+      sm.g.dcol[mcol] = st.dcol;
+      sm.g.prow[grp & 1][mcol] = st.prow;
       __syncthreads();
-      // Refill this buffer with the group two ahead, and its entry with the
-      // group four ahead.
-      {
-        const int en = st.en_next;
-        fetch(st, grp + 2, en);
-        st.en_next = entry_at(grp + 4);
-      }
+      // The next group's rows, and the entries of the group after it.
+      fetch(st, grp + 1);
+      load_entries(st, grp + 2);
       // S^T and dP^T for this wave's 16 keys and the 32 columns: lane holds
       // column 16*ct + 4*q4 + r, key mykey.
       f32x4 sacc[2], dpacc[2];
@@ -280,16 +303,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
         o[1] = pack_bf16x2(acc[2] * scale, acc[3] * scale);
         *reinterpret_cast<u32x2*>(part_dq + prow * D + 16 * dtw + 4 * q4) = o;
       }
-    };
-    // Drain the prologue's loads: the wait counts at the loop head are the
-    // merge of the entry and back-edge states, and an empty entry state keeps
-    // them those of the loop itself (which waits only for the buffer in use).
-    __builtin_amdgcn_s_waitcnt(0);
-    // Groups go in pairs so that each buffer's role is fixed in the code; an
-    // odd last group is followed by one fully masked group.
-    for (int grp = 0; grp < ngroups; grp += 2) {
-      step(sx, grp);
-      step(sy, grp + 1);
     }
   }
   // Rows 16*w + 4*q4 + r, d 16*dt + m16.

@@ -32,7 +32,7 @@ msa_status check_dims(const msa_dims* p, unsigned need) {
   if (d.h_q % d.h_kv != 0) return MSA_ERR_SHAPE;
   if ((int64_t)d.pos0 + d.n_q > d.n_kv) return MSA_ERR_SHAPE;
   if ((need & kDecode) && d.n_q != 1) return MSA_ERR_SHAPE;
-  if (d.block != 128 || d.topk > 32) return MSA_ERR_UNSUPPORTED;
+  if (d.block != 128 || d.topk > 64) return MSA_ERR_UNSUPPORTED;
   const int g = d.h_q / d.h_kv;
   if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return MSA_ERR_UNSUPPORTED;
   if ((need & kNeedD) && d.d != 64 && d.d != 128) return MSA_ERR_UNSUPPORTED;

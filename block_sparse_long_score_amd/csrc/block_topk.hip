@@ -197,11 +197,11 @@ __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __re
                                                                const int* __restrict__ seq_len) {
   __shared__ uint32_t ck[kWgWaves][64];
   __shared__ int32_t ci[kWgWaves][64];
-  __shared__ uint32_t cand_k[kWgWaves][32];
-  __shared__ int32_t cand_i[kWgWaves][32];
+  __shared__ uint32_t cand_k[kWgWaves][64];
+  __shared__ int32_t cand_i[kWgWaves][64];
   __shared__ int cand_n[kWgWaves];
-  __shared__ uint32_t cat_k[kWgWaves * 32];
-  __shared__ int32_t cat_i[kWgWaves * 32];
+  __shared__ uint32_t cat_k[kWgWaves * 64];
+  __shared__ int32_t cat_i[kWgWaves * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = blockIdx.x;
   const int64_t bt = row / h_kv;
@@ -251,13 +251,14 @@ __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __re
   }
   __syncthreads();
   if (wave != 0) return;
-  uint32_t key[2];
+  // At most kWgWaves * (topk - 1) <= 4 * 63 candidates.
+  uint32_t key[kWgWaves];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kWgWaves; ++i) {
     const int c = i * 64 + lane;
     key[i] = c < total ? cat_k[c] : 0u;
   }
-  wave_select<2>(key, kk, ck[0], ci[0], [&](int pos, uint32_t, int c) { out[pos] = cat_i[c]; });
+  wave_select<kWgWaves>(key, kk, ck[0], ci[0], [&](int pos, uint32_t, int c) { out[pos] = cat_i[c]; });
 }
 
 template <int V>

@@ -156,10 +156,10 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
       return entries[sm.lbase[lo] + f - sm.lstart[lo]];
     };
     auto fetch = [&](IbStage& st, int grp, int en, int gc) {
-      const int t = en >> 5;
+      const int t = entry_token(en);
       const bool live = grp * kIbCols + scol < ncols;
       const int64_t qrow = ((int64_t)b * n_q + t) * h_kv + gc;
-      const int sr = (int)(qrow * topk + (en & 31));
+      const int sr = (int)(qrow * topk + entry_slot(en));
       st.q = ld16(q_idx + qrow * DI + sch * 8);
       st.coef = coef[sr];
       st.plim = live ? pos0 + t : -1;
@@ -311,14 +311,17 @@ hipError_t launch_index_bwd_t(const Dims& d, const uint16_t* q_idx, const uint16
   int* amax = reinterpret_cast<int*>(base + L.part_o);
   const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
   if (nrows > 0) {
-    const int R = d.topk > 16 ? 32 : 16;
+    const int R = d.topk > 32 ? 64 : d.topk > 16 ? 32 : 16;
     const int64_t wgs = (nrows * R + 255) / 256;
     LaunchTimer timer("index_kl_coef", stream);
     if (R == 16)
       hipLaunchKernelGGL(index_kl_coef<16>, dim3((unsigned)wgs), dim3(256), 0, stream, blk, bscore, target, dkl,
                          coef, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale);
-    else
+    else if (R == 32)
       hipLaunchKernelGGL(index_kl_coef<32>, dim3((unsigned)wgs), dim3(256), 0, stream, blk, bscore, target, dkl,
+                         coef, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale);
+    else
+      hipLaunchKernelGGL(index_kl_coef<64>, dim3((unsigned)wgs), dim3(256), 0, stream, blk, bscore, target, dkl,
                          coef, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale);
   }
   hipError_t e = launch_csr(d, blk, ws, stream);

@@ -30,6 +30,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBlock = 128;   // KV block size B (tokens); the only size supported
 
+// A CSR entry packs (query token t, selection slot): t << kSlotBits | slot.
+constexpr int kSlotBits = 6;  // topk <= 64
+__device__ __forceinline__ int entry_token(int en) { return en >> kSlotBits; }
+__device__ __forceinline__ int entry_slot(int en) { return en & ((1 << kSlotBits) - 1); }
+
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -92,7 +97,7 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 // Reductions over the R lanes of a row: DPP moves inside each row of 16 lanes
 // (swap neighbours, swap pairs, mirror within 8, mirror within 16; after each
 // step every lane holds the reduction of its group), then one cross-row swap
-// when R == 32.
+// when R >= 32 (and a second one when R == 64).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
@@ -104,7 +109,8 @@ __device__ __forceinline__ float row_reduce(float v, Op op) {
   v = op(v, dpp_f<0x4e>(v));                           // quad_perm [2,3,0,1]
   v = op(v, dpp_f<0x141>(v));                          // row_half_mirror
   v = op(v, dpp_f<0x140>(v));                          // row_mirror
-  if constexpr (R == 32) v = op(v, shfl_xor_f(v, 16));
+  if constexpr (R >= 32) v = op(v, shfl_xor_f(v, 16));
+  if constexpr (R == 64) v = op(v, shfl_xor_f(v, 32));
   return v;
 }
 

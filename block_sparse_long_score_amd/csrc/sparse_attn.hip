@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kFillThreads) void csr_fill_chunks(const int32_t* _
       }
       if (j >= 0) {
         const int pos = cur[j] + rank;
-        entries[pos] = ((tb + tl) << 5) | slot;        // slot < 32, t < 2^26
+        entries[pos] = ((tb + tl) << kSlotBits) | slot;   // slot < 64, t < 2^25
       }
       __builtin_amdgcn_wave_barrier();
       if (j >= 0 && last) cur[j] += rank + 1;          // after every lane has read its cursor
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void sparse_kv_outer(
       for (int ct = 0; ct < 2; ++ct) {
         const bool valid = entry_of(cg, ct) < eb;
         const int hh = (cg * 32 + ct * 16 + (lane & 15)) & (G - 1);
-        const int t = en[ct] >> 5, slot = en[ct] & 31;
+        const int t = entry_token(en[ct]), slot = entry_slot(en[ct]);
         const int p = pos0 + t;
         c.qrow[ct] = q + (((int64_t)b * n_q + t) * h_q + g * G + hh) * D;
         c.plim[ct] = valid ? p : INT_MAX;
@@ -553,14 +553,17 @@ template <int G>
 hipError_t launch_target_t(const Dims& d, const float* part_ml, const int32_t* blk, const float* bscore,
                            float idx_scale, float* target, float* kl, hipStream_t stream) {
   const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
-  const int R = d.topk > 16 ? 32 : 16;
+  const int R = d.topk > 32 ? 64 : d.topk > 16 ? 32 : 16;
   const int64_t wgs = (nrows * R + 255) / 256;
   LaunchTimer timer("block_target_kl", stream);
   if (R == 16)
     hipLaunchKernelGGL((block_target_kl<G, 16>), dim3((unsigned)wgs), dim3(256), 0, stream, part_ml, blk, bscore,
                        target, kl, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale * kLog2e);
-  else
+  else if (R == 32)
     hipLaunchKernelGGL((block_target_kl<G, 32>), dim3((unsigned)wgs), dim3(256), 0, stream, part_ml, blk, bscore,
+                       target, kl, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale * kLog2e);
+  else
+    hipLaunchKernelGGL((block_target_kl<G, 64>), dim3((unsigned)wgs), dim3(256), 0, stream, part_ml, blk, bscore,
                        target, kl, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale * kLog2e);
   return hipGetLastError();
 }

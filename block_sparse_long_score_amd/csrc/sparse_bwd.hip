@@ -185,19 +185,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int gc = min(grp * kBwdCols + 4 * scg + kk, ncols - 1);
-        const int64_t row = ((int64_t)b * n_q + (st.en[kk] >> 5)) * h_q + g * G + (gc & (G - 1));
+        const int64_t row = ((int64_t)b * n_q + entry_token(st.en[kk])) * h_q + g * G + (gc & (G - 1));
         st.v[kk] = ld16(src + row * D + sch * 8);
       }
       const int gc = grp * kBwdCols + mcol;
       const int hh = min(gc, ncols - 1) & (G - 1);
-      const int t = st.men >> 5;
+      const int t = entry_token(st.men);
       const int64_t row = ((int64_t)b * n_q + t) * h_q + g * G + hh;
       st.lse2 = lse[row] * kLog2e;
       st.dcol = dcol[row];
       // Selects by mask, not a ternary: a branch here would make the
       // compiler's wait counts at the loop head conservative.
       const int64_t live = -(int64_t)(gc < ncols);
-      const int64_t pr = ((((int64_t)b * n_q + t) * h_kv + g) * topk + (st.men & 31)) * G + hh;
+      const int64_t pr = ((((int64_t)b * n_q + t) * h_kv + g) * topk + entry_slot(st.men)) * G + hh;
       st.plim = (int)(((int64_t)(pos0 + t) & live) | (-1 & ~live));
       st.prow = (pr & live) | (sink_row & ~live);
     };

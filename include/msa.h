@@ -38,7 +38,7 @@
  *     synchronisation.  Inputs are never written.  Same inputs, same outputs,
  *     bit for bit (no floating-point atomics).  Functions are stateless and
  *     thread-safe.
- *   - Supported: block == 128; 1 <= topk <= 32; d, d_idx in {64, 128};
+ *   - Supported: block == 128; 1 <= topk <= 64; d, d_idx in {64, 128};
  *     h_q / h_kv in {1, 2, 4, 8, 16}; n_kv <= 1,048,576; pos0 + n_q <= n_kv;
  *     batch * n_q * h_kv * topk < 2^31.  batch == 0 or n_q == 0 is a no-op.
  *   - NaN or infinite inputs give undefined (but memory-safe) results.

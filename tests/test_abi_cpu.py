@@ -96,7 +96,7 @@ def test_decode_needs_single_query():
 
 @pytest.mark.parametrize("kw,op", [
     (dict(block=64), "both"),
-    (dict(topk=33), "both"),
+    (dict(topk=65), "both"),
     (dict(d=96), "attn"),
     (dict(d_idx=32), "index"),
     (dict(h_q=64, h_kv=2), "both"),          # group of 32

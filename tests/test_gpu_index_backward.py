@@ -63,6 +63,8 @@ CASES = {
     "chunk_ragged_g4": (11, Shape(1, 300, 1000, 700, 8, 2, 128, 128, topk=4), 0.1),
     "batch2_g16_d64": (12, Shape(2, 257, 600, 343, 16, 1, 64, 64, topk=3), 0.05),
     "g2_topk32_all_blocks": (14, Shape(1, 130, 2100, 1970, 16, 8, 64, 128, topk=32), 0.1),
+    # k = 64, 63 of up to 93 earlier blocks, G = 8
+    "topk64": (20, Shape(1, 300, 12000, 11700, 16, 2, 64, 64, topk=64), 0.1),
     "g8_chunk": (31, Shape(1, 700, 6000, 5300, 64, 8, 128, 128, topk=16), 1 / math.sqrt(128)),
 }
 

@@ -38,6 +38,12 @@ CASES = {
     "decode_mha16_d64": (18, Shape(2, 1, 1500, 1499, 16, 16, 64, 64, topk=4)),
     # decode with fewer causal blocks than k
     "decode_short": (19, Shape(2, 1, 300, 299, 4, 2, 64, 128, topk=16)),
+    # k = 64 (8,192 selected tokens): 63 of up to 93 earlier blocks, G = 8
+    "topk64_g8": (20, Shape(1, 300, 12000, 11700, 16, 2, 64, 64, topk=64)),
+    # k = 48, rows from below k blocks to twice k, MHA
+    "topk48_mha": (21, Shape(1, 257, 12600, 12343, 4, 4, 128, 128, topk=48)),
+    # decode with k = 64 over 1,000 blocks
+    "decode_topk64": (22, Shape(2, 1, 128000, 127999, 16, 2, 128, 128, topk=64)),
 }
 
 
@@ -165,7 +171,8 @@ def test_block_topk_entry_matches_oracle_selection():
                 assert (got[b, t, gg] == want).all(), (b, t, gg)
 
 
-@pytest.mark.parametrize("jl_span,topk", [((1048000, 1048575), 16), ((300000, 300127), 32), ((1040000, 1040200), 1)])
+@pytest.mark.parametrize("jl_span,topk", [((1048000, 1048575), 16), ((300000, 300127), 32), ((1040000, 1040200), 1),
+                                          ((900000, 900100), 64)])
 def test_block_topk_long_rows_workgroup_path(jl_span, topk):
     """Rows longer than 2,048 candidates take the workgroup-per-row kernel
     (quarters selected separately, then merged); heavy ties on every row."""

@@ -55,6 +55,8 @@ CASES = {
     "g2_topk32": (14, Shape(1, 130, 2100, 1970, 16, 8, 64, 128, topk=32), 0.1),
     # MHA, topk=1: the target is 1 on the local block and the KL 0
     "mha_topk1": (15, Shape(1, 200, 3000, 2800, 8, 8, 128, 128, topk=1), 1 / math.sqrt(128)),
+    # k = 64 (64 lanes per row), 63 of up to 93 earlier blocks
+    "topk64": (20, Shape(1, 300, 12000, 11700, 16, 2, 64, 64, topk=64), 0.1),
     # idx_scale 0: KL = ln(live slots) - entropy(target)
     "zero_idx_scale": (16, Shape(1, 300, 3000, 2700, 16, 4, 128, 128, topk=8), 0.0),
 }

@@ -19,6 +19,7 @@ enum : unsigned {
   kNeedDIdx = 2u,   // index dimension is used
   kDecode = 4u,     // n_q must be 1
   kCsr = 8u,        // per-(b, g, block) lists must fit int32
+  kOnly128 = 16u,   // the op works on 128-token blocks only
 };
 
 constexpr int64_t kMaxKv = 1 << 20;
@@ -32,7 +33,9 @@ msa_status check_dims(const msa_dims* p, unsigned need) {
   if (d.h_q % d.h_kv != 0) return MSA_ERR_SHAPE;
   if ((int64_t)d.pos0 + d.n_q > d.n_kv) return MSA_ERR_SHAPE;
   if ((need & kDecode) && d.n_q != 1) return MSA_ERR_SHAPE;
-  if (d.block != 128 || d.topk > 64) return MSA_ERR_UNSUPPORTED;
+  if (d.block != 128 && d.block != 256) return MSA_ERR_UNSUPPORTED;
+  if ((need & kOnly128) && d.block != 128) return MSA_ERR_UNSUPPORTED;
+  if (d.topk > 64 || (d.block == 256 && d.topk > 32)) return MSA_ERR_UNSUPPORTED;
   const int g = d.h_q / d.h_kv;
   if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return MSA_ERR_UNSUPPORTED;
   if ((need & kNeedD) && d.d != 64 && d.d != 128) return MSA_ERR_UNSUPPORTED;
@@ -41,7 +44,7 @@ msa_status check_dims(const msa_dims* p, unsigned need) {
   if (d.batch > 65535) return MSA_ERR_UNSUPPORTED;
   if ((int64_t)d.batch * d.n_q * d.h_kv * d.topk >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
   if ((int64_t)d.n_q * d.h_kv > (int64_t(1) << 25)) return MSA_ERR_UNSUPPORTED;
-  const int64_t nblk = (d.n_kv + d.block - 1) / d.block;
+  const int64_t nblk = (d.n_kv + 127) / 128;           // the lists are per 128-token block
   if ((need & kCsr) && (int64_t)d.batch * d.h_kv * nblk >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }
@@ -54,8 +57,66 @@ Dims to_dims(const msa_dims& d) {
 
 bool empty(const msa_dims& d) { return d.batch == 0 || d.n_q == 0; }
 
+size_t nrows(const Dims& d) { return (size_t)d.batch * d.n_q * d.h_kv; }
+
+// 256-token blocks run on the 128-token kernels: index scores per 128-token
+// block, pooled in pairs; a selection of 256-token blocks expanded into twice
+// as many 128-token blocks for the main branch.
+Dims index128(const Dims& d) {
+  Dims c = d;
+  c.block = 128;
+  return c;
+}
+Dims blocks128(const Dims& d) {
+  Dims c = index128(d);
+  if (d.block == 256) c.topk = 2 * d.topk;
+  return c;
+}
+
+// Pooled scores at offset 0 (the documented layout), for 256-token blocks
+// followed by the 128-token pooled scores they come from.
 size_t index_ws_bytes(const Dims& d) {
-  return msa::align_up((size_t)d.batch * d.n_q * d.h_kv * d.nblk() * sizeof(float), 256);
+  const size_t own = msa::align_up(nrows(d) * d.nblk() * sizeof(float), 256);
+  if (d.block == 128) return own;
+  return own + msa::align_up(nrows(d) * index128(d).nblk() * sizeof(float), 256);
+}
+// The expanded selection of a 256-token-block call, then the main branch's own.
+size_t sel_bytes(const Dims& d) {
+  return d.block == 128 ? 0 : msa::align_up(nrows(d) * 2 * d.topk * sizeof(int32_t), 256);
+}
+size_t prefill_ws_bytes(const Dims& d) { return sel_bytes(d) + msa::prefill_ws_layout(blocks128(d)).total; }
+size_t decode_ws_bytes(const Dims& d) { return sel_bytes(d) + msa::sparse_decode_ws_layout(blocks128(d)).total; }
+
+hipError_t run_index_topk(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, int32_t* blk, void* ws,
+                          hipStream_t s) {
+  float* bscore = static_cast<float*>(ws);
+  hipError_t e;
+  if (d.block == 128) {
+    e = msa::launch_index_scores(d, q_idx, k_idx, bscore, s);
+  } else {
+    float* p128 = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                           msa::align_up(nrows(d) * d.nblk() * sizeof(float), 256));
+    e = msa::launch_index_scores(index128(d), q_idx, k_idx, p128, s);
+    if (e == hipSuccess) e = msa::launch_pool_block_pairs(d, p128, bscore, s);
+  }
+  if (e != hipSuccess) return e;
+  return msa::launch_block_topk(d, bscore, blk, s);
+}
+
+hipError_t run_sparse(const Dims& d, bool decode, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const int32_t* blk, float scale, uint16_t* out, float* lse, void* ws, hipStream_t s) {
+  const Dims c = blocks128(d);
+  const int32_t* b = blk;
+  void* rest = ws;
+  if (d.block != 128) {
+    int32_t* b128 = static_cast<int32_t*>(ws);
+    const hipError_t e = msa::launch_expand_block_pairs(d, blk, b128, s);
+    if (e != hipSuccess) return e;
+    b = b128;
+    rest = static_cast<char*>(ws) + sel_bytes(d);
+  }
+  return decode ? msa::launch_sparse_decode(c, q, k, v, b, scale, out, lse, rest, s)
+                : msa::launch_sparse_prefill(c, q, k, v, b, scale, out, lse, rest, s);
 }
 
 unsigned op_needs(msa_op op) {
@@ -81,7 +142,7 @@ size_t chunked_ws_bytes(const Dims& d, int chunk, size_t* prefill_off) {
   c.n_q = chunk;
   const size_t idx = index_ws_bytes(c);
   if (prefill_off) *prefill_off = idx;
-  return idx + msa::prefill_ws_layout(c).total;
+  return idx + prefill_ws_bytes(c);
 }
 
 }  // namespace
@@ -95,9 +156,9 @@ size_t msa_workspace_size(msa_op op, const msa_dims* dims) {
   switch (op) {
     case MSA_OP_INDEX_TOPK: return index_ws_bytes(d);
     case MSA_OP_BLOCK_TOPK: return 0;
-    case MSA_OP_SPARSE_PREFILL: return msa::prefill_ws_layout(d).total;
-    case MSA_OP_SPARSE_DECODE: return msa::sparse_decode_ws_layout(d).total;
-    case MSA_OP_DENSE_GQA: return d.n_q == 1 ? msa::dense_decode_ws_layout(d).total : 0;
+    case MSA_OP_SPARSE_PREFILL: return prefill_ws_bytes(d);
+    case MSA_OP_SPARSE_DECODE: return decode_ws_bytes(d);
+    case MSA_OP_DENSE_GQA: return d.n_q == 1 ? msa::dense_decode_ws_layout(index128(d)).total : 0;
   }
   return 0;
 }
@@ -125,16 +186,12 @@ msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uin
   const Dims d = to_dims(*dims);
   if (!workspace || workspace_bytes < index_ws_bytes(d)) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* bscore = static_cast<float*>(workspace);
-  st = hip_status(msa::launch_index_scores(d, q_idx, k_idx, bscore, s));
-  if (st != MSA_OK) return st;
-  return hip_status(msa::launch_block_topk(d, bscore, blk_idx, s));
+  return hip_status(run_index_topk(d, q_idx, k_idx, blk_idx, workspace, static_cast<hipStream_t>(stream)));
 }
 
 msa_status msa_index_scores(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,
                             msa_stream stream) {
-  msa_status st = check_dims(dims, op_needs(MSA_OP_INDEX_TOPK));
+  msa_status st = check_dims(dims, op_needs(MSA_OP_INDEX_TOPK) | kOnly128);
   if (st != MSA_OK) return st;
   if (empty(*dims)) return MSA_OK;
   if (!q_idx || !k_idx || !bscore) return MSA_ERR_NULL;
@@ -162,18 +219,17 @@ msa_status msa_sparse_prefill(const msa_dims* dims, const uint16_t* q, const uin
       (lse && misaligned(lse)))
     return MSA_ERR_ALIGN;
   const Dims d = to_dims(*dims);
-  const size_t need = msa::prefill_ws_layout(d).total;
-  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < prefill_ws_bytes(d)) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
-  return hip_status(msa::launch_sparse_prefill(d, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
-                                               static_cast<hipStream_t>(stream)));
+  return hip_status(run_sparse(d, false, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
+                               static_cast<hipStream_t>(stream)));
 }
 
 msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const int32_t* blk_idx, const float* bscore, float idx_scale, float scale,
                                      uint16_t* out, float* lse, float* target, float* kl, void* workspace,
                                      size_t workspace_bytes, msa_stream stream) {
-  msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_PREFILL));
+  msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_PREFILL) | kOnly128);
   if (st != MSA_OK) return st;
   if (!std::isfinite(idx_scale)) return MSA_ERR_SHAPE;
   if (empty(*dims)) return MSA_OK;
@@ -195,7 +251,7 @@ msa_status msa_sparse_prefill_backward(const msa_dims* dims, const uint16_t* q, 
                                        const float* lse, const uint16_t* dout, float scale, uint16_t* dq,
                                        uint16_t* dk, uint16_t* dv, void* workspace, size_t workspace_bytes,
                                        msa_stream stream) {
-  msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_PREFILL));
+  msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_PREFILL) | kOnly128);
   if (st != MSA_OK) return st;
   if (dims->batch == 0 || dims->n_kv == 0) return MSA_OK;
   if (!k || !v || !dk || !dv) return MSA_ERR_NULL;
@@ -216,7 +272,7 @@ msa_status msa_index_backward(const msa_dims* dims, const uint16_t* q_idx, const
                               const int32_t* blk_idx, const float* bscore, const float* target, const float* dkl,
                               float idx_scale, float* dq_idx, float* dk_idx, void* workspace, size_t workspace_bytes,
                               msa_stream stream) {
-  msa_status st = check_dims(dims, kNeedDIdx | kCsr);
+  msa_status st = check_dims(dims, kNeedDIdx | kCsr | kOnly128);
   if (st != MSA_OK) return st;
   if (dims->h_kv > 128) return MSA_ERR_UNSUPPORTED;
   if (!std::isfinite(idx_scale)) return MSA_ERR_SHAPE;
@@ -245,11 +301,10 @@ msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint
       (lse && misaligned(lse)))
     return MSA_ERR_ALIGN;
   const Dims d = to_dims(*dims);
-  const size_t need = msa::sparse_decode_ws_layout(d).total;
-  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < decode_ws_bytes(d)) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
-  return hip_status(msa::launch_sparse_decode(d, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
-                                              static_cast<hipStream_t>(stream)));
+  return hip_status(run_sparse(d, true, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
+                               static_cast<hipStream_t>(stream)));
 }
 
 size_t msa_prefill_chunked_workspace_size(const msa_dims* dims, int32_t chunk) {
@@ -276,7 +331,6 @@ msa_status msa_prefill_chunked(const msa_dims* dims, int32_t chunk, const uint16
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float sc = resolve_scale(scale, d.d);
-  float* bscore = static_cast<float*>(workspace);
   void* pws = static_cast<char*>(workspace) + pre_off;
   for (int b = 0; b < d.batch; ++b) {
     for (int t0 = 0; t0 < d.n_q; t0 += cq) {
@@ -292,9 +346,8 @@ msa_status msa_prefill_chunked(const msa_dims* dims, int32_t chunk, const uint16
       int32_t* cb = blk_idx + row * d.h_kv * d.topk;
       uint16_t* co = out + row * d.h_q * d.d;
       float* cl = lse ? lse + row * d.h_q : nullptr;
-      st = hip_status(msa::launch_index_scores(c, ci, ck, bscore, s));
-      if (st == MSA_OK) st = hip_status(msa::launch_block_topk(c, bscore, cb, s));
-      if (st == MSA_OK) st = hip_status(msa::launch_sparse_prefill(c, cqp, k + kv_off, v + kv_off, cb, sc, co, cl, pws, s));
+      st = hip_status(run_index_topk(c, ci, ck, cb, workspace, s));
+      if (st == MSA_OK) st = hip_status(run_sparse(c, false, cqp, k + kv_off, v + kv_off, cb, sc, co, cl, pws, s));
       if (st != MSA_OK) return st;
     }
   }
@@ -314,11 +367,7 @@ msa_status msa_index_topk_varlen(const msa_dims* dims, const int32_t* seq_len, c
   d.seq_len = seq_len;
   if (!workspace || workspace_bytes < index_ws_bytes(d)) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* bscore = static_cast<float*>(workspace);
-  st = hip_status(msa::launch_index_scores(d, q_idx, k_idx, bscore, s));
-  if (st != MSA_OK) return st;
-  return hip_status(msa::launch_block_topk(d, bscore, blk_idx, s));
+  return hip_status(run_index_topk(d, q_idx, k_idx, blk_idx, workspace, static_cast<hipStream_t>(stream)));
 }
 
 msa_status msa_sparse_decode_varlen(const msa_dims* dims, const int32_t* seq_len, const uint16_t* q,
@@ -334,11 +383,10 @@ msa_status msa_sparse_decode_varlen(const msa_dims* dims, const int32_t* seq_len
     return MSA_ERR_ALIGN;
   Dims d = to_dims(*dims);
   d.seq_len = seq_len;
-  const size_t need = msa::sparse_decode_ws_layout(d).total;
-  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < decode_ws_bytes(d)) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
-  return hip_status(msa::launch_sparse_decode(d, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
-                                              static_cast<hipStream_t>(stream)));
+  return hip_status(run_sparse(d, true, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
+                               static_cast<hipStream_t>(stream)));
 }
 
 msa_status msa_dense_gqa(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v, float scale,
@@ -349,7 +397,7 @@ msa_status msa_dense_gqa(const msa_dims* dims, const uint16_t* q, const uint16_t
   if (!q || !k || !v || !out) return MSA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || (lse && misaligned(lse)))
     return MSA_ERR_ALIGN;
-  const Dims d = to_dims(*dims);
+  const Dims d = index128(to_dims(*dims));          // the selection block plays no part
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float sc = resolve_scale(scale, d.d);
   if (d.n_q == 1) {

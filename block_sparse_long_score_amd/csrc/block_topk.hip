@@ -135,7 +135,8 @@ template <int V>
 __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* __restrict__ bscore,
                                                                    int32_t* __restrict__ blk, int n_q, int pos0,
                                                                    int h_kv, int nblk, int topk, int64_t nrows,
-                                                                   int n_kv, const int* __restrict__ seq_len) {
+                                                                   int n_kv, const int* __restrict__ seq_len,
+                                                                   int lb) {
   __shared__ uint32_t ck[kRowsPerWg][64];
   __shared__ int32_t ci[kRowsPerWg][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* 
   // Candidates of a row: blocks 0 .. jl-1 (0 when the row keeps all its blocks).
   auto local_block = [&](int64_t row) {
     const int64_t bt = row / h_kv;
-    return (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + (int)(bt % n_q)) / kBlock;
+    return (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + (int)(bt % n_q)) >> lb;
   };
   auto n_cand = [&](int64_t row) {
     const int jl = local_block(row);
@@ -194,7 +195,7 @@ template <int V>
 __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __restrict__ bscore,
                                                                int32_t* __restrict__ blk, int n_q, int pos0,
                                                                int h_kv, int nblk, int topk, int n_kv,
-                                                               const int* __restrict__ seq_len) {
+                                                               const int* __restrict__ seq_len, int lb) {
   __shared__ uint32_t ck[kWgWaves][64];
   __shared__ int32_t ci[kWgWaves][64];
   __shared__ uint32_t cand_k[kWgWaves][64];
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __re
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = blockIdx.x;
   const int64_t bt = row / h_kv;
-  const int jl = (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + (int)(bt % n_q)) / kBlock;
+  const int jl = (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + (int)(bt % n_q)) >> lb;
   int32_t* out = blk + row * topk;
   if (jl + 1 <= topk) {                                // whole workgroup leaves together
     for (int i = threadIdx.x; i < topk; i += kWgWaves * 64) out[i] = (i <= jl) ? i : -1;
@@ -269,7 +270,7 @@ hipError_t launch_v(const Dims& d, const float* bscore, int32_t* blk, hipStream_
   {
     LaunchTimer timer("block_topk_rows", stream);
     hipLaunchKernelGGL(block_topk_rows<V>, dim3((unsigned)wgs), dim3(kRowsPerWg * 64), 0, stream, bscore, blk,
-                       d.n_q, d.pos0, d.h_kv, d.nblk(), d.topk, nrows, d.n_kv, d.seq_len);
+                       d.n_q, d.pos0, d.h_kv, d.nblk(), d.topk, nrows, d.n_kv, d.seq_len, block_shift(d));
   }
   return hipGetLastError();
 }
@@ -280,7 +281,7 @@ hipError_t launch_wg(const Dims& d, const float* bscore, int32_t* blk, hipStream
   {
     LaunchTimer timer("block_topk_wg", stream);
     hipLaunchKernelGGL(block_topk_wg<V>, dim3((unsigned)nrows), dim3(kWgWaves * 64), 0, stream, bscore, blk, d.n_q,
-                       d.pos0, d.h_kv, d.nblk(), d.topk, d.n_kv, d.seq_len);
+                       d.pos0, d.h_kv, d.nblk(), d.topk, d.n_kv, d.seq_len, block_shift(d));
   }
   return hipGetLastError();
 }
@@ -288,7 +289,7 @@ hipError_t launch_wg(const Dims& d, const float* bscore, int32_t* blk, hipStream
 }  // namespace
 
 hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
-  const int jl_max = d.seq_len ? (d.n_kv - 1) / kBlock : (d.pos0 + d.n_q - 1) / kBlock;   // most candidates of a row
+  const int jl_max = (d.seq_len ? d.n_kv - 1 : d.pos0 + d.n_q - 1) >> block_shift(d);   // most candidates of a row
   const int per_lane = (jl_max + 63) / 64;
   if (per_lane <= 1) return launch_v<1>(d, bscore, blk, stream);
   if (per_lane <= 2) return launch_v<2>(d, bscore, blk, stream);
@@ -300,6 +301,64 @@ hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk, h
   const int per_lane_q = ((jl_max + kWgWaves - 1) / kWgWaves + 63) / 64;
   if (per_lane_q <= 16) return launch_wg<16>(d, bscore, blk, stream);
   return launch_wg<32>(d, bscore, blk, stream);         // the C-ABI caps nblk at 8192
+}
+
+// ------------------------------------------------- 256-token blocks -------
+//
+// A block of 256 tokens is two blocks of 128: its pooled score is the larger
+// of the two 128-token pooled scores (the second one only when it holds a
+// causal token), so the top-k over 256-token blocks runs on these maxima, and
+// a selected 256-token block j stands for the 128-token blocks 2j and 2j + 1
+// in the main branch (a 128-token block past the query is skipped there).
+
+namespace {
+
+__global__ __launch_bounds__(256) void pool_block_pairs(const float* __restrict__ p128, float* __restrict__ p256,
+                                                        int64_t nrows, int n_q, int pos0, int h_kv, int nblk128,
+                                                        int nblk256, int n_kv, const int* __restrict__ seq_len) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nrows * nblk256) return;
+  const int64_t row = i / nblk256;
+  const int j = (int)(i % nblk256);
+  const int64_t bt = row / h_kv;
+  const int jl128 = (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + (int)(bt % n_q)) / kBlock;
+  const float* src = p128 + row * nblk128;
+  float v = -INFINITY;
+  if (2 * j <= jl128) v = src[2 * j];
+  if (2 * j + 1 <= jl128) v = vmax(v, src[2 * j + 1]);
+  p256[i] = v;
+}
+
+__global__ __launch_bounds__(256) void expand_block_pairs(const int32_t* __restrict__ blk256,
+                                                          int32_t* __restrict__ blk128, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int j = blk256[i];
+  int2 o;
+  o.x = j >= 0 ? 2 * j : -1;
+  o.y = j >= 0 ? 2 * j + 1 : -1;
+  *reinterpret_cast<int2*>(blk128 + 2 * i) = o;
+}
+
+}  // namespace
+
+hipError_t launch_pool_block_pairs(const Dims& d, const float* p128, float* p256, hipStream_t stream) {
+  const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
+  const int nblk128 = (d.n_kv + kBlock - 1) / kBlock, nblk256 = (d.n_kv + 2 * kBlock - 1) / (2 * kBlock);
+  const int64_t n = nrows * nblk256;
+  if (n == 0) return hipSuccess;
+  LaunchTimer timer("pool_block_pairs", stream);
+  hipLaunchKernelGGL(pool_block_pairs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p128, p256, nrows,
+                     d.n_q, d.pos0, d.h_kv, nblk128, nblk256, d.n_kv, d.seq_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_block_pairs(const Dims& d, const int32_t* blk256, int32_t* blk128, hipStream_t stream) {
+  const int64_t n = (int64_t)d.batch * d.n_q * d.h_kv * d.topk;
+  if (n == 0) return hipSuccess;
+  LaunchTimer timer("expand_block_pairs", stream);
+  hipLaunchKernelGGL(expand_block_pairs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, blk256, blk128, n);
+  return hipGetLastError();
 }
 
 }  // namespace msa

@@ -59,6 +59,13 @@ DecodeWs dense_decode_ws_layout(const Dims& d);
 hipError_t launch_index_scores(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,
                                hipStream_t stream);
 hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk_idx, hipStream_t stream);
+// log2 of the selection block size (128 or 256).
+inline int block_shift(const Dims& d) { return d.block == 256 ? 8 : 7; }
+// 256-token blocks from 128-token ones: pooled scores of pairs (rows of the
+// 256-token dims d), and a 256-token selection expanded into 128-token blocks
+// (2 * topk per row, ascending, -1 padded).
+hipError_t launch_pool_block_pairs(const Dims& d, const float* p128, float* p256, hipStream_t stream);
+hipError_t launch_expand_block_pairs(const Dims& d, const int32_t* blk256, int32_t* blk128, hipStream_t stream);
 hipError_t launch_sparse_prefill(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* ws,
                                  hipStream_t stream);

@@ -38,9 +38,20 @@
  *     synchronisation.  Inputs are never written.  Same inputs, same outputs,
  *     bit for bit (no floating-point atomics).  Functions are stateless and
  *     thread-safe.
- *   - Supported: block == 128; 1 <= topk <= 64; d, d_idx in {64, 128};
+ *   - Supported: block 128 or 256; 1 <= topk <= 64 (<= 32 with block 256);
+ *     d, d_idx in {64, 128};
  *     h_q / h_kv in {1, 2, 4, 8, 16}; n_kv <= 1,048,576; pos0 + n_q <= n_kv;
  *     batch * n_q * h_kv * topk < 2^31.  batch == 0 or n_q == 0 is a no-op.
+ *   - Block 256 (the pages note that block size and selection must be
+ *     re-tuned for longer contexts; lefilia.fr / yhxrc.cn articles): a block
+ *     of 256 tokens is two of 128, its pooled score the larger of theirs, so
+ *     the same pooled scores, selections and outputs follow as with a plain
+ *     256-token max-pool; the main branch runs on the two 128-token halves of
+ *     each selected block.  msa_index_scores, msa_sparse_prefill_target and
+ *     both backward calls take block 128 only (MSA_ERR_UNSUPPORTED).  With
+ *     block 256 the index workspace holds the 256-token pooled scores at
+ *     offset 0 followed by the 128-token ones, and the sparse workspaces begin
+ *     with the expanded 128-token selection.
  *   - NaN or infinite inputs give undefined (but memory-safe) results.
  */
 #ifndef MSA_H_

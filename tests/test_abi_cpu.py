@@ -260,3 +260,26 @@ def test_index_backward_argument_checks():
     need = lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d))
     assert call(d, wsb=need - 1) == WS
     assert call(dims(batch=0), qi=None, ki=None, dki=None, ws=None) == OK
+
+
+def test_block256_rules():
+    """256-token blocks: the forward calls take them (k <= 32), the target and
+    backward calls and msa_index_scores do not."""
+    lib = M.lib()
+    d = dims(block=256, topk=16)
+    d33 = dims(block=256, topk=33)
+    assert lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d)) > 0
+    assert lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d33)) == 0
+    assert prefill_call(d33) == UNSUP
+    # index workspace holds the 256-token pooled scores and the 128-token ones
+    d128 = dims(block=128, topk=16)
+    w256 = lib.msa_workspace_size(M.MSA_OP_INDEX_TOPK, ctypes.byref(d))
+    w128 = lib.msa_workspace_size(M.MSA_OP_INDEX_TOPK, ctypes.byref(d128))
+    assert w256 >= w128 + w128 // 2
+    assert lib.msa_index_scores(ctypes.byref(d), FAKE, FAKE, FAKE, None) == UNSUP
+    assert lib.msa_sparse_prefill_target(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0),
+                                         ctypes.c_float(0.0), FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUP
+    assert lib.msa_sparse_prefill_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           ctypes.c_float(0.0), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUP
+    assert lib.msa_index_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE,
+                                  FAKE, FAKE, 1 << 40, None) == UNSUP

@@ -22,6 +22,8 @@ CASES = {
     "single_chunk": (53, Shape(1, 700, 2500, 1800, 8, 2, 128, 64, topk=4), 5000),
     # chunk of one query
     "chunk_of_one": (54, Shape(1, 40, 1500, 1460, 8, 8, 64, 128, topk=16), 1),
+    # 256-token blocks, ragged last chunk
+    "block256": (55, Shape(2, 1000, 6000, 5000, 16, 4, 128, 128, block=256, topk=8), 384),
 }
 
 

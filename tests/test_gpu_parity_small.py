@@ -44,6 +44,14 @@ CASES = {
     "topk48_mha": (21, Shape(1, 257, 12600, 12343, 4, 4, 128, 128, topk=48)),
     # decode with k = 64 over 1,000 blocks
     "decode_topk64": (22, Shape(2, 1, 128000, 127999, 16, 2, 128, 128, topk=64)),
+    # 256-token blocks: partial last block (1000 = 3 * 256 + 232), ragged chunk, k = 3
+    "block256_chunk_ragged": (23, Shape(1, 300, 1000, 700, 8, 2, 128, 128, block=256, topk=3)),
+    # 256-token blocks, G = 8, 15 of up to 35 earlier blocks
+    "block256_g8": (24, Shape(1, 600, 9000, 8400, 64, 8, 128, 128, block=256, topk=16)),
+    # 256-token blocks, k = 32 (64 blocks of 128 in the main branch), two sequences, d = 64
+    "block256_k32_d64": (25, Shape(2, 257, 20000, 19743, 16, 2, 64, 64, block=256, topk=32)),
+    # 256-token blocks, decode
+    "block256_decode": (26, Shape(3, 1, 50000, 49999, 64, 8, 128, 128, block=256, topk=16)),
 }
 
 

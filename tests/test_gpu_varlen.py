@@ -43,11 +43,14 @@ def check_against_oracle(s, seq_len, inp, blk, bscore, out, lse, what):
     chk.verify()
 
 
-@pytest.mark.parametrize("case", ["mixed_g4", "mixed_mqa_d64"])
+@pytest.mark.parametrize("case", ["mixed_g4", "mixed_mqa_d64", "block256"])
 def test_varlen_decode_matches_oracle_per_sequence(case):
     if case == "mixed_g4":
         s = Shape(7, 1, 3000, 2999, 16, 4, 128, 128, topk=8)
         seq_len = [1, 127, 128, 129, 1023, 2000, 3000]
+    elif case == "block256":
+        s = Shape(7, 1, 9000, 8999, 16, 4, 128, 128, block=256, topk=8)
+        seq_len = [1, 255, 256, 257, 3000, 8000, 9000]
     else:
         s = Shape(5, 1, 2500, 2499, 4, 1, 64, 64, topk=16)
         seq_len = [2500, 5, 300, 2047, 1300]

@@ -42,8 +42,8 @@
  *     d, d_idx in {64, 128};
  *     h_q / h_kv in {1, 2, 4, 8, 16}; n_kv <= 1,048,576; pos0 + n_q <= n_kv;
  *     batch * n_q * h_kv * topk < 2^31.  batch == 0 or n_q == 0 is a no-op.
- *   - Block 256 (the pages note that block size and selection must be
- *     re-tuned for longer contexts; lefilia.fr / yhxrc.cn articles): a block
+ *   - Block 256 (yhxrc.cn article, "社區沖擊與深層信號": block size and
+ *     selection may have to be re-tuned for far longer contexts): a block
  *     of 256 tokens is two of 128, its pooled score the larger of theirs, so
  *     the same pooled scores, selections and outputs follow as with a plain
  *     256-token max-pool; the main branch runs on the two 128-token halves of

@@ -257,11 +257,21 @@ def main():
     ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
     torch.cuda.synchronize()
 
-    stages = [
-        lambda: M.msa_index_scores(s, inp["q_idx"], inp["k_idx"], bscore),
-        lambda: M.msa_block_topk(s, bscore, blk),
-        lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
-    ]
+    if s.block == 128:
+        stages = [
+            lambda: M.msa_index_scores(s, inp["q_idx"], inp["k_idx"], bscore),
+            lambda: M.msa_block_topk(s, bscore, blk),
+            lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
+        ]
+    else:
+        # 256-token blocks: msa_index_topk scores, pools in pairs and selects
+        # in one call (its time is reported under the index stage).
+        ws_idx = M.alloc_workspace(M.MSA_OP_INDEX_TOPK, s)
+        stages = [
+            lambda: M.msa_index_topk(s, inp["q_idx"], inp["k_idx"], blk, ws_idx),
+            lambda: None,
+            lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
+        ]
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
     ms_step, (ms_idx, ms_topk, ms_sparse), kern = time_calls(torch, stages, args.steps, args.warmup, M)
     tokens = s.batch * s.n_q
@@ -323,7 +333,7 @@ def main():
         "end_to_end_mfma_frac": (f_idx + f_sp) / (ms_step * 1e-3) / PEAK_BF16_FLOPS,
     }
 
-    if not args.no_topk_compare:
+    if not args.no_topk_compare and s.block == 128:
         vals = bscore[..., : s.nblk]
         ms_torch, _ = time_calls(torch, [lambda: torch.topk(vals, s.topk - 1, dim=-1)], 3, 1)
         result["topk_vs_torch"] = {"msa_block_topk_ms": ms_topk, "torch_topk_ms": ms_torch,
@@ -331,7 +341,7 @@ def main():
                                    "note": "torch.topk over the full pooled rows, k-1 per row; timing only"}
         log(f"top-k: msa {ms_topk:.3f} ms vs torch.topk {ms_torch:.3f} ms")
 
-    if not args.no_target:
+    if not args.no_target and s.block == 128:
         # Index-branch training target (forward only): msa_sparse_prefill plus
         # block_target_kl on the same inputs; block_target_kl's own time from
         # the library's event pairs.
@@ -350,7 +360,7 @@ def main():
             f"({tb / (ms_k * 1e-3) / PEAK_HBM_BYTES:.1%} of HBM peak)")
         del target, kl
 
-    if not args.no_backward:
+    if not args.no_backward and s.block == 128:
         # Main-branch backward on the same selection: dq, dk, dv from a seeded
         # output gradient; algorithmic work 10 d flops per (query head, visible
         # key) (S, dP, dV, dK, dQ), i.e. 2.5x the forward's S4 count.

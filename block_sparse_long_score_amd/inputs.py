@@ -65,6 +65,10 @@ WORKLOADS = {
     "decode_1m_b8": (6, Shape(8, 1, 1048576, 1048575, 64, 8, 128, 128)),
     # a whole 1,048,576-token causal prefill (run in chunks of 8,192 queries)
     "prefill_1m_full": (7, Shape(1, 1048576, 1048576, 0, 64, 8, 128, 128)),
+    # selection variants on the 131,072-token prefill's tensors: 32 blocks of
+    # 128 (4,096 tokens), and 8 blocks of 256 (the same 2,048-token budget)
+    "prefill_128k_k32": (3, Shape(1, 131072, 131072, 0, 64, 8, 128, 128, topk=32)),
+    "prefill_128k_b256": (3, Shape(1, 131072, 131072, 0, 64, 8, 128, 128, block=256, topk=8)),
 }
 
 

@@ -324,7 +324,7 @@ hipError_t launch_index_bwd_t(const Dims& d, const uint16_t* q_idx, const uint16
       hipLaunchKernelGGL(index_kl_coef<64>, dim3((unsigned)wgs), dim3(256), 0, stream, blk, bscore, target, dkl,
                          coef, nrows, d.n_q, d.h_kv, d.pos0, d.topk, d.nblk(), idx_scale);
   }
-  hipError_t e = launch_csr(d, blk, ws, stream);
+  hipError_t e = launch_csr(d, blk, ws, stream, true);    // sums run in list order
   if (e != hipSuccess) return e;
   {
     LaunchTimer timer("index_bwd_kv", stream);

@@ -45,8 +45,9 @@ struct PrefillWs {
   int64_t lists, chunks, entries_max;
 };
 PrefillWs prefill_ws_layout(const Dims& d);
-// Builds the per-(b, g, block) lists of (t, slot) entries in the workspace.
-hipError_t launch_csr(const Dims& d, const int32_t* blk, void* ws, hipStream_t stream);
+// Builds the per-(b, g, block) lists of (t, slot) entries in the workspace;
+// `ordered`: each list sorted by (t, slot), for kernels that sum over a list.
+hipError_t launch_csr(const Dims& d, const int32_t* blk, void* ws, hipStream_t stream, bool ordered);
 
 // Decode / dense-decode partials.
 struct DecodeWs {

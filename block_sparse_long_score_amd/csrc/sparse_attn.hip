@@ -129,6 +129,30 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan(const int* __restrict__
   if (tid == kScanThreads - 1) off[lists] = s_e[tid];
 }
 
+// Unordered fill, for callers whose results do not depend on the order inside
+// a list (the forward: every partial comes from its own column): entries of
+// chunk c go to off[list] + (prefix of earlier chunks) + a rank taken from an
+// LDS cursor.
+__global__ __launch_bounds__(kCsrThreads) void csr_fill_any(const int32_t* __restrict__ blk,
+                                                            const int* __restrict__ off,
+                                                            const int* __restrict__ ccnt,
+                                                            int* __restrict__ entries, int n_q, int h_kv, int topk,
+                                                            int nblk, int pos0, int tc, int chunks) {
+  __shared__ int cur[kCsrMaxBlocks];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int t0 = c * tc, t1 = min(n_q, t0 + tc);
+  const int* pre = ccnt + (((int64_t)b * h_kv + g) * chunks + c) * nblk;
+  const int* loff = off + ((int64_t)b * h_kv + g) * nblk;
+  for (int j = threadIdx.x; j < nblk; j += kCsrThreads) cur[j] = loff[j] + pre[j];
+  __syncthreads();
+  const int n = (t1 - t0) * topk;
+  for (int k = threadIdx.x; k < n; k += kCsrThreads) {
+    const int t = t0 + k / topk, slot = k % topk;
+    const int j = entry_block(blk, ((int64_t)b * n_q + t) * h_kv + g, slot, topk, t, pos0);
+    if (j >= 0) entries[atomicAdd(&cur[j], 1)] = (t << kSlotBits) | slot;
+  }
+}
+
 // Entries of chunk c go to off[list] + (prefix of earlier chunks) + their rank
 // among the chunk's entries of that list in (token, slot) order.  One wave per
 // chunk: its lanes take the chunk's items in rounds of 64 (64 / T tokens, T =
@@ -580,7 +604,7 @@ hipError_t launch_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* k,
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
   const int nblk = d.nblk();
   const int lists = (int)L.lists;
-  hipError_t e = launch_csr(d, blk, ws, stream);
+  hipError_t e = launch_csr(d, blk, ws, stream, false);   // partials do not depend on list order
   if (e != hipSuccess) return e;
   {
     LaunchTimer timer("sparse_kv_outer", stream);
@@ -634,7 +658,7 @@ hipError_t decode_by_group(const Dims& d, const uint16_t* q, const uint16_t* k, 
 
 }  // namespace
 
-hipError_t launch_csr(const Dims& d, const int32_t* blk, void* ws, hipStream_t stream) {
+hipError_t launch_csr(const Dims& d, const int32_t* blk, void* ws, hipStream_t stream, bool ordered) {
   const PrefillWs L = prefill_ws_layout(d);
   char* base = static_cast<char*>(ws);
   int* cnt = reinterpret_cast<int*>(base + L.cnt);
@@ -660,10 +684,14 @@ hipError_t launch_csr(const Dims& d, const int32_t* blk, void* ws, hipStream_t s
     LaunchTimer timer("csr_scan", stream);
     hipLaunchKernelGGL(csr_scan, dim3(1), dim3(kScanThreads), 0, stream, cnt, off, lists);
   }
-  {
+  if (ordered) {
     LaunchTimer timer("csr_fill_chunks", stream);
     hipLaunchKernelGGL(csr_fill_chunks, cgrid, dim3(kFillThreads), (unsigned)(nblk * sizeof(int)), stream, blk, off,
                        ccnt, entries, d.n_q, d.h_kv, d.topk, nblk, d.pos0, tc, chunks);
+  } else {
+    LaunchTimer timer("csr_fill_any", stream);
+    hipLaunchKernelGGL(csr_fill_any, cgrid, dim3(kCsrThreads), 0, stream, blk, off, ccnt, entries, d.n_q, d.h_kv,
+                       d.topk, nblk, d.pos0, tc, chunks);
   }
   return hipGetLastError();
 }

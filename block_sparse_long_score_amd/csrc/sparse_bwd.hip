@@ -381,7 +381,7 @@ hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, const uint16_t* k, con
     LaunchTimer timer("bwd_row_dot", stream);
     hipLaunchKernelGGL(bwd_row_dot<D>, dim3((unsigned)row_wgs), dim3(256), 0, stream, out, dout, dcol, nrows);
   }
-  hipError_t e = launch_csr(d, blk, ws, stream);
+  hipError_t e = launch_csr(d, blk, ws, stream, true);    // sums run in list order
   if (e != hipSuccess) return e;
   {
     LaunchTimer timer("sparse_bwd_kv", stream);

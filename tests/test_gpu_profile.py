@@ -24,7 +24,7 @@ def test_profile_records_each_launch():
         M.msa_block_topk(s, bscore, blk)
         M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, None, ws)
     k = M.msa_profile_end()
-    for name in ("index_scores_tiled", "block_topk_rows", "csr_count_chunks", "csr_fill_chunks", "sparse_kv_outer",
+    for name in ("index_scores_tiled", "block_topk_rows", "csr_count_chunks", "csr_fill_any", "sparse_kv_outer",
                  "merge_partials"):
         assert name in k, (name, k)
         assert k[name][0] == 2 and k[name][1] > 0.0, (name, k[name])

@@ -30,7 +30,7 @@ constexpr int kBwdCols = 32;                           // (entry x head) columns
 // d at u ^ ((d >> 2) & 7).
 // Rows are padded to kTtStride elements and the unit is XOR'd with (d >> 3) & 7:
 // the dk / dv operand reads (16 rows x 4 units per wave) then hit every bank
-// pair once, and the staging writes (8-byte words of 4 columns) at most twice.
+// pair once, and the staging writes (4-byte words of 2 columns) at most twice.
 constexpr int kTtStride = 40;
 __device__ __forceinline__ int tt_off(int d, int col) {
   return d * kTtStride + 4 * (((col >> 2) ^ (d >> 3)) & 7) + (col & 3);
@@ -84,16 +84,16 @@ __global__ __launch_bounds__(256) void bwd_row_dot(const uint16_t* __restrict__ 
   if (row < nrows && dl == 0) dcol[row] = sum;
 }
 
-// Registers of the next column group: this thread's staging tile (4 columns x
+// Registers of the next column group: this thread's staging tile (2 columns x
 // one 16-byte chunk of q or dout), the values of its meta column (tid & 31),
-// and the entries of the group after it (the 4 staging columns and the meta
+// and the entries of the group after it (the 2 staging columns and the meta
 // column).
 struct BwdStage {
-  u32x4 v[4];
+  u32x4 v[2];
   int64_t prow;
   float lse2, dcol;
   int plim;
-  int en[4], men;
+  int en[2], men;
 };
 
 template <int D, int LOG2G>
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
   constexpr int DC = D / 8;                            // 16-byte chunks per row
   constexpr int DT = D / 16;                           // 16-wide d tiles
   constexpr int CTW = D / 64;                          // column tiles of dq per wave
-  constexpr int NST = 2 * 8 * DC;                      // staging threads: 4-column tiles of q and dout
+  constexpr int NST = 2 * 16 * DC;                     // staging threads: 2-column tiles of q and dout
   __shared__ BwdLds<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m16 = lane & 15, q4 = lane >> 4;
@@ -167,10 +167,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
   const int ngroups = (ncols + kBwdCols - 1) / kBwdCols;
   if (ngroups > 0) {
     const int skey = s0 + mykey;
-    // Staging role: tensor `which` (q or dout), columns 4*scg .. 4*scg + 3,
-    // chunk sch.  Threads beyond NST mirror the first NST and write nothing;
-    // every thread also carries the meta values of column tid & 31.
-    const int st_id = tid % NST, which = st_id / (8 * DC), scg = (st_id % (8 * DC)) / DC, sch = st_id % DC;
+    // Staging role: tensor `which` (q or dout), columns 2*scp and 2*scp + 1,
+    // chunk sch (d = 128: every thread; d = 64: threads beyond NST mirror the
+    // first NST and write nothing); every thread also carries the meta values
+    // of column tid & 31.
+    const int st_id = tid % NST, which = st_id / (16 * DC), scp = (st_id % (16 * DC)) / DC, sch = st_id % DC;
     const int mcol = tid & 31;
     const uint16_t* src = which ? dout : q;
     // Every load of the loop reads a real row (the column index is clamped), so
@@ -183,8 +184,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
     };
     auto fetch = [&](BwdStage& st, int grp) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int gc = min(grp * kBwdCols + 4 * scg + kk, ncols - 1);
+      for (int kk = 0; kk < 2; ++kk) {
+        const int gc = min(grp * kBwdCols + 2 * scp + kk, ncols - 1);
         const int64_t row = ((int64_t)b * n_q + entry_token(st.en[kk])) * h_q + g * G + (gc & (G - 1));
         st.v[kk] = ld16(src + row * D + sch * 8);
       }
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
     };
     auto load_entries = [&](BwdStage& st, int grp) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) st.en[kk] = entry_at(grp, 4 * scg + kk);
+      for (int kk = 0; kk < 2; ++kk) st.en[kk] = entry_at(grp, 2 * scp + kk);
       st.men = entry_at(grp, mcol);
     };
     BwdStage st;
@@ -215,22 +216,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
     // them those of the loop itself.
     __builtin_amdgcn_s_waitcnt(0);
     for (int grp = 0; grp < ngroups; ++grp) {
-      // Transpose the staging tile in registers (4 columns per 8-byte word),
+      // Transpose the staging tile in registers (2 columns per 4-byte word),
       // outside the writer branch so the waits for the loads stay outside too.
-      u32x2 tw[8];
+      uint32_t tw[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int wd = e >> 1, sh = 16 * (e & 1);
-        tw[e][0] = ((st.v[0][wd] >> sh) & 0xffffu) | (((st.v[1][wd] >> sh) & 0xffffu) << 16);
-        tw[e][1] = ((st.v[2][wd] >> sh) & 0xffffu) | (((st.v[3][wd] >> sh) & 0xffffu) << 16);
+        tw[e] = ((st.v[0][wd] >> sh) & 0xffffu) | (((st.v[1][wd] >> sh) & 0xffffu) << 16);
       }
       if (tid < NST) {                                 // wave-uniform
         uint16_t* rt = which ? sm.g.dor : sm.g.qr;
         uint16_t* tt = which ? sm.g.dot : sm.g.qt;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) st16(&rt[rt_off<D>(4 * scg + kk, sch)], st.v[kk]);
+        for (int kk = 0; kk < 2; ++kk) st16(&rt[rt_off<D>(2 * scp + kk, sch)], st.v[kk]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x2*>(&tt[tt_off(8 * sch + e, 4 * scg)]) = tw[e];
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(&tt[tt_off(8 * sch + e, 2 * scp)]) = tw[e];
       }
       // Every thread of a meta column writes the same values.
       sm.g.plim[mcol] = st.plim;

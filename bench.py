@@ -452,6 +452,26 @@ def main():
             dec["index_scores_skinny_hbm_frac"] = kidx_bytes / (tot / n * 1e-3) / PEAK_HBM_BYTES
         log(f"decode step {ms_dec:.3f} ms ({ms_di:.3f} index top-k + {ms_ds:.3f} sparse) -> "
             f"{dec['tok_s']:.4g} tok/s, {dec['hbm_frac'] * 100:.1f}% of HBM peak")
+        # The same step captured once in a HIP graph and replayed: a serving
+        # loop's form, without launch gaps between its kernels.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for f in dec_calls:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for f in dec_calls:
+                f()
+        ms_g, _ = time_calls(torch, [graph.replay], dsteps, args.warmup)
+        dec["graph_ms_per_step"] = ms_g
+        dec["graph_tok_s"] = ds.batch / (ms_g * 1e-3)
+        dec["graph_hbm_frac"] = by / (ms_g * 1e-3) / PEAK_HBM_BYTES
+        log(f"decode step as a HIP graph {ms_g:.3f} ms -> {dec['graph_tok_s']:.4g} tok/s, "
+            f"{dec['graph_hbm_frac'] * 100:.1f}% of HBM peak")
+        del graph
         if not args.no_dense:
             ddws = M.alloc_workspace(M.MSA_OP_DENSE_GQA, ds)
             ms_dd, _ = time_calls(torch, [lambda: M.msa_dense_gqa(ds, dinp["q"], dinp["k"], dinp["v"], dout, dlse,

@@ -74,10 +74,12 @@ CASES = {
     "mha_d128": (13, Shape(1, 520, 520, 0, 8, 8, 128, 64, topk=2)),
     # G = 2, topk 32 >= every causal block
     "g2_topk32_all_blocks": (14, Shape(1, 130, 2100, 1970, 16, 8, 64, 128, topk=32)),
-    # G = 8 at the real head shape
     # k = 64, 63 of up to 93 earlier blocks, G = 8
     "topk64": (20, Shape(1, 300, 12000, 11700, 16, 2, 64, 64, topk=64)),
+    # G = 8 at the real head shape
     "g8_chunk": (31, Shape(1, 700, 6000, 5300, 64, 8, 128, 128, topk=16)),
+    # the whole sequence inside one partial block
+    "single_partial_block": (27, Shape(1, 50, 50, 0, 8, 2, 128, 128, topk=16)),
 }
 
 

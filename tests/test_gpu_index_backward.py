@@ -66,6 +66,8 @@ CASES = {
     # k = 64, 63 of up to 93 earlier blocks, G = 8
     "topk64": (20, Shape(1, 300, 12000, 11700, 16, 2, 64, 64, topk=64), 0.1),
     "g8_chunk": (31, Shape(1, 700, 6000, 5300, 64, 8, 128, 128, topk=16), 1 / math.sqrt(128)),
+    # one live slot per row (the sequence inside one block): every gradient is zero
+    "single_partial_block": (27, Shape(1, 50, 50, 0, 8, 2, 128, 128, topk=16), 0.1),
 }
 
 

@@ -52,6 +52,14 @@ CASES = {
     "block256_k32_d64": (25, Shape(2, 257, 20000, 19743, 16, 2, 64, 64, block=256, topk=32)),
     # 256-token blocks, decode
     "block256_decode": (26, Shape(3, 1, 50000, 49999, 64, 8, 128, 128, block=256, topk=16)),
+    # the whole sequence inside one partial block: every row selects block 0 only
+    "single_partial_block": (27, Shape(1, 50, 50, 0, 8, 2, 128, 128, topk=16)),
+    # decode of the very first token: one key, one block
+    "first_token_decode": (28, Shape(1, 1, 1, 0, 4, 1, 64, 64, topk=16)),
+    # two full blocks, k = 2: the second block's rows take both blocks
+    "two_full_blocks_k2": (29, Shape(1, 256, 256, 0, 8, 2, 64, 64, topk=2)),
+    # 256-token blocks, the sequence inside one partial block
+    "block256_single_partial": (30, Shape(1, 100, 100, 0, 8, 2, 64, 64, block=256, topk=4)),
 }
 
 

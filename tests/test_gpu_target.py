@@ -59,6 +59,8 @@ CASES = {
     "topk64": (20, Shape(1, 300, 12000, 11700, 16, 2, 64, 64, topk=64), 0.1),
     # idx_scale 0: KL = ln(live slots) - entropy(target)
     "zero_idx_scale": (16, Shape(1, 300, 3000, 2700, 16, 4, 128, 128, topk=8), 0.0),
+    # the sequence inside one partial block: target 1 on block 0, KL 0
+    "single_partial_block": (27, Shape(1, 50, 50, 0, 8, 2, 128, 128, topk=16), 0.1),
 }
 
 

@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="prefill_128k")
     ap.add_argument("--decode-workload", default="decode_1m_b8")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the decode step replayed as a HIP graph")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the variable-length decode leg")
     ap.add_argument("--no-prefill-1m", action="store_true",
                     help="skip the whole 1M-token chunked prefill leg")
     ap.add_argument("--no-dense", action="store_true")
@@ -219,6 +221,27 @@ def cpu_baseline(s, inp, seconds, seed=99):
 
 
 # -------------------------------------------------------------------- main --
+
+def decode_graph_leg(torch, dec, dec_calls, dsteps, warmup, batch, by):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in dec_calls:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for f in dec_calls:
+            f()
+    ms_g, _ = time_calls(torch, [graph.replay], dsteps, warmup)
+    dec["graph_ms_per_step"] = ms_g
+    dec["graph_tok_s"] = batch / (ms_g * 1e-3)
+    dec["graph_hbm_frac"] = by / (ms_g * 1e-3) / PEAK_HBM_BYTES
+    log(f"decode step as a HIP graph {ms_g:.3f} ms -> {dec['graph_tok_s']:.4g} tok/s, "
+        f"{dec['graph_hbm_frac'] * 100:.1f}% of HBM peak")
+    del graph
+
 
 def main():
     args = parse()
@@ -454,24 +477,8 @@ def main():
             f"{dec['tok_s']:.4g} tok/s, {dec['hbm_frac'] * 100:.1f}% of HBM peak")
         # The same step captured once in a HIP graph and replayed: a serving
         # loop's form, without launch gaps between its kernels.
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for f in dec_calls:
-                f()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for f in dec_calls:
-                f()
-        ms_g, _ = time_calls(torch, [graph.replay], dsteps, args.warmup)
-        dec["graph_ms_per_step"] = ms_g
-        dec["graph_tok_s"] = ds.batch / (ms_g * 1e-3)
-        dec["graph_hbm_frac"] = by / (ms_g * 1e-3) / PEAK_HBM_BYTES
-        log(f"decode step as a HIP graph {ms_g:.3f} ms -> {dec['graph_tok_s']:.4g} tok/s, "
-            f"{dec['graph_hbm_frac'] * 100:.1f}% of HBM peak")
-        del graph
+        if not args.no_graph:
+            decode_graph_leg(torch, dec, dec_calls, dsteps, args.warmup, ds.batch, by)
         if not args.no_dense:
             ddws = M.alloc_workspace(M.MSA_OP_DENSE_GQA, ds)
             ms_dd, _ = time_calls(torch, [lambda: M.msa_dense_gqa(ds, dinp["q"], dinp["k"], dinp["v"], dout, dlse,
@@ -481,6 +488,7 @@ def main():
             log(f"dense decode {ms_dd:.3f} ms -> MSA decode speedup {ms_dd / ms_dec:.2f}x")
         result["decode"] = dec
 
+    if not args.no_decode and not args.no_varlen:
         # Variable-length decode on the same caches: each sequence holds its
         # own number of tokens of the 1M capacity.
         lens = [ds.n_kv, 786432, 524288, 262144, 100000, 10000, 1000, 100][: ds.batch]

@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-target", action="store_true", help="skip the index-branch target (KL) leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the main-branch and index-branch backward legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the measured bf16 GEMM and device-copy reference rates")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
@@ -147,6 +149,50 @@ def measured_traffic(kernel, workload):
 
 # ------------------------------------------------------------------ timing --
 
+LAST_STEPS = []   # per-step times (ms) of the latest time_calls
+
+
+def step_stats():
+    v = sorted(LAST_STEPS)
+    n = len(v)
+    med = (v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])) if n else None
+    return {"median": med, "min": v[0] if n else None}
+
+
+def measured_references(torch):
+    """What this chip sustains on two plain library operations, as context for
+    the published peaks: the best of two large bf16 GEMMs (torch.matmul) and a
+    device copy of 4 GiB (bytes read + written per second)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, work, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return work * reps / (e0.elapsed_time(e1) * 1e-3)
+
+    gemm, shape = 0.0, None
+    for n in (8192, 16384):
+        a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+        b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+        r = rate(lambda: torch.matmul(a, b), 2.0 * n ** 3, 10)
+        if r > gemm:
+            gemm, shape = r, [n, n, n]
+        del a, b
+    src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    copy = rate(lambda: dst.copy_(src), 2.0 * src.numel(), 10)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_tflops": gemm / 1e12, "bf16_gemm_shape": shape, "d2d_copy_gbs": copy / 1e9,
+            "d2d_copy_bytes": 2 * (4 << 30), "source": "torch.matmul and Tensor.copy_"}
+
+
 def time_calls(torch, fns, steps, warmup, M=None):
     """Run the list of zero-argument launches `fns` as one step; returns the
     mean per-step wall time (events around the whole timed region) and the mean
@@ -173,6 +219,7 @@ def time_calls(torch, fns, steps, warmup, M=None):
     end.record()
     torch.cuda.synchronize()
     kernels = M.msa_profile_end() if M is not None else None
+    LAST_STEPS[:] = [ev[i][0].elapsed_time(ev[i][len(fns)]) for i in range(steps)]
     total = start.elapsed_time(end) / steps
     per = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps for j in range(len(fns))]
     if M is not None:
@@ -297,6 +344,7 @@ def main():
         ]
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
     ms_step, (ms_idx, ms_topk, ms_sparse), kern = time_calls(torch, stages, args.steps, args.warmup, M)
+    prefill_steps = step_stats()
     tokens = s.batch * s.n_q
     value = tokens / (ms_step * 1e-3)
     f_idx, f_sp = index_flops(s), sparse_flops(s)
@@ -354,6 +402,8 @@ def main():
         "stages": per_stage,
         "kernels": kernels,
         "end_to_end_mfma_frac": (f_idx + f_sp) / (ms_step * 1e-3) / PEAK_BF16_FLOPS,
+        "ms_per_step_median": prefill_steps["median"],
+        "ms_per_step_min": prefill_steps["min"],
     }
 
     if not args.no_topk_compare and s.block == 128:
@@ -443,6 +493,17 @@ def main():
     del ws, out, lse, bscore, blk, inp
     torch.cuda.empty_cache()
 
+    ref = None
+    if not args.no_reference:
+        ref = measured_references(torch)
+        rl = result["roofline"]
+        rl["frac_of_measured"] = (rl["achieved"] / ref["bf16_gemm_tflops"] if rl["unit"] == "TFLOP/s"
+                                  else rl["achieved"] / ref["d2d_copy_gbs"])
+        result["reference"] = ref
+        log(f"measured references: bf16 GEMM {ref['bf16_gemm_tflops']:.0f} TFLOP/s, "
+            f"device copy {ref['d2d_copy_gbs']:.0f} GB/s; "
+            f"dominant kernel at {rl['frac_of_measured']:.1%} of the measured rate for its bound")
+
     if not args.no_decode:
         did, ds = WORKLOADS[args.decode_workload]
         log(f"decode workload {args.decode_workload}: {ds}")
@@ -458,6 +519,7 @@ def main():
             lambda: M.msa_sparse_decode(ds, dinp["q"], dinp["k"], dinp["v"], dblk, dout, dlse, dws_s),
         ]
         ms_dec, (ms_di, ms_ds) = time_calls(torch, dec_calls, dsteps, args.warmup)
+        dec_steps = step_stats()
         # Per-kernel times from a second pass: event records would weigh on
         # these sub-millisecond steps, so they stay out of the timed one.
         _, _, dkern = time_calls(torch, dec_calls, dsteps, 1, M)
@@ -469,7 +531,10 @@ def main():
                "algorithmic_bytes": by, "hbm_gbs": by / (ms_dec * 1e-3) / 1e9,
                "hbm_frac": by / (ms_dec * 1e-3) / PEAK_HBM_BYTES,
                "kernels": {name: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / dsteps}
-                           for name, (n, tot) in dkern.items()}}
+                           for name, (n, tot) in dkern.items()},
+               "ms_per_step_median": dec_steps["median"], "ms_per_step_min": dec_steps["min"]}
+        if ref:
+            dec["hbm_gbs_over_measured_copy"] = dec["hbm_gbs"] / ref["d2d_copy_gbs"]
         if "index_scores_skinny" in dkern:
             n, tot = dkern["index_scores_skinny"]
             dec["index_scores_skinny_hbm_frac"] = kidx_bytes / (tot / n * 1e-3) / PEAK_HBM_BYTES

@@ -138,18 +138,6 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
-// Streaming stores (non-temporal hint) for data written once and read once by
-// a later kernel: the forward's attention partials and its output.  Measured
-// on the 131,072-token prefill: the sparse stage runs ~1.3 ms faster with them
-// (the backward's dq partials run slower and keep plain stores).
-__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-}
-__device__ __forceinline__ void st8_stream(void* p, float x, float y) {
-  typedef __attribute__((ext_vector_type(2))) float f2;
-  __builtin_nontemporal_store(f2{x, y}, reinterpret_cast<f2*>(p));
-}
-
 // ---------------------------------------------------------------------------
 // One KV block of one K/V head staged in LDS, rows 16-byte aligned and
 // unpadded; 16-byte chunks are XOR-swizzled per row (chunk c of row r sits at

@@ -368,10 +368,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void sparse_kv_outer(
           const f32x4 a0 = acc[ct][pp][0], a1 = acc[ct][pp][1];
           u32x4 o = {pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]), pack_bf16x2(a1[0], a1[1]),
                      pack_bf16x2(a1[2], a1[3])};
-          st16_stream(dst + 32 * pp + 8 * q4, o);
+          st16(dst + 32 * pp + 8 * q4, o);
         }
         // (m, l) is replicated over the column's four lane groups; all store it.
-        st8_stream(part_ml + 2 * cur_c.prow[ct], bmax[ct], bsum[ct]);
+        *reinterpret_cast<float2*>(part_ml + 2 * cur_c.prow[ct]) = make_float2(bmax[ct], bsum[ct]);
       }
       cur_c = nxt_c;
 #pragma unroll
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict
   u32x4 r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-  st16_stream(out + row * D + dl * 8, r);
+  st16(out + row * D + dl * 8, r);
   if (lse && dl == 0) lse[row] = (M + __log2f(L)) * kLn2;
 }
 

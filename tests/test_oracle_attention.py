@@ -93,7 +93,7 @@ def test_sparse_matches_torch_sdpa_on_selection_mask(h_q, h_kv):
 
 
 def test_sparse_equals_dense_when_budget_covers_context():
-    """The benchmark spec self-check: with k*B >= n_kv every causal token is selected."""
+    """With k*B >= n_kv every causal token is selected, so the sparse attention equals dense causal GQA."""
     r = rng(13)
     b, n_q, n_kv, h_q, h_kv, d, d_idx, block = 1, 64, 64, 4, 2, 16, 8, 8
     q, k, v = rand_qkv(r, b, n_q, n_kv, h_q, h_kv, d)

@@ -42,7 +42,9 @@ msa_status check_dims(const msa_dims* p, unsigned need) {
   if ((need & kNeedDIdx) && d.d_idx != 64 && d.d_idx != 128) return MSA_ERR_UNSUPPORTED;
   if (d.n_kv > kMaxKv) return MSA_ERR_UNSUPPORTED;
   if (d.batch > 65535) return MSA_ERR_UNSUPPORTED;
-  if ((int64_t)d.batch * d.n_q * d.h_kv * d.topk >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
+  // CSR entries (one per selected 128-token block of a row: twice k for 256-token blocks) are int32 indices.
+  const int64_t k128 = d.block == 256 ? 2 * (int64_t)d.topk : d.topk;
+  if ((int64_t)d.batch * d.n_q * d.h_kv * k128 >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
   if ((int64_t)d.n_q * d.h_kv > (int64_t(1) << 25)) return MSA_ERR_UNSUPPORTED;
   const int64_t nblk = (d.n_kv + 127) / 128;           // the lists are per 128-token block
   if ((need & kCsr) && (int64_t)d.batch * d.h_kv * nblk >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;

@@ -41,7 +41,8 @@
  *   - Supported: block 128 or 256; 1 <= topk <= 64 (<= 32 with block 256);
  *     d, d_idx in {64, 128};
  *     h_q / h_kv in {1, 2, 4, 8, 16}; n_kv <= 1,048,576; pos0 + n_q <= n_kv;
- *     batch * n_q * h_kv * topk < 2^31.  batch == 0 or n_q == 0 is a no-op.
+ *     batch * n_q * h_kv * topk < 2^31 (2 * topk with block 256);
+ *     n_q * h_kv <= 2^25.  batch == 0 or n_q == 0 is a no-op.
  *   - Block 256 (yhxrc.cn article, "社區沖擊與深層信號": block size and
  *     selection may have to be re-tuned for far longer contexts): a block
  *     of 256 tokens is two of 128, its pooled score the larger of theirs, so

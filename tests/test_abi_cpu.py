@@ -283,3 +283,18 @@ def test_block256_rules():
                                            ctypes.c_float(0.0), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUP
     assert lib.msa_index_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE,
                                   FAKE, FAKE, 1 << 40, None) == UNSUP
+
+
+def test_entry_count_bound_counts_128_token_selections():
+    """The CSR entries of a call (one per selected 128-token block of a
+    (sequence, query, group) row) must fit int32; 256-token blocks select
+    twice as many 128-token blocks as k."""
+    lib = M.lib()
+    big = dict(batch=2, n_q=1 << 20, n_kv=1 << 20, pos0=0, h_q=16, h_kv=16, d=64, d_idx=64)
+    ok256 = dims(block=256, topk=31, **big)                 # 2 * 2^20 * 16 * 62 < 2^31
+    over256 = dims(block=256, topk=32, **big)               # 2 * 2^20 * 16 * 64 = 2^31
+    assert lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(ok256)) > 0
+    assert lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(over256)) == 0
+    assert prefill_call(over256) == UNSUP
+    over128 = dims(block=128, topk=64, **big)               # the same count on 128-token blocks
+    assert lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(over128)) == 0

@@ -376,12 +376,19 @@ def main():
     bound, work, peak, scale, unit = algorithmic[dom_name]
     avg = kernels[dom_name]["avg_ms"]
     achieved = work / (avg * 1e-3)
+    traffic = measured_traffic(dom_name, args.workload)
     roofline = {"kernel": dom_name, "bound": bound, "achieved": achieved / scale, "peak": peak / scale,
                 "unit": unit, "frac": achieved / peak,
-                "traffic": measured_traffic(dom_name, args.workload),
+                "traffic": traffic,
                 "algorithmic_per_launch": work, "avg_launch_ms": avg}
+    if traffic is not None:
+        # The same launch priced by the HBM bytes it moves (from the committed counters).
+        roofline["traffic_gbs"] = traffic / (avg * 1e-3) / 1e9
+        roofline["traffic_frac_of_hbm_peak"] = traffic / (avg * 1e-3) / PEAK_HBM_BYTES
     log(f"dominant kernel {dom_name}: {avg:.3f} ms per launch, {achieved / scale:.1f} {unit} "
-        f"({achieved / peak:.1%} of peak)")
+        f"({achieved / peak:.1%} of peak)" + (f"; moves {traffic / 1e9:.1f} GB of HBM traffic = "
+                                              f"{roofline['traffic_frac_of_hbm_peak']:.1%} of HBM peak"
+                                              if traffic is not None else ""))
 
     result = {
         "metric": METRIC,

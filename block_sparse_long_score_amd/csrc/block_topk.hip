@@ -31,9 +31,8 @@ namespace {
 constexpr int kRowsPerWg = 4;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;                       // -0 ties with +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // finite keys are >= 0x007fffff
+  const uint32_t u = __float_as_uint(f + 0.0f);        // -0 + 0 = +0: -0 ties with +0
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);   // negative: ~u, else u | sign; finite keys >= 0x007fffff
 }
 
 // Largest T with #{lanes : x >= T} >= kk  (= the kk-th largest x).

@@ -187,6 +187,30 @@ def test_block_topk_entry_matches_oracle_selection():
                 assert (got[b, t, gg] == want).all(), (b, t, gg)
 
 
+@pytest.mark.parametrize("s", [Shape(1, 200, 20000, 19800, 8, 2, 128, 128, topk=16),
+                               Shape(1, 64, 1048576, 1048512, 8, 2, 128, 128, topk=16)])
+def test_block_topk_signed_zeros_and_denormals(s):
+    """Pooled scores drawn from -0, +0, subnormals of both signs, the smallest
+    normal and large magnitudes: -0 ties with +0 (ties go to the lower block)
+    and subnormals keep their order, for the per-wave rows and the
+    per-workgroup long rows."""
+    special = np.array([-0.0, 0.0, 1e-40, -1e-40, 1.4e-45, -1.4e-45, 1.1754944e-38, -1.1754944e-38, 1.0, -1.0,
+                        3e38, -3e38], dtype=np.float32)
+    rng = np.random.default_rng(5)
+    sc32 = special[rng.integers(0, len(special), size=(s.batch, s.n_q, s.h_kv, s.nblk))]
+    bscore = torch.from_numpy(sc32).cuda()
+    blk = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.int32, device="cuda")
+    from block_sparse_long_score_amd import msa as M
+    M.msa_block_topk(s, bscore, blk)
+    got = blk.cpu().numpy()
+    sc = sc32.astype(np.float64)
+    for t in range(s.n_q):
+        jl = (s.pos0 + t) // s.block
+        for gg in range(s.h_kv):
+            want = O.select_blocks(sc[0, t, gg, : jl + 1], jl, s.topk)
+            assert (got[0, t, gg] == want).all(), (t, gg)
+
+
 @pytest.mark.parametrize("jl_span,topk", [((1048000, 1048575), 16), ((300000, 300127), 32), ((1040000, 1040200), 1),
                                           ((900000, 900100), 64)])
 def test_block_topk_long_rows_workgroup_path(jl_span, topk):

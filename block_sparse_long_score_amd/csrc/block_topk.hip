@@ -143,18 +143,29 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* 
   if (row0 >= nrows) return;
   const int64_t row_end = min(row0 + (int64_t)kRowsPerWave, nrows);
   const int kk = topk - 1;
-  // Candidates of a row: blocks 0 .. jl-1 (0 when the row keeps all its blocks).
-  auto local_block = [&](int64_t row) {
-    const int64_t bt = row / h_kv;
-    return (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + (int)(bt % n_q)) >> lb;
+  // (sequence, token) of a row, found once for the wave's first row and then
+  // stepped row by row (wave-uniform; rows are (b * n_q + t) * h_kv + g).
+  int rb, rt, rg;
+  {
+    const int64_t bt = row0 / h_kv;
+    rg = (int)(row0 - bt * h_kv);
+    rb = (int)(bt / n_q);
+    rt = (int)(bt - (int64_t)rb * n_q);
+  }
+  auto step = [&](int& b, int& t, int& g) {
+    if (++g == h_kv) {
+      g = 0;
+      if (++t == n_q) {
+        t = 0;
+        ++b;
+      }
+    }
   };
-  auto n_cand = [&](int64_t row) {
-    const int jl = local_block(row);
-    return jl + 1 <= topk ? 0 : jl;
-  };
-  auto load = [&](int64_t row, float (&f)[V]) {
+  // Local block of a row; its candidates are blocks 0 .. jl-1 (none when the row keeps all its blocks).
+  auto local_block = [&](int b, int t) { return (seq_pos0(seq_len, b, pos0, n_q, n_kv) + t) >> lb; };
+  auto load = [&](int64_t row, int jl, float (&f)[V]) {
     const float* sc = bscore + row * nblk;
-    const int n = n_cand(row);
+    const int n = jl + 1 <= topk ? 0 : jl;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const int e = i * 64 + lane;
@@ -162,11 +173,16 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* 
     }
   };
   float cur[V], nxt[V];
-  load(row0, cur);
+  int jl_next = local_block(rb, rt);
+  load(row0, jl_next, cur);
 #pragma unroll 1
   for (int64_t row = row0; row < row_end; ++row) {
-    if (row + 1 < row_end) load(row + 1, nxt);
-    const int jl = local_block(row);
+    const int jl = jl_next;
+    if (row + 1 < row_end) {                           // wave-uniform; the last row has no successor to look up
+      step(rb, rt, rg);
+      jl_next = local_block(rb, rt);
+      load(row + 1, jl_next, nxt);
+    }
     int32_t* out = blk + row * topk;
     if (jl + 1 <= topk) {
       for (int i = lane; i < topk; i += 64) out[i] = (i <= jl) ? i : -1;

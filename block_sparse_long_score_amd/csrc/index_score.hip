@@ -108,7 +108,7 @@ __device__ __forceinline__ void tiled_segment(IndexSmem<DI>& sm, const uint16_t*
   const int64_t r_end = min(r0 + (int64_t)kTiledRows, nrows);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave index is uniform
   const int half = lane >> 5, r32 = lane & 31;
 
   // This wave's columns: rows rw0 + 32*ct + r32.
@@ -132,7 +132,6 @@ __device__ __forceinline__ void tiled_segment(IndexSmem<DI>& sm, const uint16_t*
       qb[ct][kc] = valid ? ld16(qr + kc * 16 + half * 8) : u32x4{0u, 0u, 0u, 0u};
   }
   float* const orow = sm.o + (wave * kTiledColsPerWave + r32) * Smem::OS;   // + ct*32*OS
-  float* const grow = bscore + ((int64_t)b * nrows + rw0 + r32) * nblk;      // + ct*32*nblk
 
   // Key block staging: item i of this thread is key row key0 + i * KSTEP.
   constexpr int CHUNKS = kBlock * DI / 8;
@@ -180,20 +179,41 @@ __device__ __forceinline__ void tiled_segment(IndexSmem<DI>& sm, const uint16_t*
     // The next key block goes to LDS before any pooled stores are issued, so
     // the wait for its loads never includes the stores of a write-out.
     if (j + 1 < je) stash(sm.k[cur ^ 1]);
-    // Write out a full group (or the last one): lane half h writes entries
-    // jf + 8h .. jf + 8h + 7 of its rows, skipping blocks past the row's own.
+    // Write out a full group (or the last one) row-contiguously: lane l takes
+    // entry jf + (l & 15) of rows 4i + (l >> 4), so each store instruction
+    // covers 4 rows x 16 consecutive blocks (four 64-byte runs) instead of 64
+    // rows x 4 bytes.  Blocks past a row's own, and rows past the tile, are
+    // skipped; the per-row test is needed only once the group reaches the
+    // wave's earliest own block.
     if (live && (j - jf == kFlush - 1 || j == je - 1 || j == jw_max)) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int n = j - jf + 1;
+      const int e = lane & 15, rsub = lane >> 4;
+      const int nrw = (int)min((int64_t)kTiledColsPerWave, r_end - rw0);
+      const bool all_causal = j <= (pos0 + tw0) / kBlock;
+      // Wave-uniform bases with 32-bit byte offsets (a wave's rows span at
+      // most 128 x 8192 entries); each pass issues its 4 LDS reads before its
+      // 4 stores.
+      const float* ow = sm.o + wave * kTiledColsPerWave * Smem::OS;
+      char* gw = reinterpret_cast<char*>(bscore + ((int64_t)b * nrows + rw0) * nblk + jf);
+      if (e < n) {
+#pragma unroll 1
+        for (int i0 = 0; i0 < kTiledColsPerWave / 4; i0 += 4) {
+          float v[4];
+          bool ok[4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int jl = plim[ct] >= 0 ? plim[ct] / kBlock : -1;
+          for (int u = 0; u < 4; ++u) {
+            const int c = 4 * (i0 + u) + rsub;
+            ok[u] = c < nrw && (all_causal || jf + e <= (pos0 + ((int)rw0 + c) / h_kv) / kBlock);   // rows < 2^25
+            v[u] = ow[c * Smem::OS + e];
+          }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jj = half * 8 + e;
-          if (jj < n && jf + jj <= jl) grow[(int64_t)ct * 32 * nblk + jf + jj] = orow[ct * 32 * Smem::OS + jj];
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t off = (uint32_t)((4 * (i0 + u) + rsub) * nblk + e) * 4u;
+            if (ok[u]) *reinterpret_cast<float*>(gw + off) = v[u];
+          }
         }
       }
       jf = j + 1;

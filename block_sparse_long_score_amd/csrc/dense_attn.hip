@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void dense_decode_chunks(
     uint16_t* __restrict__ part_o, float* __restrict__ part_ml, int n_kv, int pos0, int h_q, int h_kv, int nsplit,
     int64_t units, float sl2) {
   __shared__ float pt[kThreads / 64][kBlock * 16 + 16];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t unit = (int64_t)blockIdx.x * (kThreads / 64) + wave;   // (b, g, chunk)
   if (unit >= units) return;
   const int split = (int)(unit % nsplit);

@@ -174,6 +174,7 @@ const char* msa_status_str(msa_status s) {
     case MSA_ERR_ALIGN: return "MSA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
     case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE: workspace missing or too small";
     case MSA_ERR_HIP: return "MSA_ERR_HIP: a kernel launch failed";
+    case MSA_ERR_TOO_LARGE: return "MSA_ERR_TOO_LARGE: the call needs more than the library's static scratch";
   }
   return "unknown msa_status";
 }
@@ -189,6 +190,20 @@ msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uin
   if (!workspace || workspace_bytes < index_ws_bytes(d)) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
   return hip_status(run_index_topk(d, q_idx, k_idx, blk_idx, workspace, static_cast<hipStream_t>(stream)));
+}
+
+msa_status msa_index_topk_noalloc(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
+                                  int32_t* blk_idx, msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_INDEX_TOPK));
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  if (!q_idx || !k_idx || !blk_idx) return MSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(k_idx) || misaligned(blk_idx)) return MSA_ERR_ALIGN;
+  const Dims d = to_dims(*dims);
+  if (index_ws_bytes(d) > msa::kScratchBytes) return MSA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (msa::scratch_for_current_device(&ws) != hipSuccess) return MSA_ERR_HIP;
+  return hip_status(run_index_topk(d, q_idx, k_idx, blk_idx, ws, static_cast<hipStream_t>(stream)));
 }
 
 msa_status msa_index_scores(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,

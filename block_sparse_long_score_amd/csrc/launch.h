@@ -97,4 +97,9 @@ hipError_t launch_dense_decode(const Dims& d, const uint16_t* q, const uint16_t*
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The library's own device scratch (msa_index_topk_noalloc): kScratchBytes per
+// device, in the code object; its device address on the current device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_for_current_device(void** ptr);
+
 }  // namespace msa

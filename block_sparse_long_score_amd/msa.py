@@ -32,6 +32,7 @@ STATUS = {
     4: "MSA_ERR_ALIGN",
     5: "MSA_ERR_WORKSPACE",
     6: "MSA_ERR_HIP",
+    7: "MSA_ERR_TOO_LARGE",
 }
 
 EXPORTED = (
@@ -52,6 +53,7 @@ EXPORTED = (
     "msa_sparse_prefill_target",
     "msa_sparse_prefill_backward",
     "msa_index_backward",
+    "msa_index_topk_noalloc",
 )
 
 
@@ -93,6 +95,7 @@ def lib() -> ctypes.CDLL:
     L.msa_status_str.argtypes = [I32]
     L.msa_status_str.restype = ctypes.c_char_p
     L.msa_index_topk.argtypes = [D, P, P, P, P, S, VP]
+    L.msa_index_topk_noalloc.argtypes = [D, P, P, P, VP]
     L.msa_index_scores.argtypes = [D, P, P, P, VP]
     L.msa_block_topk.argtypes = [D, P, P, VP]
     L.msa_sparse_prefill.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
@@ -170,6 +173,16 @@ def msa_index_topk(s: Shape, q_idx, k_idx, blk_idx, workspace, stream=None) -> N
     wp, wb = _ws(workspace)
     st = lib().msa_index_topk(ctypes.byref(d), _ptr(q_idx), _ptr(k_idx), _ptr(blk_idx), wp, wb, _stream(stream))
     _raise(st, "msa_index_topk")
+
+
+def msa_index_topk_noalloc(s: Shape, q_idx, k_idx, blk_idx, stream=None) -> None:
+    """msa_index_topk on the library's own scratch (no workspace argument)."""
+    _check(q_idx, "q_idx", torch.bfloat16, (s.batch, s.n_q, s.h_kv, s.d_idx))
+    _check(k_idx, "k_idx", torch.bfloat16, (s.batch, s.n_kv, s.d_idx))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, s.n_q, s.h_kv, s.topk))
+    d = dims_of(s)
+    st = lib().msa_index_topk_noalloc(ctypes.byref(d), _ptr(q_idx), _ptr(k_idx), _ptr(blk_idx), _stream(stream))
+    _raise(st, "msa_index_topk_noalloc")
 
 
 def msa_index_scores(s: Shape, q_idx, k_idx, bscore, stream=None) -> None:

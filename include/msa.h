@@ -36,8 +36,10 @@
  *     status; no exception crosses the ABI.  MSA_ERR_HIP reports a launch
  *     failure; faults inside kernels surface at the caller's next
  *     synchronisation.  Inputs are never written.  Same inputs, same outputs,
- *     bit for bit (no floating-point atomics).  Functions are stateless and
- *     thread-safe.
+ *     bit for bit (no floating-point atomics).  Functions keep no state
+ *     between calls and are thread-safe, with two documented exceptions:
+ *     msa_index_topk_noalloc (one shared scratch array per GPU) and the
+ *     kernel-timing hook (msa_profile_begin / msa_profile_end).
  *   - Supported: block 128 or 256; 1 <= topk <= 64 (<= 32 with block 256);
  *     d, d_idx in {64, 128};
  *     h_q / h_kv in {1, 2, 4, 8, 16}; n_kv <= 1,048,576; pos0 + n_q <= n_kv;
@@ -85,7 +87,8 @@ typedef enum msa_status {
   MSA_ERR_UNSUPPORTED = 3, /* sizes this build does not implement (see the list above) */
   MSA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   MSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than msa_workspace_size() */
-  MSA_ERR_HIP = 6          /* a kernel launch failed */
+  MSA_ERR_HIP = 6,         /* a kernel launch failed */
+  MSA_ERR_TOO_LARGE = 7    /* msa_index_topk_noalloc: more than the library's static scratch */
 } msa_status;
 
 typedef enum msa_op {
@@ -121,6 +124,25 @@ const char* msa_status_str(msa_status status);
  * <= 3 and d_idx <= 128 they are exact. */
 msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
                           int32_t* blk_idx, void* workspace, size_t workspace_bytes, msa_stream stream);
+
+/* msa_index_topk without a workspace argument, for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments (minus the
+ * workspace), same checks and the same blk_idx, bit for bit.  The pooled
+ * scores go to a scratch array of 64 MiB that the library keeps in its code
+ * object: every GPU the library runs on holds its own copy from the first use
+ * until the process ends.  The call itself allocates nothing.
+ *   - Returns MSA_ERR_TOO_LARGE when the call needs more than 64 MiB, i.e.
+ *     msa_workspace_size(MSA_OP_INDEX_TOPK, dims) > 64 << 20 (for example
+ *     batch * n_q * h_kv * nblk > 16,777,216 with 128-token blocks).
+ *   - Every call on one GPU uses that GPU's single array, which keeps the last
+ *     call's contents: calls whose work overlaps on one GPU (other streams,
+ *     other threads) race and give undefined results.  Calls ordered on one
+ *     stream are safe.
+ *   - The first call on a device looks up the array's device address
+ *     (MSA_ERR_HIP if that fails). */
+msa_status msa_index_topk_noalloc(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
+                                  int32_t* blk_idx, msa_stream stream);
 
 /* Scoring and block max-pool alone (the first half of msa_index_topk), for
  * callers that want the pooled scores themselves.

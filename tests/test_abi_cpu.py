@@ -298,3 +298,19 @@ def test_entry_count_bound_counts_128_token_selections():
     assert prefill_call(over256) == UNSUP
     over128 = dims(block=128, topk=64, **big)               # the same count on 128-token blocks
     assert lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(over128)) == 0
+
+
+def test_noalloc_index_topk_host_checks():
+    """The allocation-free index top-k validates like msa_index_topk and
+    rejects a call larger than its 64 MiB scratch before any HIP call."""
+    call = lambda d, q=FAKE, k=FAKE, blk=FAKE: M.lib().msa_index_topk_noalloc(
+        ctypes.byref(d) if d is not None else None, q, k, blk, None)
+    assert call(None) == NULL
+    assert call(dims(), q=None) == NULL
+    assert call(dims(), blk=ODD) == ALIGN
+    assert call(dims(h_q=6, h_kv=4)) == SHAPE
+    assert call(dims(d_idx=96)) == UNSUP
+    assert call(dims(batch=0)) == OK
+    # 2 * 2048 * 8 * 1024 fp32 pooled scores = 128 MiB
+    assert call(dims(batch=2, n_q=2048, n_kv=131072, pos0=129024, h_q=64, h_kv=8)) == 7
+    assert M.STATUS[7] == "MSA_ERR_TOO_LARGE"

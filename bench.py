@@ -14,8 +14,13 @@ index scoring + block max-pool (msa_index_scores), exponential-free top-k
     over its measured average duration),
   * the decode leg (1M-token caches, batch 8: index top-k + sparse decode),
   * the library's own dense causal GQA on the same inputs (speedup),
-  * the top-k kernel against torch.topk on the same pooled scores,
-  * `cpu_baseline`: the fp64 oracle timed on a bounded sample of the workload.
+  * the top-k kernel against torch.topk on the same candidates, and the top-k
+    alone on 1,048,576 full rows of 1,023 candidates against torch.topk and
+    torch.sort on the same rows,
+  * the other configurations: 32K prefill and the 8,192-query prefill chunk at
+    1M (each with the dense comparison), decode of 64 sequences at 256K,
+  * `cpu_baseline`: the fp64 oracle timed on a bounded sample of the workload,
+    with the host's CPU count and model.
 All progress goes to stderr; stdout gets exactly one JSON line.
 """
 
@@ -51,6 +56,10 @@ def parse():
                     help="skip the whole 1M-token chunked prefill leg")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-topk-compare", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations' legs (32K prefill, the 1M prefill chunk, 256K x 64 decode)")
+    ap.add_argument("--no-topk-full", action="store_true",
+                    help="skip the top-k alone on full 1,024-candidate rows against torch.topk and torch.sort")
     ap.add_argument("--no-target", action="store_true", help="skip the index-branch target (KL) leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the main-branch and index-branch backward legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -229,6 +238,20 @@ def time_calls(torch, fns, steps, warmup, M=None):
 
 # ------------------------------------------------------------ CPU baseline --
 
+def host_cpu():
+    """The host the oracle runs on: logical CPU count and CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "cpu_model": model}
+
+
 def cpu_baseline(s, inp, seconds, seed=99):
     """The fp64 oracle, as it stands, on a seeded sample of query rows of the
     same workload: all groups' index scoring, pooling and selection, then all
@@ -263,8 +286,143 @@ def cpu_baseline(s, inp, seconds, seed=99):
             break
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "host": host_cpu(),
             "sample": f"{done} query rows drawn uniformly (seed {seed}) from the {s.n_q}-token prefill, "
                       f"all {s.h_kv} groups and {s.h_q} heads each, {el:.1f} s on the host"}
+
+
+# ------------------------------------------------------ other configurations --
+
+def prefill_config_leg(torch, M, name, steps, warmup, dense_reps=2):
+    """One step of the prefill hot path (index scores, top-k, sparse prefill)
+    on another configuration's inputs, with the library's dense GQA on the
+    same inputs."""
+    from block_sparse_long_score_amd.inputs import WORKLOADS, make_inputs
+    cid, s = WORKLOADS[name]
+    log(f"prefill leg {name}: {s}")
+    inp = make_inputs(s, cid, device="cuda")
+    bscore = torch.empty((s.batch, s.n_q, s.h_kv, s.nblk), dtype=torch.float32, device="cuda")
+    blk = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((s.batch, s.n_q, s.h_q), dtype=torch.float32, device="cuda")
+    ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
+    stages = [
+        lambda: M.msa_index_scores(s, inp["q_idx"], inp["k_idx"], bscore),
+        lambda: M.msa_block_topk(s, bscore, blk),
+        lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
+    ]
+    ms, (mi, mt, msp) = time_calls(torch, stages, steps, warmup)
+    st = step_stats()
+    fi, fsp = index_flops(s), sparse_flops(s)
+    tokens = s.batch * s.n_q
+    leg = {"workload": name, "n_q": s.n_q, "n_kv": s.n_kv, "pos0": s.pos0, "steps": steps,
+           "ms_per_step": ms, "ms_per_step_median": st["median"], "ms_per_step_min": st["min"],
+           "tok_s": tokens / (ms * 1e-3), "algorithmic_flops": fi + fsp,
+           "end_to_end_mfma_frac": (fi + fsp) / (ms * 1e-3) / PEAK_BF16_FLOPS,
+           "stages_ms": {"index_scores": mi, "block_topk": mt, "sparse_prefill": msp},
+           "index_scores_mfma_frac": fi / (mi * 1e-3) / PEAK_BF16_FLOPS,
+           "block_topk_hbm_frac": topk_bytes(s) / (mt * 1e-3) / PEAK_HBM_BYTES,
+           "sparse_prefill_mfma_frac": fsp / (msp * 1e-3) / PEAK_BF16_FLOPS}
+    log(f"{name}: step {ms:.3f} ms (index {mi:.3f}, top-k {mt:.3f}, sparse {msp:.3f}) -> "
+        f"{leg['tok_s']:.4g} tok/s, {leg['end_to_end_mfma_frac']:.1%} of MFMA peak")
+    if dense_reps:
+        ms_d, _ = time_calls(torch, [lambda: M.msa_dense_gqa(s, inp["q"], inp["k"], inp["v"], out, lse)],
+                             dense_reps, 1)
+        fd = dense_flops(s)
+        leg["dense_gqa"] = {"ms": ms_d, "mfma_frac": fd / (ms_d * 1e-3) / PEAK_BF16_FLOPS,
+                            "msa_speedup": ms_d / ms}
+        log(f"{name}: dense GQA {ms_d:.2f} ms ({leg['dense_gqa']['mfma_frac']:.1%} of MFMA peak) -> "
+            f"MSA {ms_d / ms:.2f}x faster")
+    del inp, bscore, blk, out, lse, ws
+    torch.cuda.empty_cache()
+    return leg
+
+
+def decode_config_leg(torch, M, name, steps, warmup, dense_reps=3):
+    """One decode step (index top-k + sparse decode) on another
+    configuration's inputs, with the library's dense decode beside it."""
+    from block_sparse_long_score_amd.inputs import WORKLOADS, make_inputs
+    cid, s = WORKLOADS[name]
+    log(f"decode leg {name}: {s}")
+    inp = make_inputs(s, cid, device="cuda")
+    ws_i = M.alloc_workspace(M.MSA_OP_INDEX_TOPK, s)
+    ws_s = M.alloc_workspace(M.MSA_OP_SPARSE_DECODE, s)
+    blk = torch.empty((s.batch, 1, s.h_kv, s.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((s.batch, 1, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((s.batch, 1, s.h_q), dtype=torch.float32, device="cuda")
+    calls = [
+        lambda: M.msa_index_topk(s, inp["q_idx"], inp["k_idx"], blk, ws_i),
+        lambda: M.msa_sparse_decode(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws_s),
+    ]
+    ms, (mi, msd) = time_calls(torch, calls, steps, warmup)
+    st = step_stats()
+    _, _, kern = time_calls(torch, calls, steps, 1, M)
+    by = decode_bytes(s)
+    leg = {"workload": name, "batch": s.batch, "n_kv": s.n_kv, "steps": steps,
+           "ms_per_step": ms, "ms_per_step_median": st["median"], "ms_per_step_min": st["min"],
+           "tok_s": s.batch / (ms * 1e-3), "algorithmic_bytes": by,
+           "hbm_gbs": by / (ms * 1e-3) / 1e9, "hbm_frac": by / (ms * 1e-3) / PEAK_HBM_BYTES,
+           "index_topk_ms": mi, "sparse_decode_ms": msd,
+           "kernels": {n: {"launches": c, "avg_ms": t / c} for n, (c, t) in kern.items()}}
+    log(f"{name}: step {ms:.3f} ms -> {leg['tok_s']:.4g} tok/s, {leg['hbm_frac']:.1%} of HBM peak")
+    if dense_reps:
+        dws = M.alloc_workspace(M.MSA_OP_DENSE_GQA, s)
+        ms_d, _ = time_calls(torch, [lambda: M.msa_dense_gqa(s, inp["q"], inp["k"], inp["v"], out, lse, dws)],
+                             dense_reps, 1)
+        kv = float(s.batch * s.n_kv * s.h_kv * s.d * 2 * 2)
+        leg["dense_gqa"] = {"ms": ms_d, "kv_bytes": kv, "hbm_frac": kv / (ms_d * 1e-3) / PEAK_HBM_BYTES,
+                            "msa_speedup": ms_d / ms}
+        log(f"{name}: dense decode {ms_d:.3f} ms -> MSA {ms_d / ms:.2f}x faster")
+        del dws
+    del inp, ws_i, ws_s, blk, out, lse
+    torch.cuda.empty_cache()
+    return leg
+
+
+# The top-k alone on full rows: 1,048,576 (query, group) rows whose local block
+# is 1023, so each row has 1,023 candidate blocks (blocks 0..1022) in a
+# 1,024-wide row: 1,024 sequences x 128 queries at positions 130,944..131,071
+# x 8 groups.  Pooled scores are integers drawn uniformly from [80, 170] (the
+# central range of the 128K workload's pooled scores: 1st-99th percentile
+# 81-170), so ties are as frequent as in real rows.
+TOPK_FULL_SHAPE = dict(batch=1024, n_q=128, n_kv=131072, pos0=130944, h_q=64, h_kv=8, d=128, d_idx=128)
+TOPK_FULL_SEED = 3099
+
+
+def topk_full_scores(torch, s, device="cuda"):
+    """The full-row top-k leg's pooled scores; column 1023 (every row's local
+    block, never a candidate) is -inf so a library top-k over the whole row
+    makes the same choice as msa_block_topk over its 1,023 candidates."""
+    g = torch.Generator(device=device)
+    g.manual_seed(TOPK_FULL_SEED)
+    sc = torch.randint(80, 171, (s.batch, s.n_q, s.h_kv, s.nblk), generator=g, dtype=torch.float32, device=device)
+    sc[..., s.nblk - 1] = -math.inf
+    return sc
+
+
+def topk_full_leg(torch, M, steps):
+    from block_sparse_long_score_amd.inputs import Shape
+    s = Shape(**TOPK_FULL_SHAPE)
+    log(f"top-k alone on full rows: {s}")
+    sc = topk_full_scores(torch, s)
+    blk = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.int32, device="cuda")
+    ms_msa, _ = time_calls(torch, [lambda: M.msa_block_topk(s, sc, blk)], steps, 1)
+    ms_topk, _ = time_calls(torch, [lambda: torch.topk(sc, s.topk - 1, dim=-1)], 3, 1)
+    ms_sort, _ = time_calls(torch, [lambda: torch.sort(sc, dim=-1, descending=True, stable=True)], 3, 1)
+    by = topk_bytes(s)
+    rows = s.batch * s.n_q * s.h_kv
+    leg = {"rows": rows, "candidates_per_row": s.nblk - 1, "row_entries": s.nblk, "algorithmic_bytes": by,
+           "msa_block_topk_ms": ms_msa, "hbm_gbs": by / (ms_msa * 1e-3) / 1e9,
+           "hbm_frac": by / (ms_msa * 1e-3) / PEAK_HBM_BYTES,
+           "torch_topk_ms": ms_topk, "torch_sort_stable_ms": ms_sort,
+           "speedup_vs_torch_topk": ms_topk / ms_msa, "speedup_vs_torch_sort": ms_sort / ms_msa,
+           "note": "same 1,024-wide rows for all three (the local-block column is -inf); torch.topk takes k-1 "
+                   "per row, torch.sort (stable, descending) orders whole rows; timing only"}
+    log(f"top-k full rows: msa {ms_msa:.3f} ms ({leg['hbm_frac']:.1%} of HBM peak), torch.topk {ms_topk:.3f} ms, "
+        f"torch.sort {ms_sort:.3f} ms")
+    del sc, blk
+    torch.cuda.empty_cache()
+    return leg
 
 
 # -------------------------------------------------------------------- main --
@@ -414,11 +572,22 @@ def main():
     }
 
     if not args.no_topk_compare and s.block == 128:
-        vals = bscore[..., : s.nblk]
+        # torch.topk on the same candidates: entries at and past each row's
+        # local block are set to -inf in a copy, so the library top-k makes
+        # the same choice; torch.topk still reads every row entry (4 GiB at
+        # 128K) where msa_block_topk reads only the candidates (2 GiB).
+        vals = bscore.clone()
+        jl = (s.pos0 + torch.arange(s.n_q, device=dev)) // s.block
+        col = torch.arange(s.nblk, device=dev)
+        vals.masked_fill_((col[None, :] >= jl[:, None])[None, :, None, :], -math.inf)
         ms_torch, _ = time_calls(torch, [lambda: torch.topk(vals, s.topk - 1, dim=-1)], 3, 1)
+        del vals
         result["topk_vs_torch"] = {"msa_block_topk_ms": ms_topk, "torch_topk_ms": ms_torch,
                                    "speedup": ms_torch / ms_topk,
-                                   "note": "torch.topk over the full pooled rows, k-1 per row; timing only"}
+                                   "msa_bytes": topk_bytes(s), "torch_bytes": float(bscore.numel() * 4),
+                                   "note": "same candidates (torch's copy has -inf at and past each row's local "
+                                           "block); torch.topk reads whole rows, msa only the candidates; the "
+                                           "equal-work comparison is the topk_full_rows leg"}
         log(f"top-k: msa {ms_topk:.3f} ms vs torch.topk {ms_torch:.3f} ms")
 
     if not args.no_target and s.block == 128:
@@ -579,10 +748,21 @@ def main():
         log(f"varlen decode {ms_vl:.3f} ms over lengths {lens} -> "
             f"{result['decode_varlen']['hbm_frac'] * 100:.1f}% of HBM peak")
 
+    if not args.no_decode:
+        del dinp, dws_i, dws_s, dblk, dout, dlse
+        torch.cuda.empty_cache()
+
+    if not args.no_configs:
+        result["configs"] = {
+            "prefill_32k": prefill_config_leg(torch, M, "prefill_32k", args.steps, args.warmup),
+            "prefill_chunk_1m": prefill_config_leg(torch, M, "prefill_chunk_1m", args.steps, args.warmup),
+            "decode_256k_b64": decode_config_leg(torch, M, "decode_256k_b64", max(args.steps, 20), args.warmup),
+        }
+
+    if not args.no_topk_full:
+        result["topk_full_rows"] = topk_full_leg(torch, M, max(args.steps, 5))
+
     if not args.no_prefill_1m:
-        if not args.no_decode:
-            del dinp, dws_i, dws_s, dblk, dout, dlse
-            torch.cuda.empty_cache()
         # A whole 1M-token prefill, chunk by chunk (index branch + sparse
         # attention per 8,192 queries over the growing causal range).
         fid, fs = WORKLOADS["prefill_1m_full"]

@@ -24,29 +24,31 @@ struct Record {
 
 constexpr size_t kPoolEvents = 4096;      // created up front, so recording stays cheap
 
+// g_pool, g_next, g_extra and g_records are only touched with g_mu held, so
+// launches on other threads may overlap msa_profile_begin / msa_profile_end.
 std::atomic<bool> g_on{false};
 std::mutex g_mu;
 std::vector<Record> g_records;
 std::vector<hipEvent_t> g_pool;           // created by msa_profile_begin
-std::atomic<size_t> g_next{0};
+size_t g_next = 0;
 std::vector<hipEvent_t> g_extra;          // created on demand once the pool is used up
 
 hipEvent_t take_event() {
-  const size_t i = g_next.fetch_add(1, std::memory_order_relaxed);
-  if (i < g_pool.size()) return g_pool[i];
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_next < g_pool.size()) return g_pool[g_next++];
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lock(g_mu);
   g_extra.push_back(e);
   return e;
 }
 
-void release_events() {
+// Caller holds g_mu.
+void release_events_locked() {
   for (hipEvent_t e : g_pool) (void)hipEventDestroy(e);
   for (hipEvent_t e : g_extra) (void)hipEventDestroy(e);
   g_pool.clear();
   g_extra.clear();
-  g_next.store(0, std::memory_order_relaxed);
+  g_next = 0;
 }
 
 }  // namespace
@@ -86,16 +88,14 @@ extern "C" {
 
 msa_status msa_profile_begin(void) {
   msa::g_on.store(false, std::memory_order_release);
-  {
-    std::lock_guard<std::mutex> lock(msa::g_mu);
-    msa::g_records.clear();
-  }
-  msa::release_events();
+  std::lock_guard<std::mutex> lock(msa::g_mu);
+  msa::g_records.clear();
+  msa::release_events_locked();
   msa::g_pool.reserve(msa::kPoolEvents);
   for (size_t i = 0; i < msa::kPoolEvents; ++i) {
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) {
-      msa::release_events();
+      msa::release_events_locked();
       return MSA_ERR_HIP;
     }
     msa::g_pool.push_back(e);
@@ -123,7 +123,10 @@ msa_status msa_profile_end(msa_kernel_time* out, int32_t capacity, int32_t* coun
       a.second += ms;
     }
   }
-  msa::release_events();
+  {
+    std::lock_guard<std::mutex> lock(msa::g_mu);
+    msa::release_events_locked();
+  }
   if (!count) return MSA_ERR_NULL;
   if (!ok) return MSA_ERR_HIP;
   std::vector<std::pair<std::string, std::pair<int32_t, double>>> v(agg.begin(), agg.end());

@@ -323,8 +323,9 @@ msa_status msa_dense_gqa(const msa_dims* dims, const uint16_t* q, const uint16_t
  * 4096 HIP events on the host (no device memory; more are created if a run
  * records over 2048 launches) and returns MSA_ERR_HIP if it cannot; recording
  * adds two event records to the stream per launch, so leave it off outside
- * measurements.  Not thread-safe against concurrent begin/end calls; launches
- * from several threads are recorded safely.
+ * measurements.  Launches from several threads are recorded safely, also while
+ * another thread calls msa_profile_begin or msa_profile_end (the event pool is
+ * guarded by a mutex); two begin/end calls must not overlap each other.
  *   out       array of `capacity` entries, filled with the kernels in order of
  *             decreasing total time (may be NULL when capacity is 0)
  *   count     out: number of distinct kernels recorded (may exceed capacity)

@@ -28,41 +28,68 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+# Outputs are views into larger buffers whose every element starts as a
+# sentinel: NaN for the float outputs, -7 (never a block index or padding) for
+# the selections.  After a call, the guard bands on both sides must still hold
+# the sentinel bit for bit, and no sentinel may survive inside the output.
+GUARD = 4096
+_SENTINEL = {torch.bfloat16: float("nan"), torch.float32: float("nan"), torch.int32: -7}
+_BITS = {torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.int32: torch.int32}
+
+
+class Guarded:
+    def __init__(self, shape, dtype):
+        self.n = int(np.prod(shape))
+        self.dtype = dtype
+        self.buf = torch.full((self.n + 2 * GUARD,), _SENTINEL[dtype], dtype=dtype, device="cuda")
+        self.sentinel_bits = self.buf[:1].view(_BITS[dtype]).clone()
+        self.view = self.buf[GUARD:GUARD + self.n].view(shape)
+
+    def check(self, what: str):
+        bits = self.buf.view(_BITS[self.dtype])
+        for band, name in ((bits[:GUARD], "before"), (bits[GUARD + self.n:], "after")):
+            assert bool((band == self.sentinel_bits).all()), f"{what}: a write landed in the guard band {name} it"
+        inside = bits[GUARD:GUARD + self.n]
+        assert not bool((inside == self.sentinel_bits).any()), f"{what}: an element was never written"
+
+
 def run_index(s: Shape, q_idx, k_idx):
     ws = M.alloc_workspace(M.MSA_OP_INDEX_TOPK, s)
-    blk = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.int32, device="cuda")
-    M.msa_index_topk(s, q_idx, k_idx, blk, ws)
+    g = Guarded((s.batch, s.n_q, s.h_kv, s.topk), torch.int32)
+    M.msa_index_topk(s, q_idx, k_idx, g.view, ws)
+    torch.cuda.synchronize()
+    g.check("blk_idx")
     n = s.batch * s.n_q * s.h_kv * s.nblk
     bscore = ws[: n * 4].view(torch.float32).view(s.batch, s.n_q, s.h_kv, s.nblk)
-    return blk, bscore
+    return g.view, bscore
+
+
+def _run_out_lse(s: Shape, fn):
+    go = Guarded((s.batch, s.n_q, s.h_q, s.d), torch.bfloat16)
+    gl = Guarded((s.batch, s.n_q, s.h_q), torch.float32)
+    fn(go.view, gl.view)
+    torch.cuda.synchronize()
+    go.check("out")
+    gl.check("lse")
+    return go.view, gl.view
 
 
 def run_sparse(s: Shape, q, k, v, blk):
-    out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((s.batch, s.n_q, s.h_q), dtype=torch.float32, device="cuda")
     if s.n_q == 1:
         ws = M.alloc_workspace(M.MSA_OP_SPARSE_DECODE, s)
-        M.msa_sparse_decode(s, q, k, v, blk, out, lse, ws)
-    else:
-        ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
-        M.msa_sparse_prefill(s, q, k, v, blk, out, lse, ws)
-    return out, lse
+        return _run_out_lse(s, lambda out, lse: M.msa_sparse_decode(s, q, k, v, blk, out, lse, ws))
+    ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
+    return _run_out_lse(s, lambda out, lse: M.msa_sparse_prefill(s, q, k, v, blk, out, lse, ws))
 
 
 def run_sparse_prefill_path(s: Shape, q, k, v, blk):
-    out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((s.batch, s.n_q, s.h_q), dtype=torch.float32, device="cuda")
     ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
-    M.msa_sparse_prefill(s, q, k, v, blk, out, lse, ws)
-    return out, lse
+    return _run_out_lse(s, lambda out, lse: M.msa_sparse_prefill(s, q, k, v, blk, out, lse, ws))
 
 
 def run_dense(s: Shape, q, k, v):
-    out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((s.batch, s.n_q, s.h_q), dtype=torch.float32, device="cuda")
     ws = M.alloc_workspace(M.MSA_OP_DENSE_GQA, s)
-    M.msa_dense_gqa(s, q, k, v, out, lse, ws)
-    return out, lse
+    return _run_out_lse(s, lambda out, lse: M.msa_dense_gqa(s, q, k, v, out, lse, ws))
 
 
 class OutCheck:

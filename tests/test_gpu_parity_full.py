@@ -7,6 +7,7 @@ one (first and last rows and block-boundary rows always included).
   decode_256k_b64   64 sequences of 262,144 tokens; 16 sequences
   prefill_chunk_1m  8,192 queries at 1,040,384.. of a 1,048,576 cache; 20 rows
   decode_1m_b8      8 sequences of 1,048,576 tokens; all 8
+  topk_full_rows    the top-k alone on 1,048,576 rows of 1,023 candidates; 64 rows
 """
 
 import numpy as np
@@ -73,3 +74,35 @@ def test_prefill_chunk_1m():
 
 def test_decode_1m_b8():
     run_case("decode_1m_b8", 0, 2)
+
+
+def test_topk_full_rows():
+    """The benchmark's top-k-alone leg at its full size (1,048,576 rows of
+    1,023 candidates, the same seeded pooled scores and launch): selections
+    bit-exact against the oracle's select_blocks on 64 sampled rows."""
+    import importlib.util
+    import os
+
+    from block_sparse_long_score_amd import msa as M
+    from block_sparse_long_score_amd.inputs import Shape
+    from oracle import msa_oracle as O
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_for_topk", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    s = Shape(**bench.TOPK_FULL_SHAPE)
+    print(f"case topk_full_rows: {s}", flush=True)
+    sc = bench.topk_full_scores(torch, s)
+    blk = torch.full((s.batch, s.n_q, s.h_kv, s.topk), -7, dtype=torch.int32, device="cuda")
+    M.msa_block_topk(s, sc, blk)
+    torch.cuda.synchronize()
+    assert not (blk == -7).any(), "a row was not written"
+    rows = s.batch * s.n_q * s.h_kv
+    flat_sc, flat_blk = sc.view(rows, s.nblk), blk.view(rows, s.topk)
+    for r in sample_rows(rows, 64, 3098):
+        t = (r // s.h_kv) % s.n_q
+        jl = (s.pos0 + t) // s.block
+        want = O.select_blocks(flat_sc[r].double().cpu().numpy(), jl, s.topk)
+        got = flat_blk[r].cpu().numpy()
+        assert np.array_equal(got, want.astype(np.int32)), (r, got.tolist(), want.tolist())

@@ -128,30 +128,18 @@ __device__ __forceinline__ void wave_select(const uint32_t (&key)[V], int kk, ui
 
 // Rows of up to 64*V candidates: one wave per kRowsPerWave consecutive
 // (query, group) rows, the next row's scores loaded while the current row is
-// selected.
+// selected.  Each wave holds only as many scores per lane as its own longest
+// row needs (causal prefill rows grow with the token, so most waves need far
+// fewer than the launch's longest row).
 constexpr int kRowsPerWave = 8;
+
 template <int V>
-__global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* __restrict__ bscore,
-                                                                   int32_t* __restrict__ blk, int n_q, int pos0,
-                                                                   int h_kv, int nblk, int topk, int64_t nrows,
-                                                                   int n_kv, const int* __restrict__ seq_len,
-                                                                   int lb) {
-  __shared__ uint32_t ck[kRowsPerWg][64];
-  __shared__ int32_t ci[kRowsPerWg][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * kRowsPerWg + wave) * kRowsPerWave;
-  if (row0 >= nrows) return;
-  const int64_t row_end = min(row0 + (int64_t)kRowsPerWave, nrows);
+__device__ __forceinline__ void topk_rows_body(const float* __restrict__ bscore, int32_t* __restrict__ blk,
+                                               int64_t row0, int64_t row_end, int rb, int rt, int rg, int n_q,
+                                               int pos0, int h_kv, int nblk, int topk, int n_kv,
+                                               const int* __restrict__ seq_len, int lb, uint32_t* ck, int32_t* ci) {
+  const int lane = lane_id();
   const int kk = topk - 1;
-  // (sequence, token) of a row, found once for the wave's first row and then
-  // stepped row by row (wave-uniform; rows are (b * n_q + t) * h_kv + g).
-  int rb, rt, rg;
-  {
-    const int64_t bt = row0 / h_kv;
-    rg = (int)(row0 - bt * h_kv);
-    rb = (int)(bt / n_q);
-    rt = (int)(bt - (int64_t)rb * n_q);
-  }
   auto step = [&](int& b, int& t, int& g) {
     if (++g == h_kv) {
       g = 0;
@@ -193,7 +181,7 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* 
         uint32_t key[V];
 #pragma unroll
         for (int i = 0; i < V; ++i) key[i] = (i * 64 + lane < n) ? order_key(cur[i]) : 0u;   // 0: below every key
-        wave_select<V>(key, kk, ck[wave], ci[wave], [&](int pos, uint32_t, int e) { out[pos] = e; });
+        wave_select<V>(key, kk, ck, ci, [&](int pos, uint32_t, int e) { out[pos] = e; });
       }
     }
 #pragma unroll
@@ -201,30 +189,80 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* 
   }
 }
 
-// Long rows (up to 256*V candidates): a workgroup per row.  Wave w selects the
-// exact top-kk of its contiguous quarter [w*n/4, (w+1)*n/4) into LDS; the
-// quarters are in block order, so wave 0's exact top-kk over the (at most 4*kk)
-// survivors, ties broken by position, is the row's answer.
-constexpr int kWgWaves = 4;
 template <int V>
-__global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __restrict__ bscore,
-                                                               int32_t* __restrict__ blk, int n_q, int pos0,
-                                                               int h_kv, int nblk, int topk, int n_kv,
-                                                               const int* __restrict__ seq_len, int lb) {
-  __shared__ uint32_t ck[kWgWaves][64];
-  __shared__ int32_t ci[kWgWaves][64];
-  __shared__ uint32_t cand_k[kWgWaves][64];
-  __shared__ int32_t cand_i[kWgWaves][64];
-  __shared__ int cand_n[kWgWaves];
-  __shared__ uint32_t cat_k[kWgWaves * 64];
-  __shared__ int32_t cat_i[kWgWaves * 64];
+__global__ __launch_bounds__(kRowsPerWg * 64) void block_topk_rows(const float* __restrict__ bscore,
+                                                                   int32_t* __restrict__ blk, int n_q, int pos0,
+                                                                   int h_kv, int nblk, int topk, int64_t nrows,
+                                                                   int n_kv, const int* __restrict__ seq_len,
+                                                                   int lb) {
+  __shared__ uint32_t ck[kRowsPerWg][64];
+  __shared__ int32_t ci[kRowsPerWg][64];
+  const int wave = threadIdx.x >> 6;
+  const int64_t row0 = ((int64_t)blockIdx.x * kRowsPerWg + wave) * kRowsPerWave;
+  if (row0 >= nrows) return;
+  const int64_t row_end = min(row0 + (int64_t)kRowsPerWave, nrows);
+  // (sequence, token, group) of the wave's first row (wave-uniform; rows are
+  // (b * n_q + t) * h_kv + g), and the most candidates any of its rows has.
+  int rb, rt, rg;
+  {
+    const int64_t bt = row0 / h_kv;
+    rg = (int)(row0 - bt * h_kv);
+    rb = (int)(bt / n_q);
+    rt = (int)(bt - (int64_t)rb * n_q);
+  }
+  int need = 0;
+  for (int64_t row = row0; row < row_end; ++row) {
+    const int64_t bt = row / h_kv;
+    const int b = (int)(bt / n_q), t = (int)(bt - (int64_t)b * n_q);
+    const int jl = (seq_pos0(seq_len, b, pos0, n_q, n_kv) + t) >> lb;
+    need = max(need, jl + 1 <= topk ? 0 : jl);
+  }
+  need = __builtin_amdgcn_readfirstlane(need);
+#define MSA_TOPK_ROWS(VV)                                                                                      \
+  topk_rows_body<VV>(bscore, blk, row0, row_end, rb, rt, rg, n_q, pos0, h_kv, nblk, topk, n_kv, seq_len, lb, \
+                     ck[wave], ci[wave])
+  if (V >= 2 && need <= 64) {
+    MSA_TOPK_ROWS(1);
+  } else if constexpr (V >= 4) {
+    if (need <= 128) {
+      MSA_TOPK_ROWS(2);
+    } else if (V >= 8 && need <= 256) {
+      MSA_TOPK_ROWS((V >= 8 ? 4 : V));
+    } else if (V >= 16 && need <= 512) {
+      MSA_TOPK_ROWS((V >= 16 ? 8 : V));
+    } else {
+      MSA_TOPK_ROWS(V);
+    }
+  } else {
+    MSA_TOPK_ROWS(V);
+  }
+#undef MSA_TOPK_ROWS
+}
+
+// Long rows, or few rows: a workgroup of NW waves per row.  Wave w selects the
+// exact top-kk of its contiguous slice [w*n/NW, (w+1)*n/NW) into LDS; the
+// slices are in block order, so wave 0's exact top-kk over the (at most NW*kk)
+// survivors, ties broken by position, is the row's answer.
+template <int V, int NW>
+__global__ __launch_bounds__(NW * 64) void block_topk_wg(const float* __restrict__ bscore,
+                                                         int32_t* __restrict__ blk, int n_q, int pos0, int h_kv,
+                                                         int nblk, int topk, int n_kv,
+                                                         const int* __restrict__ seq_len, int lb) {
+  constexpr int CV = (NW * 63 + 63) / 64;              // survivor slots per lane in the final round
+  __shared__ uint32_t ck[NW][64];
+  __shared__ int32_t ci[NW][64];
+  __shared__ uint32_t cand_k[NW][64];
+  __shared__ int32_t cand_i[NW][64];
+  __shared__ int cand_n[NW];
+  __shared__ uint32_t cat_k[CV * 64];
+  __shared__ int32_t cat_i[CV * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = blockIdx.x;
   const int64_t bt = row / h_kv;
   const int jl = (seq_pos0(seq_len, (int)(bt / n_q), pos0, n_q, n_kv) + (int)(bt % n_q)) >> lb;
   int32_t* out = blk + row * topk;
   if (jl + 1 <= topk) {                                // whole workgroup leaves together
-    for (int i = threadIdx.x; i < topk; i += kWgWaves * 64) out[i] = (i <= jl) ? i : -1;
+    for (int i = threadIdx.x; i < topk; i += NW * 64) out[i] = (i <= jl) ? i : -1;
     return;
   }
   const int kk = topk - 1;
@@ -232,9 +270,9 @@ __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __re
   if (kk == 0) return;
   const float* sc = bscore + row * nblk;
   const int n = jl;
-  const int q0 = (int)((int64_t)n * wave / kWgWaves), q1 = (int)((int64_t)n * (wave + 1) / kWgWaves);
+  const int q0 = (int)((int64_t)n * wave / NW), q1 = (int)((int64_t)n * (wave + 1) / NW);
   const int nq = q1 - q0;
-  if (nq <= kk) {                                      // the whole quarter survives
+  if (nq <= kk) {                                      // the whole slice survives
     for (int e = lane; e < nq; e += 64) {
       cand_k[wave][e] = order_key(sc[q0 + e]);
       cand_i[wave][e] = q0 + e;
@@ -254,10 +292,10 @@ __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __re
     if (lane == 0) cand_n[wave] = kk;
   }
   __syncthreads();
-  // Concatenate the quarters' survivors in block order into cat_*.
+  // Concatenate the slices' survivors in block order into cat_*.
   int start = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < kWgWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     if (w < wave) start += cand_n[w];
     total += cand_n[w];
   }
@@ -267,14 +305,14 @@ __global__ __launch_bounds__(kWgWaves * 64) void block_topk_wg(const float* __re
   }
   __syncthreads();
   if (wave != 0) return;
-  // At most kWgWaves * (topk - 1) <= 4 * 63 candidates.
-  uint32_t key[kWgWaves];
+  // At most NW * (topk - 1) <= NW * 63 candidates.
+  uint32_t key[CV];
 #pragma unroll
-  for (int i = 0; i < kWgWaves; ++i) {
+  for (int i = 0; i < CV; ++i) {
     const int c = i * 64 + lane;
     key[i] = c < total ? cat_k[c] : 0u;
   }
-  wave_select<kWgWaves>(key, kk, ck[0], ci[0], [&](int pos, uint32_t, int c) { out[pos] = cat_i[c]; });
+  wave_select<CV>(key, kk, ck[0], ci[0], [&](int pos, uint32_t, int c) { out[pos] = cat_i[c]; });
 }
 
 template <int V>
@@ -290,32 +328,47 @@ hipError_t launch_v(const Dims& d, const float* bscore, int32_t* blk, hipStream_
   return hipGetLastError();
 }
 
-template <int V>
+template <int V, int NW>
 hipError_t launch_wg(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
   const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
   {
     LaunchTimer timer("block_topk_wg", stream);
-    hipLaunchKernelGGL(block_topk_wg<V>, dim3((unsigned)nrows), dim3(kWgWaves * 64), 0, stream, bscore, blk, d.n_q,
+    hipLaunchKernelGGL((block_topk_wg<V, NW>), dim3((unsigned)nrows), dim3(NW * 64), 0, stream, bscore, blk, d.n_q,
                        d.pos0, d.h_kv, d.nblk(), d.topk, d.n_kv, d.seq_len, block_shift(d));
   }
   return hipGetLastError();
+}
+
+// A workgroup of NW waves per row, each wave holding V candidates per lane.
+template <int NW>
+hipError_t launch_wg_v(const Dims& d, int jl_max, const float* bscore, int32_t* blk, hipStream_t stream) {
+  const int per_lane = ((jl_max + NW - 1) / NW + 63) / 64;
+  if (per_lane <= 4) return launch_wg<4, NW>(d, bscore, blk, stream);
+  if (per_lane <= 8) return launch_wg<8, NW>(d, bscore, blk, stream);
+  if (per_lane <= 16) return launch_wg<16, NW>(d, bscore, blk, stream);
+  return launch_wg<32, NW>(d, bscore, blk, stream);
 }
 
 }  // namespace
 
 hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk, hipStream_t stream) {
   const int jl_max = (d.seq_len ? d.n_kv - 1 : d.pos0 + d.n_q - 1) >> block_shift(d);   // most candidates of a row
+  const int64_t nrows = (int64_t)d.batch * d.n_q * d.h_kv;
+  // Few rows (decode): a workgroup per row, its waves splitting the row, so the
+  // launch still has a few thousand waves loading scores.
+  const int64_t slots = 4LL * device_cu_count();       // one wave per SIMD
+  if (nrows * 4 < slots * 4 && jl_max > 256) {
+    if (nrows * 16 <= slots * 4 || jl_max > 4096) return launch_wg_v<16>(d, jl_max, bscore, blk, stream);
+    return launch_wg_v<8>(d, jl_max, bscore, blk, stream);
+  }
   const int per_lane = (jl_max + 63) / 64;
   if (per_lane <= 1) return launch_v<1>(d, bscore, blk, stream);
   if (per_lane <= 2) return launch_v<2>(d, bscore, blk, stream);
   if (per_lane <= 4) return launch_v<4>(d, bscore, blk, stream);
   if (per_lane <= 8) return launch_v<8>(d, bscore, blk, stream);
   if (per_lane <= 16) return launch_v<16>(d, bscore, blk, stream);
-  if (per_lane <= 32) return launch_v<32>(d, bscore, blk, stream);
-  // longer rows: a workgroup per row, a quarter row per wave
-  const int per_lane_q = ((jl_max + kWgWaves - 1) / kWgWaves + 63) / 64;
-  if (per_lane_q <= 16) return launch_wg<16>(d, bscore, blk, stream);
-  return launch_wg<32>(d, bscore, blk, stream);         // the C-ABI caps nblk at 8192
+  // longer rows (more than 1,024 candidates): a workgroup of 8 waves per row
+  return launch_wg_v<8>(d, jl_max, bscore, blk, stream);   // the C-ABI caps nblk at 8192
 }
 
 // ------------------------------------------------- 256-token blocks -------

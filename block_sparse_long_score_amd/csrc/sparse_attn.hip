@@ -26,8 +26,6 @@
 namespace msa {
 namespace {
 
-constexpr int kAttnThreads = 256;
-
 int64_t prefill_entries_max(const Dims& d) { return (int64_t)d.batch * d.n_q * d.h_kv * d.topk; }
 
 // ---------------------------------------------------------------- CSR --------
@@ -392,31 +390,179 @@ __global__ __launch_bounds__(kKvThreads, 1) void sparse_kv_outer(
 }
 
 // ------------------------------------------------------------ decode -------
+//
+// One workgroup of four waves per (sequence, group, run of four selection
+// slots), one wave per selected block.  A wave requests its query heads and
+// the block's 128 keys at once, forms S^T = K Q^T on MFMA, then requests the
+// 128 values (into the key registers, now free) while the softmax runs, and
+// accumulates P V on the vector ALUs; at about 210 registers two waves fit per
+// SIMD, so one workgroup's loads overlap another's arithmetic.  The four
+// waves' results are merged in LDS into one partial (o unnormalised, m, l) per
+// head, so the merge kernel combines ceil(topk / 4) partials per (sequence,
+// head).  (Splitting a block over two waves measured slower at 64 sequences x
+// 256K: 145 against 113 us.)
+
+constexpr int kDecSlots = 4;                           // selection slots per workgroup
+constexpr int kDecWavesPerBlock = 1;
+constexpr int kDecWaves = kDecWavesPerBlock * kDecSlots;
+constexpr int kDecKeys = kBlock / kDecWavesPerBlock;   // keys per wave
 
 template <int D, int G>
-__global__ __launch_bounds__(kAttnThreads) void sparse_decode_blocks(
+__global__ __launch_bounds__(kDecWaves * 64) void sparse_decode_blocks(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ blk, uint16_t* __restrict__ part_o, float* __restrict__ part_ml, int n_kv, int pos0,
-    int h_q, int h_kv, int topk, int64_t units, float sl2, const int* __restrict__ seq_len) {
-  __shared__ float pt[kAttnThreads / 64][kBlock * 16 + 16];
-  const int wave = threadIdx.x >> 6;
-  const int64_t unit = (int64_t)blockIdx.x * (kAttnThreads / 64) + wave;   // (b, g, slot)
-  if (unit >= units) return;
-  const int64_t bg = unit / topk;
+    int h_q, int h_kv, int topk, int nsub, float sl2, const int* __restrict__ seq_len) {
+  constexpr int CC = D / 32;                           // 32-wide contraction chunks of a key
+  constexpr int KT = kDecKeys / 16;                    // 16-key MFMA tiles per wave
+  constexpr int LPR = D / 8;                           // lanes per V row (16-byte pieces)
+  constexpr int KPI = 64 / LPR;                        // keys per V load instruction
+  constexpr int VI = kDecKeys / KPI;                   // V loads per lane
+  __shared__ float pt[kDecWaves][kDecKeys * 16];       // P[key][head] per wave
+  __shared__ float so[kDecWaves][G * D];               // each wave's unnormalised o
+  __shared__ float sml[kDecWaves][2 * G];              // each wave's (m, l) per head
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t unit = blockIdx.x;                     // (b, g, run of four slots)
+  const int sub = (int)(unit % nsub);
+  const int64_t bg = unit / nsub;
   const int g = (int)(bg % h_kv), b = (int)(bg / h_kv);
-  pos0 = seq_pos0(seq_len, b, pos0, 1, n_kv);
-  const int j = blk[unit];
-  if (j < 0 || j > pos0 / kBlock) return;              // padding, or not a causal block
-  const int64_t head0 = ((int64_t)b * n_kv * h_kv + g) * D;
-  decode_attend<D, G>(q + ((int64_t)b * h_q + g * G) * D, k + head0, v + head0, (int64_t)h_kv * D, n_kv, pos0, j,
-                      j + 1, sl2, pt[wave], part_o + unit * G * D, part_ml + unit * G * 2);
+  const int p = seq_pos0(seq_len, b, pos0, 1, n_kv);
+  const int slot = sub * kDecSlots + wave / kDecWavesPerBlock;
+  const int j = __builtin_amdgcn_readfirstlane(slot < topk ? blk[bg * topk + slot] : -1);
+  const int s0 = j * kBlock + (wave % kDecWavesPerBlock) * kDecKeys;   // this wave's first key
+  const int col = lane & 15, q4 = lane >> 4;
+  const int kg = lane / LPR, dl = lane % LPR;
+  // wave-uniform: a selected, causal block whose part holds a visible key
+  if (j >= 0 && j <= p / kBlock && s0 <= p) {
+    const int64_t rs = (int64_t)h_kv * D;
+    const int64_t head0 = ((int64_t)b * n_kv * h_kv + g) * D;
+    const uint16_t* kb = k + head0;
+    const uint16_t* vb = v + head0;
+    const uint16_t* qh = q + ((int64_t)b * h_q + g * G) * D;
+    u32x4 qb[CC], a[KT][CC], vv[VI];
+#pragma unroll
+    for (int cc = 0; cc < CC; ++cc) qb[cc] = (col < G) ? ld16(qh + col * D + cc * 32 + q4 * 8) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const int s = s0 + kt * 16 + col;
+#pragma unroll
+      for (int cc = 0; cc < CC; ++cc)
+        a[kt][cc] = (s < n_kv) ? ld16(kb + (int64_t)s * rs + cc * 32 + q4 * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x4 sc[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < CC; ++cc) sc[kt] = mfma_16x16x32(a[kt][cc], qb[cc], sc[kt]);
+    }
+    // The values are requested once the keys are consumed and arrive while
+    // the softmax runs.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int it = 0; it < VI; ++it) {
+      const int s = s0 + it * KPI + kg;
+      vv[it] = (s < n_kv) ? ld16(vb + (int64_t)s * rs + dl * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = (s0 + kt * 16 + q4 * 4 + r > p) ? -INFINITY : sc[kt][r] * sl2;
+        sc[kt][r] = x;
+        mx = vmax(mx, x);
+      }
+    mx = colgroup_max(mx);                             // finite: key s0 <= p is visible
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(sc[kt][r] - mx);
+        sum += e;
+        if (col < G) pt[wave][(kt * 16 + q4 * 4 + r) * 16 + col] = e;
+      }
+    sum = colgroup_sum(sum);
+    if (q4 == 0 && col < G) {
+      sml[wave][col] = mx;
+      sml[wave][G + col] = sum;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // P V: lane (kg, dl) owns d = 8 dl .. 8 dl + 7 for keys kg, kg + KPI, ...
+    float acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < VI; ++it) {
+      float vf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = bf16_to_f32(vv[it][e] & 0xffffu);
+        vf[2 * e + 1] = bf16_to_f32(vv[it][e] >> 16);
+      }
+      const float* prow = &pt[wave][(it * KPI + kg) * 16];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float pr = prow[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = acc[h][e];
+#pragma unroll
+        for (int m = LPR; m < 64; m <<= 1) x += shfl_xor_f(x, m);
+        acc[h][e] = x;
+      }
+    if (kg == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        *reinterpret_cast<f32x4*>(&so[wave][h * D + dl * 8]) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+        *reinterpret_cast<f32x4*>(&so[wave][h * D + dl * 8 + 4]) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+      }
+    }
+  } else {                                             // padding, a block past the query, or an all-future part
+    if (lane < G) {
+      sml[wave][lane] = -INFINITY;
+      sml[wave][G + lane] = 0.f;
+    }
+  }
+  __syncthreads();
+  // Merge the waves: thread t takes elements t, t + 64 kDecWaves, ... of [G][D].
+  for (int e = threadIdx.x; e < G * D; e += kDecWaves * 64) {
+    const int h = e / D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = vmax(M, sml[w][h]);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float m = sml[w][h];
+      if (m != -INFINITY) {                            // only waves that attended keys wrote so[w]
+        const float wt = __builtin_amdgcn_exp2f(m - M);
+        L = fmaf(wt, sml[w][G + h], L);
+        o = fmaf(wt, so[w][e], o);
+      }
+    }
+    part_o[unit * G * D + e] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);
+    if (e % D == 0) *reinterpret_cast<float2*>(part_ml + 2 * (unit * G + h)) = make_float2(M, L);
+  }
 }
 
 // ------------------------------------------------------------- merge --------
 
-// Slot s of a row takes part when it holds a result: for the sparse paths when
-// blk[.., s] is a block index in [0, jl]; for split dense decode (blk == nullptr)
-// when s * per <= jl.  With M the largest partial max and w_s = exp2(m_s - M):
+// Slot s of a row takes part when it holds a result: for the sparse prefill
+// when blk[.., s] is a block index in [0, jl]; for split dense decode (blk ==
+// nullptr, per > 0) when s * per <= jl; for sparse decode (blk == nullptr, per
+// == 0) when its m is finite.  With M the largest partial max and
+// w_s = exp2(m_s - M):
 // out = sum_s w_s o_s / sum_s w_s l_s  (o_s unnormalised), lse = ln2 (M + log2 L).
 template <int D>
 __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict__ part_o,
@@ -454,11 +600,11 @@ __global__ __launch_bounds__(256) void merge_partials(const uint16_t* __restrict
     for (int i = 0; i < 8; ++i) {
       const int s = min(s0 + i, nslot - 1);
       const int j = brow ? brow[s] : s * per;
-      on[i] = (s0 + i < nslot) && j >= 0 && j <= jl;
       const int64_t pr = (unit0 + s) * G + hh;
       const float2 ml = *reinterpret_cast<const float2*>(part_ml + 2 * pr);
       mv[i] = ml.x;
       lv[i] = ml.y;
+      on[i] = (s0 + i < nslot) && j >= 0 && j <= jl && (brow || per > 0 || ml.x != -INFINITY);
       o[i] = ld16(part_o + pr * D + dl * 8);
     }
     float bm = -INFINITY;
@@ -622,14 +768,14 @@ hipError_t launch_decode_t(const Dims& d, const uint16_t* q, const uint16_t* k, 
   char* base = static_cast<char*>(ws);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
-  const int64_t units = (int64_t)d.batch * d.h_kv * d.topk;
-  const int64_t wgs = (units + 3) / 4;
+  const int64_t wgs = (int64_t)d.batch * d.h_kv * L.nslot;
   {
     LaunchTimer timer("sparse_decode_blocks", stream);
-    hipLaunchKernelGGL((sparse_decode_blocks<D, G>), dim3((unsigned)wgs), dim3(kAttnThreads), 0, stream, q, k, v, blk,
-                       part_o, part_ml, d.n_kv, d.pos0, d.h_q, d.h_kv, d.topk, units, sl2, d.seq_len);
+    hipLaunchKernelGGL((sparse_decode_blocks<D, G>), dim3((unsigned)wgs), dim3(kDecWaves * 64), 0, stream, q, k, v,
+                       blk, part_o, part_ml, d.n_kv, d.pos0, d.h_q, d.h_kv, d.topk, L.nslot, sl2, d.seq_len);
   }
-  return launch_merge_t<D>(d, part_o, part_ml, blk, out, lse, d.topk, 1, stream);
+  // One partial per run of four slots; a run without a selected causal block has m = -inf.
+  return launch_merge_t<D>(d, part_o, part_ml, nullptr, out, lse, L.nslot, 0, stream);
 }
 
 template <int D>
@@ -716,7 +862,7 @@ PrefillWs prefill_ws_layout(const Dims& d) {
 
 DecodeWs sparse_decode_ws_layout(const Dims& d) {
   DecodeWs L{};
-  L.nslot = d.topk;
+  L.nslot = (d.topk + kDecSlots - 1) / kDecSlots;      // one partial per run of four selection slots
   const size_t units = (size_t)d.batch * d.h_kv * d.topk * d.group();
   size_t o = 0;
   L.part_o = o;

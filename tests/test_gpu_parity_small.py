@@ -232,3 +232,33 @@ def test_block_topk_long_rows_workgroup_path(jl_span, topk):
         for gg in range(s.h_kv):
             want = O.select_blocks(sc[0, t, gg, : jl + 1], jl, s.topk)
             assert (got[0, t, gg] == want).all(), (t, gg, got[0, t, gg], want)
+
+
+def test_block_topk_rows_width_buckets():
+    """The per-wave rows kernel holds only as many scores per lane as the
+    wave's longest row needs (64, 128, 256, 512 or 1,024 candidates): rows on
+    both sides of every width boundary, including waves whose rows straddle
+    one (8 rows per wave = 2 tokens x 4 groups here), against the oracle's
+    selection on heavy-tie integer scores."""
+    s = Shape(1, 131072, 131072, 0, 8, 4, 128, 128, topk=16)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    bscore = torch.randint(-5, 6, (s.batch, s.n_q, s.h_kv, s.nblk), generator=g, device="cuda").float()
+    blk = torch.full((s.batch, s.n_q, s.h_kv, s.topk), -7, dtype=torch.int32, device="cuda")
+    from block_sparse_long_score_amd import msa as M
+    M.msa_block_topk(s, bscore, blk)
+    torch.cuda.synchronize()
+    assert not bool((blk == -7).any())
+    toks = set()
+    for jl in (15, 16, 17, 63, 64, 65, 66, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1000, 1023):
+        for t in (128 * jl - 2, 128 * jl - 1, 128 * jl, 128 * jl + 1):
+            if 0 <= t < s.n_q:
+                toks.add(t)
+    toks.update(range(5, s.n_q, 4099))
+    sc = bscore[0].cpu().numpy().astype(np.float64)
+    got = blk[0].cpu().numpy()
+    for t in sorted(toks):
+        jl = t // s.block
+        for gg in range(s.h_kv):
+            want = O.select_blocks(sc[t, gg, : jl + 1], jl, s.topk)
+            assert (got[t, gg] == want).all(), (t, gg, got[t, gg].tolist(), want.tolist())

@@ -54,11 +54,26 @@ class Guarded:
 
 
 def run_index(s: Shape, q_idx, k_idx):
+    """msa_index_topk's selection, and the pooled scores the selection rests on.
+    With 128-token blocks the pooled scores come from a separate
+    msa_index_scores call and the selection must equal msa_block_topk's on them
+    in every row (so each test checks all rows' selections, not only the rows
+    it compares with the oracle); with 256-token blocks they are read from
+    msa_index_topk's workspace, where it documents them."""
     ws = M.alloc_workspace(M.MSA_OP_INDEX_TOPK, s)
     g = Guarded((s.batch, s.n_q, s.h_kv, s.topk), torch.int32)
     M.msa_index_topk(s, q_idx, k_idx, g.view, ws)
     torch.cuda.synchronize()
     g.check("blk_idx")
+    if s.block == 128:
+        bscore = torch.empty((s.batch, s.n_q, s.h_kv, s.nblk), dtype=torch.float32, device="cuda")
+        M.msa_index_scores(s, q_idx, k_idx, bscore)
+        ref = torch.empty_like(g.view)
+        M.msa_block_topk(s, bscore, ref)
+        torch.cuda.synchronize()
+        diff = (ref != g.view).nonzero()
+        assert diff.numel() == 0, f"msa_index_topk differs from msa_block_topk on its pooled scores at {diff[:4].tolist()}"
+        return g.view, bscore
     n = s.batch * s.n_q * s.h_kv * s.nblk
     bscore = ws[: n * 4].view(torch.float32).view(s.batch, s.n_q, s.h_kv, s.nblk)
     return g.view, bscore

@@ -1,16 +1,33 @@
 """GPU parity of the main-branch backward (msa_sparse_prefill_backward) against
 the fp64 oracle.
 
-Tolerances, from the arithmetic: products are exact bf16 x bf16 in fp32; P and
-dS enter the dv, dk and dq contractions rounded to bf16 (relative 2^-9 per
-term), dq leaves the key-outer kernel as one bf16 partial per selected block,
-D = rowsum(dout * out) uses the forward's bf16 output, and every gradient is
-rounded to bf16 once.  The bound per tensor is
+Tolerances, from the arithmetic (u = 2^-8, the unit roundoff of bf16): products
+are exact bf16 x bf16 in fp32; P and dS enter the dv, dk and dq contractions
+rounded to bf16 (relative u per term), dq leaves the key-outer kernel as one
+bf16 partial per selected block, and every gradient is rounded to bf16 once.
+The bound per tensor is
     ||err||_2 / ||ref||_2 <= 1e-2   and   max |err| <= 2e-2 * max |ref|,
-plus, per row of dq (one (token, head)) and per key row of dk / dv with a norm
-of at least a tenth of the largest row, ||err|| / ||ref|| <= 5e-2: a dq row is a
-sum of terms whose dS add up to zero, so its cancellation can lift the 2^-9
-per-term rounding to a few percent of the row (3.2e-2 seen at most).
+and per row (one (token, head) of dq, one key of dk / dv) with a norm of at
+least a tenth of the largest row
+    ||err|| <= 1e-2 * ||ref|| + allow,
+where allow is 0 for dk and dv.  For dq it covers the one error that is not
+relative to the row: D = rowsum(dout * out) is taken from the forward's bf16
+output, as flash-attention backwards do, not from the exact output.  Element d
+of that output carries three roundings, each of mean zero and independent of
+the others and across d: P_s before P.V (at most u P_s |v_s,d|), its block's
+partial c_b = sum_{s in b} P_s v_s (at most u |c_b,d|) and the result o (at
+most u |o_d|).  A rounding error of at most u|x| has a variance of at most
+(u x)^2 / 3, so the error of D has a standard deviation of at most
+    sigma = u * sqrt(sum_d dout_d^2 (sum_s P_s^2 v_s,d^2 + sum_b c_b,d^2 + o_d^2) / 3);
+and because every dS_s = P_s (dP_s - D), an error e in D moves the dq row by
+exactly -scale * e * sum_s P_s k_s.  The allowance is six such deviations:
+    allow = 6 * scale * sigma * ||sum_s P_s k_s||.
+It matters in rows that see a handful of keys, where dS cancels almost
+completely: there the D term reaches several percent of the row (an fp64
+emulation of the kernel's roundings gives 3.5e-2 for the second token of the
+4,096-token workload, and 4e-3 with the exact D); elsewhere it is far below
+1e-2.  Keeping dq's partials in fp32 would not change it (the same emulation:
+3.5e-2).
 """
 
 import math
@@ -28,7 +45,38 @@ pytestmark = pytest.mark.gpu
 
 REL_L2 = 1e-2
 MAX_REL = 2e-2
-ROW_REL = 5e-2
+ROW_REL = 1e-2
+BF16_U = 2.0 ** -8
+D_SIGMAS = 6.0
+
+
+def dq_allow(qh, keys, vals, douth, scale, blocks):
+    """Per-head allowance for the D term (module docstring) of one (token,
+    group): qh, douth [G][d]; keys, vals [n][d] the visible rows; blocks [n]
+    the block of each row."""
+    kbar, lse = O.softmax_attention(qh, keys, keys, scale)
+    p = np.exp(scale * (qh @ keys.T) - lse[:, None])        # the softmax weights, [G][n]
+    var = (p * p) @ (vals * vals) + (p @ vals) ** 2
+    for j in np.unique(blocks):
+        m = blocks == j
+        var += (p[:, m] @ vals[m]) ** 2
+    sigma = BF16_U * np.sqrt(np.sum(douth * douth * var, axis=1) / 3.0)
+    return D_SIGMAS * scale * sigma * np.linalg.norm(kbar, axis=1)
+
+
+def dq_allow_all(s: Shape, q, k, v, dout, blk):
+    """dq_allow for every (b, t, h) row, from fp64 arrays and a selection."""
+    scale = O.default_scale(s.d)
+    G = s.group
+    allow = np.zeros((s.batch, s.n_q, s.h_q))
+    for b in range(s.batch):
+        for t in range(s.n_q):
+            for g in range(s.h_kv):
+                pos = O.visible_positions(blk[b, t, g], s.pos0 + t, s.block, s.n_kv)
+                hs = slice(g * G, (g + 1) * G)
+                allow[b, t, hs] = dq_allow(q[b, t, hs], k[b, pos, g], v[b, pos, g], dout[b, t, hs], scale,
+                                           pos // s.block)
+    return allow
 
 
 def make_dout(s: Shape, seed: int):
@@ -48,17 +96,21 @@ def run_backward(s: Shape, inp, blk, dout):
     return dq, dk, dv
 
 
-def check_grad(got: np.ndarray, ref: np.ndarray, what: str):
+def check_grad(got: np.ndarray, ref: np.ndarray, what: str, allow=None):
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     err = got - ref
     rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30)
     mx = np.max(np.abs(err)) / max(np.max(np.abs(ref)), 1e-30)
     rows_ref = np.linalg.norm(ref.reshape(-1, ref.shape[-1]), axis=1)
     rows_err = np.linalg.norm(err.reshape(-1, ref.shape[-1]), axis=1)
+    rows_allow = np.zeros_like(rows_ref) if allow is None else np.asarray(allow, dtype=np.float64).ravel()
     big = rows_ref >= 0.1 * rows_ref.max() if rows_ref.size else rows_ref > 0
     row_rel = float(np.max(rows_err[big] / rows_ref[big])) if np.any(big) else 0.0
-    print(f"  {what}: rel L2 {rel:.2e}, max {mx:.2e}, worst row {row_rel:.2e}", flush=True)
-    assert rel <= REL_L2 and mx <= MAX_REL and row_rel <= ROW_REL, what
+    bound = ROW_REL * rows_ref + rows_allow
+    row_use = float(np.max(rows_err[big] / bound[big])) if np.any(big) else 0.0
+    print(f"  {what}: rel L2 {rel:.2e}, max {mx:.2e}, worst row {row_rel:.2e}, "
+          f"worst row / its bound {row_use:.2f}", flush=True)
+    assert rel <= REL_L2 and mx <= MAX_REL and row_use <= 1.0, what
     if np.max(np.abs(ref)) == 0.0:
         assert np.max(np.abs(got)) == 0.0, what
 
@@ -97,9 +149,9 @@ def test_backward_parity_every_row(name):
     blk_np = blk.cpu().numpy()
     _, blk_ref = O.msa_index_topk(U.to64(inp["q_idx"]), U.to64(inp["k_idx"]), s.pos0, s.block, s.topk)
     assert np.array_equal(blk_np, blk_ref.astype(np.int32))
-    rq, rk, rv = O.msa_sparse_attention_grad(U.to64(inp["q"]), U.to64(inp["k"]), U.to64(inp["v"]), blk_ref,
-                                             U.to64(dout), s.pos0, s.block)
-    check_grad(U.to64(dq), rq, f"{name} dq")
+    q64, k64, v64, do64 = U.to64(inp["q"]), U.to64(inp["k"]), U.to64(inp["v"]), U.to64(dout)
+    rq, rk, rv = O.msa_sparse_attention_grad(q64, k64, v64, blk_ref, do64, s.pos0, s.block)
+    check_grad(U.to64(dq), rq, f"{name} dq", dq_allow_all(s, q64, k64, v64, do64, blk_ref))
     check_grad(U.to64(dk), rk, f"{name} dk")
     check_grad(U.to64(dv), rv, f"{name} dv")
 
@@ -122,9 +174,9 @@ def test_backward_caller_selection_with_padding():
     dout = make_dout(s, 77)
     dq, dk, dv = run_backward(s, inp, torch.from_numpy(blk).cuda(), dout)
     torch.cuda.synchronize()
-    rq, rk, rv = O.msa_sparse_attention_grad(U.to64(inp["q"]), U.to64(inp["k"]), U.to64(inp["v"]), blk,
-                                             U.to64(dout), s.pos0, s.block)
-    check_grad(U.to64(dq), rq, "caller dq")
+    q64, k64, v64, do64 = U.to64(inp["q"]), U.to64(inp["k"]), U.to64(inp["v"]), U.to64(dout)
+    rq, rk, rv = O.msa_sparse_attention_grad(q64, k64, v64, blk, do64, s.pos0, s.block)
+    check_grad(U.to64(dq), rq, "caller dq", dq_allow_all(s, q64, k64, v64, do64, blk))
     check_grad(U.to64(dk), rk, "caller dk")
     check_grad(U.to64(dv), rv, "caller dv")
     assert float(dk[0, : 2 * s.block].abs().max()) == 0.0 and float(dv[0, : 2 * s.block].abs().max()) == 0.0
@@ -163,14 +215,15 @@ def test_backward_full_size_prefill_128k_sampled():
     g_dk = 5
     keys64 = {g: U.to64(inp["k"][0, :, g]) for g in range(s.h_kv)}
     vals64 = {g: U.to64(inp["v"][0, :, g]) for g in range(s.h_kv)}
-    ref_dq, got_dq = [], []
+    ref_dq, got_dq, allow_dq = [], [], []
     for (b, t, g), sel in sels.items():
         pos = O.visible_positions(sel, s.pos0 + t, s.block, s.n_kv)
-        gq, _, _ = O.softmax_attention_grad(U.to64(inp["q"][b, t, g * G:(g + 1) * G]), keys64[g][pos],
-                                            vals64[g][pos], U.to64(dout[b, t, g * G:(g + 1) * G]), scale)
+        qh, doh = U.to64(inp["q"][b, t, g * G:(g + 1) * G]), U.to64(dout[b, t, g * G:(g + 1) * G])
+        gq, _, _ = O.softmax_attention_grad(qh, keys64[g][pos], vals64[g][pos], doh, scale)
         ref_dq.append(gq)
         got_dq.append(U.to64(dq[b, t, g * G:(g + 1) * G]))
-    check_grad(np.stack(got_dq), np.stack(ref_dq), "128k dq rows")
+        allow_dq.append(dq_allow(qh, keys64[g][pos], vals64[g][pos], doh, scale, pos // s.block))
+    check_grad(np.stack(got_dq), np.stack(ref_dq), "128k dq rows", np.stack(allow_dq))
     blk_g = blk[0, :, g_dk].cpu().numpy()
     for j in (512, s.nblk - 3):
         ts = np.nonzero((blk_g == j).any(axis=1))[0]

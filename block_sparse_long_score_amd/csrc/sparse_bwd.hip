@@ -12,9 +12,10 @@
 // operands in registers, and their dk / dv rows as fp32 accumulators for the
 // whole list, so every key gradient is summed inside one workgroup in a fixed
 // order (no atomics).  For each group of 32 (entry x group head) columns the
-// columns' q and dout rows are staged in LDS row-major and transposed; each
-// wave computes S^T and dP^T for its keys, P and dS, and adds P * dout and
-// dS * q into its rows.  dS goes through LDS so that each wave can then form
+// columns' q and dout rows are staged in LDS row-major; each wave computes S^T
+// and dP^T for its keys, P and dS, and adds P * dout and dS * q into its rows,
+// reading the q and dout operands of those two products from the same
+// row-major tiles with transposing LDS reads.  dS goes through LDS so that each wave can then form
 // one 16-wide d slice of dq over all 128 keys of the block; dq leaves as one
 // bf16 partial per (t, g, slot, head), summed per (t, head) by a second kernel.
 #include "launch.h"
@@ -26,14 +27,38 @@ namespace {
 constexpr int kBwdThreads = 512;
 constexpr int kBwdCols = 32;                           // (entry x head) columns per group
 
-// [d][column] tiles (q and dout transposed): units of 4 columns, unit u of row
-// d at u ^ ((d >> 2) & 7).
-// Rows are padded to kTtStride elements and the unit is XOR'd with (d >> 3) & 7:
-// the dk / dv operand reads (16 rows x 4 units per wave) then hit every bank
-// pair once, and the staging writes (4-byte words of 2 columns) at most twice.
-constexpr int kTtStride = 40;
-__device__ __forceinline__ int tt_off(int d, int col) {
-  return d * kTtStride + 4 * (((col >> 2) ^ (d >> 3)) & 7) + (col & 3);
+// Row-major [column][d] tiles of q and dout: 16-byte chunk c of row r sits at
+// c ^ qd_swz(r).  The LDS has 64 four-byte banks; an 8-byte read (the
+// transposing one included) serves lanes 0-31 in one cycle and 32-63 in the
+// next, a 16-byte read serves in each cycle the 16 lanes with the same lane
+// index mod 4 (measured with the bank-conflict counter).  Two reads use these
+// tiles.  The S^T / dP^T operands: lane (q4, m16) reads row 16*ct + m16 at
+// chunk 4*c + q4, so for rows with equal bits 0-1, bits 2-3 of qd_swz must be a
+// bijection of row bits 2-3.  The dV / dK operands (transposing reads): lane
+// (q4, m16) reads row 4*q4 + (m16 >> 2) (+ 16) at chunk 2*dt + ((m16 & 3) >> 1),
+// so for rows with equal bit 3, bits 1-3 of qd_swz must be a bijection of row
+// bits 0-2.  With s0 = r3, s1 = r0, s2 = r1 ^ r2, s3 = r2 ^ r3 (d = 128) both
+// hold, and neither read has a bank conflict.  For d = 64 (rows of 128 bytes,
+// the row parity picks the half of the banks) the transposing reads are free of
+// conflicts and the S^T / dP^T reads conflict 2-way, as with any swizzle.
+template <int D>
+__device__ __forceinline__ int qd_swz(int r) {
+  if (D == 128)
+    return ((r >> 3) & 1) | ((r & 1) << 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 3);
+  return ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int qd_off(int r, int chunk) { return r * D + 8 * (chunk ^ qd_swz<D>(r)); }
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element i & 3 of the 8 bytes that lane 4r + (i >> 2)
+// addresses, as its element r (r = 0..3).
+__device__ __forceinline__ u32x2 ld_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
 }
 // dS tile [column][key]: 8-key chunk c of row col at c ^ (col & 15).
 __device__ __forceinline__ int ds_off(int col, int key) {
@@ -48,11 +73,12 @@ struct BwdLds {
       uint16_t v[kBlock * D];
     } kv;                                              // the block, while its operands are loaded
     struct {
-      uint16_t qr[kBwdCols * D], dor[kBwdCols * D];    // [column][d]
-      uint16_t qt[D * kTtStride], dot[D * kTtStride];  // [d][column], padded rows
+      uint16_t qr[kBwdCols * D], dor[kBwdCols * D];    // [column][d], qd_off
       uint16_t ds[kBwdCols * kBlock];                  // [column][key]
-      float lse2[kBwdCols], dcol[kBwdCols];
-      int plim[kBwdCols];                              // last visible key position, -1 for an empty column
+      // Read as 16-byte vectors of 4 consecutive columns.
+      alignas(16) float lse2[kBwdCols];
+      alignas(16) float dcol[kBwdCols];
+      alignas(16) int plim[kBwdCols];                  // last visible key position, -1 for an empty column
       // Partial dq row of each column (the sink when empty), by group parity:
       // the dq phase of one group reads it while faster waves already stage
       // the next group.
@@ -167,6 +193,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
   const int ngroups = (ncols + kBwdCols - 1) / kBwdCols;
   if (ngroups > 0) {
     const int skey = s0 + mykey;
+    // Transposing-read offsets: rows 4*q4 + (m16 >> 2) and 16 + ..., chunk
+    // 2*dt + ((m16 & 3) >> 1) (so chunk ^ qd_swz = 2*dt ^ x), element 4*(m16 & 1).
+    const int tr_r1 = 4 * q4 + (m16 >> 2), tr_r2 = tr_r1 + 16;
+    const int tr_row1 = tr_r1 * D, tr_row2 = tr_r2 * D;
+    const int tr_x1 = qd_swz<D>(tr_r1) ^ ((m16 & 3) >> 1), tr_x2 = qd_swz<D>(tr_r2) ^ ((m16 & 3) >> 1);
+    const int tr_e = 4 * (m16 & 1);
     // Staging role: tensor `which` (q or dout), columns 2*scp and 2*scp + 1,
     // chunk sch (d = 128: every thread; d = 64: threads beyond NST mirror the
     // first NST and write nothing); every thread also carries the meta values
@@ -216,21 +248,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
     // them those of the loop itself.
     __builtin_amdgcn_s_waitcnt(0);
     for (int grp = 0; grp < ngroups; ++grp) {
-      // Transpose the staging tile in registers (2 columns per 4-byte word),
-      // outside the writer branch so the waits for the loads stay outside too.
-      uint32_t tw[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1, sh = 16 * (e & 1);
-        tw[e] = ((st.v[0][wd] >> sh) & 0xffffu) | (((st.v[1][wd] >> sh) & 0xffffu) << 16);
-      }
       if (tid < NST) {                                 // wave-uniform
         uint16_t* rt = which ? sm.g.dor : sm.g.qr;
-        uint16_t* tt = which ? sm.g.dot : sm.g.qt;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) st16(&rt[rt_off<D>(2 * scp + kk, sch)], st.v[kk]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(&tt[tt_off(8 * sch + e, 2 * scp)]) = tw[e];
+        for (int kk = 0; kk < 2; ++kk) st16(&rt[qd_off<D>(2 * scp + kk, sch)], st.v[kk]);
       }
       // Every thread of a meta column writes the same values.
       sm.g.plim[mcol] = st.plim;
@@ -250,35 +271,42 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
         dpacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) {
-          sacc[ct] = mfma_16x16x32(ld16(&sm.g.qr[rt_off<D>(16 * ct + m16, 4 * c + q4)]), kop[c], sacc[ct]);
-          dpacc[ct] = mfma_16x16x32(ld16(&sm.g.dor[rt_off<D>(16 * ct + m16, 4 * c + q4)]), vop[c], dpacc[ct]);
+          sacc[ct] = mfma_16x16x32(ld16(&sm.g.qr[qd_off<D>(16 * ct + m16, 4 * c + q4)]), kop[c], sacc[ct]);
+          dpacc[ct] = mfma_16x16x32(ld16(&sm.g.dor[qd_off<D>(16 * ct + m16, 4 * c + q4)]), vop[c], dpacc[ct]);
         }
       }
       float p[2][4], ds[2][4];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 2; ++ct) {
+        const int c0 = 16 * ct + 4 * q4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.g.lse2[c0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.g.dcol[c0]);
+        const u32x4 m4 = *reinterpret_cast<const u32x4*>(&sm.g.plim[c0]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int col = 16 * ct + 4 * q4 + r;
-          const float x = fmaf(sacc[ct][r], sl2, -sm.g.lse2[col]);
-          const float pv = __builtin_amdgcn_exp2f(skey <= sm.g.plim[col] ? x : -INFINITY);
+          const float x = fmaf(sacc[ct][r], sl2, -l4[r]);
+          const float pv = __builtin_amdgcn_exp2f(skey <= (int)m4[r] ? x : -INFINITY);
           p[ct][r] = pv;
-          ds[ct][r] = pv * (dpacc[ct][r] - sm.g.dcol[col]);
+          ds[ct][r] = pv * (dpacc[ct][r] - d4[r]);
         }
+      }
       // A operands (row = this lane's key) with contraction slot 8*q4 + i <->
       // column 4*q4 + i (i < 4) or 16 + 4*q4 + i - 4 (i >= 4).
       const u32x4 pa = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                         pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
       const u32x4 dsa = {pack_bf16x2(ds[0][0], ds[0][1]), pack_bf16x2(ds[0][2], ds[0][3]),
                          pack_bf16x2(ds[1][0], ds[1][1]), pack_bf16x2(ds[1][2], ds[1][3])};
+      // B operands (column n = d 16*dt + m16, the same contraction slots):
+      // transposing reads of rows 4*q4 + (m16 >> 2) and 16 + 4*q4 + (m16 >> 2)
+      // at d 16*dt + 4*(m16 & 3); lane m16 then holds columns 4*q4 .. 4*q4 + 3
+      // (and 16 + ...) of its d.
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = 16 * dt + m16;
-        const u32x2 dlo = *reinterpret_cast<const u32x2*>(&sm.g.dot[tt_off(d, 4 * q4)]);
-        const u32x2 dhi = *reinterpret_cast<const u32x2*>(&sm.g.dot[tt_off(d, 16 + 4 * q4)]);
+        const int o1 = tr_row1 + 8 * ((2 * dt) ^ tr_x1) + tr_e;
+        const int o2 = tr_row2 + 8 * ((2 * dt) ^ tr_x2) + tr_e;
+        const u32x2 dlo = ld_tr16(&sm.g.dor[o1]), dhi = ld_tr16(&sm.g.dor[o2]);
         dva[dt] = mfma_16x16x32(pa, u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, dva[dt]);
-        const u32x2 qlo = *reinterpret_cast<const u32x2*>(&sm.g.qt[tt_off(d, 4 * q4)]);
-        const u32x2 qhi = *reinterpret_cast<const u32x2*>(&sm.g.qt[tt_off(d, 16 + 4 * q4)]);
+        const u32x2 qlo = ld_tr16(&sm.g.qr[o1]), qhi = ld_tr16(&sm.g.qr[o2]);
         dka[dt] = mfma_16x16x32(dsa, u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dka[dt]);
       }
 #pragma unroll

@@ -270,6 +270,8 @@ msa_status msa_sparse_prefill_backward(const msa_dims* dims, const uint16_t* q, 
                                        msa_stream stream) {
   msa_status st = check_dims(dims, op_needs(MSA_OP_SPARSE_PREFILL) | kOnly128);
   if (st != MSA_OK) return st;
+  // The kernel forms addresses from 32-bit byte strides of q/dout rows and of dq partials.
+  if ((int64_t)dims->h_q * dims->topk * dims->d >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
   if (dims->batch == 0 || dims->n_kv == 0) return MSA_OK;
   if (!k || !v || !dk || !dv) return MSA_ERR_NULL;
   if (dims->n_q > 0 && (!q || !blk_idx || !out || !lse || !dout || !dq)) return MSA_ERR_NULL;

@@ -79,10 +79,12 @@ struct BwdLds {
       alignas(16) float lse2[kBwdCols];
       alignas(16) float dcol[kBwdCols];
       alignas(16) int plim[kBwdCols];                  // last visible key position, -1 for an empty column
-      // Partial dq row of each column (the sink when empty), by group parity:
-      // the dq phase of one group reads it while faster waves already stage
-      // the next group.
-      int64_t prow[2][kBwdCols];
+      // Element offset of each column's partial dq row (the sink when empty),
+      // by group parity: the dq phase of one group reads it while faster waves
+      // already stage the next group.  An offset from the kernel argument, not
+      // an address: a pointer rebuilt from an integer would make the stores
+      // flat ones, which also count against the LDS wait counter.
+      uint64_t prow[2][kBwdCols];
     } g;
   };
 };
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void bwd_row_dot(const uint16_t* __restrict__ 
 // column).
 struct BwdStage {
   u32x4 v[2];
-  int64_t prow;
+  uint64_t prow;                                       // element offset of the column's dq partial row in part_dq
   float lse2, dcol;
   int plim;
   int en[2], men;
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dcol,
     const int* __restrict__ off, const int* __restrict__ entries, uint16_t* __restrict__ part_dq,
-    int64_t sink_row, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int batch, int n_q, int n_kv, int pos0,
+    int64_t sink_off, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int batch, int n_q, int n_kv, int pos0,
     int h_q, int h_kv, int nblk, int topk, float sl2, float scale) {
   constexpr int G = 1 << LOG2G;
   constexpr int DC = D / 8;                            // 16-byte chunks per row
@@ -206,33 +208,45 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
     const int st_id = tid % NST, which = st_id / (16 * DC), scp = (st_id % (16 * DC)) / DC, sch = st_id % DC;
     const int mcol = tid & 31;
     const uint16_t* src = which ? dout : q;
+    // Addresses are 32 x 32 -> 64-bit products of the token row T = b * n_q + t
+    // (< 2^31) and byte strides (< 2^32, checked on the host) onto per-lane
+    // bases.
+    const uint32_t tok0 = (uint32_t)b * (uint32_t)n_q;
+    const int* ent = entries + e0;
+    const uint32_t q_tok_bytes = (uint32_t)h_q * (D * 2);
+    const uint32_t pr_tok_elems = (uint32_t)h_q * (uint32_t)topk * D;
+    const char* src_lane = reinterpret_cast<const char*>(src) + ((size_t)g * G * D + sch * 8) * 2;
+    const uint32_t pdq_g = (uint32_t)(g * topk * G * D);
+    const float* lse_g = lse + g * G;
+    const float* dcol_g = dcol + g * G;
     // Every load of the loop reads a real row (the column index is clamped), so
     // the loop body has no memory operation behind a branch and the compiler's
     // wait counts stay exact across iterations; columns past the list end are
     // masked through plim = -1 and their dq goes to the sink row.
     auto entry_at = [&](int grp, int col) {
-      const int gc = min(grp * kBwdCols + col, ncols - 1);
-      return entries[e0 + (gc >> LOG2G)];
+      const uint32_t gc = (uint32_t)min(grp * kBwdCols + col, ncols - 1);
+      return ent[gc >> LOG2G];
     };
     auto fetch = [&](BwdStage& st, int grp) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int gc = min(grp * kBwdCols + 2 * scp + kk, ncols - 1);
-        const int64_t row = ((int64_t)b * n_q + entry_token(st.en[kk])) * h_q + g * G + (gc & (G - 1));
-        st.v[kk] = ld16(src + row * D + sch * 8);
+        const uint32_t hh = (uint32_t)min(grp * kBwdCols + 2 * scp + kk, ncols - 1) & (G - 1);
+        const uint32_t T = tok0 + (uint32_t)entry_token(st.en[kk]);
+        st.v[kk] = ld16(src_lane + hh * (D * 2) + (uint64_t)T * q_tok_bytes);
       }
       const int gc = grp * kBwdCols + mcol;
-      const int hh = min(gc, ncols - 1) & (G - 1);
+      const uint32_t hh = (uint32_t)min(gc, ncols - 1) & (G - 1);
       const int t = entry_token(st.men);
-      const int64_t row = ((int64_t)b * n_q + t) * h_q + g * G + hh;
-      st.lse2 = lse[row] * kLog2e;
-      st.dcol = dcol[row];
+      const uint32_t T = tok0 + (uint32_t)t;
+      const uint64_t row = (uint64_t)T * (uint32_t)h_q + hh;
+      st.lse2 = lse_g[row] * kLog2e;
+      st.dcol = dcol_g[row];
       // Selects by mask, not a ternary: a branch here would make the
       // compiler's wait counts at the loop head conservative.
-      const int64_t live = -(int64_t)(gc < ncols);
-      const int64_t pr = ((((int64_t)b * n_q + t) * h_kv + g) * topk + entry_slot(st.men)) * G + hh;
-      st.plim = (int)(((int64_t)(pos0 + t) & live) | (-1 & ~live));
-      st.prow = (pr & live) | (sink_row & ~live);
+      const uint64_t live = -(uint64_t)(gc < ncols);
+      const uint64_t pa = (uint64_t)T * pr_tok_elems + (pdq_g + ((uint32_t)entry_slot(st.men) * G + hh) * D);
+      st.plim = (int)(((uint32_t)(pos0 + t) & (uint32_t)live) | ~(uint32_t)live);
+      st.prow = (pa & live) | ((uint64_t)sink_off & ~live);
     };
     auto load_entries = [&](BwdStage& st, int grp) {
 #pragma unroll
@@ -325,11 +339,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc)
           acc = mfma_16x16x32(ktop[kc], ld16(&sm.g.ds[ds_off(16 * ct + m16, 32 * kc + 8 * q4)]), acc);
-        const int64_t prow = sm.g.prow[grp & 1][16 * ct + m16];
+        const uint64_t prow = sm.g.prow[grp & 1][16 * ct + m16];
         u32x2 o;
         o[0] = pack_bf16x2(acc[0] * scale, acc[1] * scale);
         o[1] = pack_bf16x2(acc[2] * scale, acc[3] * scale);
-        *reinterpret_cast<u32x2*>(part_dq + prow * D + 16 * dtw + 4 * q4) = o;
+        *reinterpret_cast<u32x2*>(part_dq + prow + 16 * dtw + 4 * q4) = o;
       }
     }
   }
@@ -414,7 +428,7 @@ hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, const uint16_t* k, con
   {
     LaunchTimer timer("sparse_bwd_kv", stream);
     hipLaunchKernelGGL((sparse_bwd_kv<D, LOG2G>), dim3((unsigned)L.lists), dim3(kBwdThreads), 0, stream, q, k, v,
-                       dout, lse, dcol, off, entries, part_dq, L.entries_max * G, dk, dv, d.batch, d.n_q, d.n_kv,
+                       dout, lse, dcol, off, entries, part_dq, L.entries_max * G * D, dk, dv, d.batch, d.n_q, d.n_kv,
                        d.pos0, d.h_q, d.h_kv, d.nblk(), d.topk, scale * kLog2e, scale);
   }
   if (nrows > 0) {

@@ -214,7 +214,8 @@ msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, co
  *   dk, dv    [batch][n_kv][h_kv][d] bf16, outputs, fully written (0 for keys
  *             no query saw, and for every key when n_q == 0).
  * Every key gradient is summed in one fixed order inside one workgroup, so the
- * results are deterministic.  Workspace: msa_workspace_size(
+ * results are deterministic.  block == 128 and h_q * topk * d < 2^31
+ * (MSA_ERR_UNSUPPORTED otherwise).  Workspace: msa_workspace_size(
  * MSA_OP_SPARSE_PREFILL, dims); do not share one workspace between this call
  * and a forward call in flight on another stream. */
 msa_status msa_sparse_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t* k,

@@ -231,6 +231,10 @@ def test_backward_argument_checks():
         assert call(d, **{n: ODD}) == ALIGN, n
     assert call(dims(h_q=6, h_kv=2)) == UNSUP
     assert call(dims(d=96)) == UNSUP
+    # h_q * topk * d must stay below 2^31 (32-bit byte strides of dq partial rows)
+    assert call(dims(batch=1, n_q=1, n_kv=128, pos0=0, h_q=262144, h_kv=16384, d=128, d_idx=128, topk=64)) == UNSUP
+    assert call(dims(batch=1, n_q=1, n_kv=128, pos0=0, h_q=131072, h_kv=8192, d=128, d_idx=128, topk=64),
+                wsb=0) == WS
     need = lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d))
     assert call(d, wsb=need - 1) == WS
     assert call(d, ws=None) == WS

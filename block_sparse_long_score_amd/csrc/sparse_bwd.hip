@@ -267,11 +267,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) st16(&rt[qd_off<D>(2 * scp + kk, sch)], st.v[kk]);
       }
-      // Every thread of a meta column writes the same values.
-      sm.g.plim[mcol] = st.plim;
-      sm.g.lse2[mcol] = st.lse2;
-      sm.g.dcol[mcol] = st.dcol;
-      sm.g.prow[grp & 1][mcol] = st.prow;
+      if (w == 0) {                                    // wave-uniform; lanes l and l + 32 agree
+        sm.g.plim[mcol] = st.plim;
+        sm.g.lse2[mcol] = st.lse2;
+        sm.g.dcol[mcol] = st.dcol;
+        sm.g.prow[grp & 1][mcol] = st.prow;
+      }
       __syncthreads();
       // The next group's rows, and the entries of the group after it.
       fetch(st, grp + 1);

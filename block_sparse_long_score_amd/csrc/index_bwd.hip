@@ -23,18 +23,23 @@ namespace {
 constexpr int kIbThreads = 512;
 constexpr int kIbCols = 32;                            // entries per group
 
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+// Max / min over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48): each gfx950 permlane swap exchanges halves between its two
+// operands, so op(result[0], result[1]) with the same value in both combines
+// every lane with its partner 16 (then 32) lanes away.
+__device__ __forceinline__ float rows_max(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = vmax(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
+  const int y = __builtin_bit_cast(int, v);
+  const auto c = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return vmax(__builtin_bit_cast(float, (int)c[0]), __builtin_bit_cast(float, (int)c[1]));
 }
-
-// Min over the 16 lanes of a row (the same DPP pattern as row_reduce).
-__device__ __forceinline__ int row_min16(int v) {
-  v = min(v, dpp_i<0xb1>(v));
-  v = min(v, dpp_i<0x4e>(v));
-  v = min(v, dpp_i<0x141>(v));
-  v = min(v, dpp_i<0x140>(v));
-  return v;
+__device__ __forceinline__ int rows_min(int v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min((int)a[0], (int)a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min((int)c[0], (int)c[1]);
 }
 
 // coef[row][s] for the live slots, 0 for the others; R lanes per row.
@@ -78,10 +83,11 @@ struct IbLds {
       uint16_t qr[2][kIbCols * DI];                    // [entry][d] index queries
       float coef[2][kIbCols];
       int plim[kIbCols];                               // last visible position, -1 for an empty column
-      int slot_row[kIbCols];                           // ((b * n_q + t) * h_kv + g) * topk + slot, -1 if empty
-      float wmax[8][kIbCols];
-      int wkey[8][kIbCols];
-      int amax[kIbCols];                               // argmax key in the block, -1 if empty
+      // ((b * n_q + t) * h_kv + g) * topk + slot, -1 if empty; by group parity
+      // (wave 0 publishes a group's argmax while faster waves stage the next).
+      int slot_row[2][kIbCols];
+      float wmax[8][kIbCols];                          // each wave's max per column
+      int wkey[8][kIbCols];                            // and the lowest key in the block that has it
     } g;
   };
   int lstart[kIbMaxLists + 1];                         // flat column where group g's list starts
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
       st16(&sm.g.qr[par][rt_off<DI>(scol, sch)], st.q);
       sm.g.coef[par][scol] = st.coef;
       sm.g.plim[scol] = st.plim;
-      sm.g.slot_row[scol] = st.srow;
+      sm.g.slot_row[par][scol] = st.srow;
       __syncthreads();
       {
         const int en = st.en_next, gn = st.g_next;
@@ -192,64 +198,65 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
         st.en_next = entry_at(grp + 4, g4);
         st.g_next = g4;
       }
-      // S^T for this wave's 16 keys: lane holds column 16*ct + 4*q4 + r.
+      // S^T for this wave's 16 keys with the key as the MFMA row (the resident
+      // key operand serves as A): lane holds keys 16*w + 4*q4 + r of column
+      // 16*ct + m16.
       f32x4 sacc[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < DI / 32; ++c)
-          sacc[ct] = mfma_16x16x32(ld16(&sm.g.qr[par][rt_off<DI>(16 * ct + m16, 4 * c + q4)]), kop[c], sacc[ct]);
+          sacc[ct] = mfma_16x16x32(kop[c], ld16(&sm.g.qr[par][rt_off<DI>(16 * ct + m16, 4 * c + q4)]), sacc[ct]);
       }
-      // Per column: the wave's max over its keys and the lowest key that has it.
+      // Per column: the wave's max over its 16 keys (4 in the lane, then over
+      // the lane's four rows) and the lowest key that has it.
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 2; ++ct) {
+        const int col = 16 * ct + m16;
+        const int lim = sm.g.plim[col] - (s0 + 16 * w + 4 * q4);   // key r visible when r <= lim
+        float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int col = 16 * ct + 4 * q4 + r;
-          const float v = skey <= sm.g.plim[col] ? sacc[ct][r] : -INFINITY;
-          const float m = row_reduce<16>(v, fmax);
-          const int kk = row_min16(v == m && m > -INFINITY ? mykey : 1 << 20);
-          if (m16 == 0) {
-            sm.g.wmax[w][col] = m;
-            sm.g.wkey[w][col] = kk;
-          }
+        for (int r = 0; r < 4; ++r) v[r] = r <= lim ? sacc[ct][r] : -INFINITY;
+        const float m = rows_max(vmax(vmax(v[0], v[1]), vmax(v[2], v[3])));
+        const int r0 = v[0] == m ? 0 : v[1] == m ? 1 : v[2] == m ? 2 : 3;
+        const int kk = rows_min(m > -INFINITY && v[r0] == m ? 16 * w + 4 * q4 + r0 : 1 << 20);
+        if (q4 == 0) {
+          sm.g.wmax[w][col] = m;
+          sm.g.wkey[w][col] = kk;
         }
+      }
       __syncthreads();
       // Across waves (ascending key ranges): the first wave that reaches the
-      // column's maximum holds its lowest argmax.  Wave 0 publishes it; its
-      // upper half stores to the sink slot.
-      if (w == 0) {
-        const int col = lane & 31;
-        float best = -INFINITY;
-        int key = -1;
+      // column's maximum holds its lowest argmax.  Every wave derives it for
+      // column lane & 31 (lanes l and l + 32 agree), so no barrier follows;
+      // wave 0 publishes it, its upper half storing to the sink slot.
+      const int colm = lane & 31;
+      float best = -INFINITY;
+      int key = -1;
 #pragma unroll
-        for (int ww = 0; ww < 8; ++ww) {
-          const float m = sm.g.wmax[ww][col];
-          key = m > best ? sm.g.wkey[ww][col] : key;
-          best = vmax(best, m);
-        }
-        const int sr = sm.g.slot_row[col];
-        key = sr < 0 ? -1 : key;
-        sm.g.amax[col] = key;
-        amax_out[(lane < 32 && sr >= 0) ? sr : sink] = key < 0 ? -1 : s0 + key;
+      for (int ww = 0; ww < 8; ++ww) {
+        const float m = sm.g.wmax[ww][colm];
+        key = m > best ? sm.g.wkey[ww][colm] : key;
+        best = vmax(best, m);
       }
-      __syncthreads();
+      const int sr = sm.g.slot_row[par][colm];
+      key = sr < 0 ? -1 : key;
+      if (w == 0) amax_out[(lane < 32 && sr >= 0) ? sr : sink] = key < 0 ? -1 : s0 + key;
       // dk_idx rows of this wave's keys, columns in list order: a ballot over
       // the 32 argmax keys picks this wave's columns.
       {
-        const int mine = sm.g.amax[lane & 31];
-        uint64_t hits = ballot(lane < kIbCols && (mine >> 4) == w);
+        uint64_t hits = ballot(lane < kIbCols && key >= 0 && (key >> 4) == w);
         while (hits) {
           const int col = __builtin_ctzll(hits);
           hits &= hits - 1;
-          const int key = __builtin_amdgcn_readfirstlane(sm.g.amax[col]);
+          const int kc = __builtin_amdgcn_readlane(key, col);
           const float cf = sm.g.coef[par][col];
 #pragma unroll
           for (int d0 = 0; d0 < DI; d0 += 64) {
             const int d = d0 + lane;
             const float qv = bf16_to_f32(sm.g.qr[par][rt_off<DI>(col, d >> 3) + (d & 7)]);
-            sm.dk[key * DI + d] = fmaf(cf, qv, sm.dk[key * DI + d]);
+            sm.dk[kc * DI + d] = fmaf(cf, qv, sm.dk[kc * DI + d]);
           }
         }
       }

@@ -37,8 +37,8 @@ KERNEL_SOURCES = {
     "sparse_kv_outer": ["sparse_attn.hip", "msa_device.h"],
     "merge_partials": ["sparse_attn.hip", "msa_device.h"],
     "sparse_decode_blocks": ["sparse_attn.hip", "msa_device.h"],
-    "block_topk_rows": ["block_topk.hip", "msa_device.h"],
-    "block_topk_wg": ["block_topk.hip", "msa_device.h"],
+    "block_topk_rows": ["block_topk.hip", "msa_select.h", "msa_device.h"],
+    "block_topk_wg": ["block_topk.hip", "msa_select.h", "msa_device.h"],
     "dense_prefill": ["dense_attn.hip", "msa_device.h"],
 }
 

@@ -240,3 +240,63 @@ def test_backward_full_size_prefill_128k_sampled():
             rv[pos[inb] - j * s.block] += gv[inb]
         check_grad(U.to64(dk[0, j * s.block:(j + 1) * s.block, g_dk]), rk, f"128k dk block {j}")
         check_grad(U.to64(dv[0, j * s.block:(j + 1) * s.block, g_dk]), rv, f"128k dv block {j}")
+
+
+def test_backward_query_rows_past_4_gib():
+    """Five sequences of 65,536 queries (h_q = 64, d = 128): the last
+    sequence's q, dout and dq rows start past byte 2^32 (token row T with
+    T * h_q * d * 2 > 2^32), so the backward's 32 x 32 -> 64-bit address
+    products carry into the upper word.  topk = 2 keeps the workspace near
+    11 GB.  dq on sampled rows of the last sequence, dk and dv on every key of
+    two whole blocks of one of its groups."""
+    from block_sparse_long_score_amd.inputs import sample_rows
+    s = Shape(5, 65536, 65536, 0, 64, 8, 128, 128, topk=2)
+    assert (s.batch - 1) * s.n_q * s.h_q * s.d * 2 >= 1 << 32
+    print(f"case rows_past_4_gib: {s}", flush=True)
+    inp = make_inputs(s, 41, device="cuda")
+    blk, bscore = U.run_index(s, inp["q_idx"], inp["k_idx"])
+    gen = torch.Generator(device="cuda").manual_seed(4141)
+    dout = torch.randn((s.batch, s.n_q, s.h_q, s.d), device="cuda", generator=gen).to(torch.bfloat16)
+    dq, dk, dv = run_backward(s, inp, blk, dout)
+    torch.cuda.synchronize()
+    print("  gpu done", flush=True)
+    b = s.batch - 1
+    scale = O.default_scale(s.d)
+    G = s.group
+    rows = [(b, t) for t in sample_rows(s.n_q, 6, 4142, [0, s.n_q - 1, 4095, 4096])]
+    kseq = U.to64(inp["k_idx"][b])
+    sels = U.check_index_rows(s, lambda bb, t: U.to64(inp["q_idx"][bb, t]), lambda bb: kseq, blk, bscore, rows)
+    keys64, vals64 = {}, {}
+
+    def kv(g):
+        if g not in keys64:
+            keys64[g], vals64[g] = U.to64(inp["k"][b, :, g]), U.to64(inp["v"][b, :, g])
+        return keys64[g], vals64[g]
+
+    ref_dq, got_dq, allow_dq = [], [], []
+    for (bb, t, g), sel in sels.items():
+        pos = O.visible_positions(sel, s.pos0 + t, s.block, s.n_kv)
+        kk, vv = kv(g)
+        qh, doh = U.to64(inp["q"][bb, t, g * G:(g + 1) * G]), U.to64(dout[bb, t, g * G:(g + 1) * G])
+        gq, _, _ = O.softmax_attention_grad(qh, kk[pos], vv[pos], doh, scale)
+        ref_dq.append(gq)
+        got_dq.append(U.to64(dq[bb, t, g * G:(g + 1) * G]))
+        allow_dq.append(dq_allow(qh, kk[pos], vv[pos], doh, scale, pos // s.block))
+    check_grad(np.stack(got_dq), np.stack(ref_dq), "rows past 4 GiB: dq rows", np.stack(allow_dq))
+    g_dk = 3
+    kk, vv = kv(g_dk)
+    blk_g = blk[b, :, g_dk].cpu().numpy()
+    for j in (7, s.nblk - 1):
+        ts = np.nonzero((blk_g == j).any(axis=1))[0]
+        print(f"  block {j}: {len(ts)} queries", flush=True)
+        rk = np.zeros((s.block, s.d))
+        rv = np.zeros((s.block, s.d))
+        for t in ts:
+            pos = O.visible_positions(blk_g[t], s.pos0 + t, s.block, s.n_kv)
+            _, gk, gv = O.softmax_attention_grad(U.to64(inp["q"][b, t, g_dk * G:(g_dk + 1) * G]), kk[pos], vv[pos],
+                                                 U.to64(dout[b, t, g_dk * G:(g_dk + 1) * G]), scale)
+            inb = (pos >= j * s.block) & (pos < (j + 1) * s.block)
+            rk[pos[inb] - j * s.block] += gk[inb]
+            rv[pos[inb] - j * s.block] += gv[inb]
+        check_grad(U.to64(dk[b, j * s.block:(j + 1) * s.block, g_dk]), rk, f"rows past 4 GiB: dk block {j}")
+        check_grad(U.to64(dv[b, j * s.block:(j + 1) * s.block, g_dk]), rv, f"rows past 4 GiB: dv block {j}")

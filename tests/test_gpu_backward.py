@@ -248,7 +248,8 @@ def test_backward_query_rows_past_4_gib():
     T * h_q * d * 2 > 2^32), so the backward's 32 x 32 -> 64-bit address
     products carry into the upper word.  topk = 2 keeps the workspace near
     11 GB.  dq on sampled rows of the last sequence, dk and dv on every key of
-    two whole blocks of one of its groups."""
+    two whole blocks of one of its groups, and the forward's output on the
+    same rows."""
     from block_sparse_long_score_amd.inputs import sample_rows
     s = Shape(5, 65536, 65536, 0, 64, 8, 128, 128, topk=2)
     assert (s.batch - 1) * s.n_q * s.h_q * s.d * 2 >= 1 << 32
@@ -266,6 +267,11 @@ def test_backward_query_rows_past_4_gib():
     rows = [(b, t) for t in sample_rows(s.n_q, 6, 4142, [0, s.n_q - 1, 4095, 4096])]
     kseq = U.to64(inp["k_idx"][b])
     sels = U.check_index_rows(s, lambda bb, t: U.to64(inp["q_idx"][bb, t]), lambda bb: kseq, blk, bscore, rows)
+    out, lse = U.run_sparse(s, inp["q"], inp["k"], inp["v"], blk)
+    chk = U.OutCheck("rows past 4 GiB: forward out")
+    U.check_sparse_rows(s, inp["q"], inp["k"], inp["v"], sels, out, lse, chk)
+    chk.verify()
+    del out, lse
     keys64, vals64 = {}, {}
 
     def kv(g):

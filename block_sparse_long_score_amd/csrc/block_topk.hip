@@ -185,12 +185,14 @@ __global__ __launch_bounds__(NW * 64) void block_topk_wg(const float* __restrict
     }
     if (lane == 0) cand_n[wave] = nq;
   } else {
+    // Loads clamped into the slice (nq > kk >= 1 here) so none is behind a
+    // branch: all V are in flight at once, then the tail is masked.
+    float f[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) f[i] = sc[q0 + min(i * 64 + lane, nq - 1)];
     uint32_t key[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int e = i * 64 + lane;
-      key[i] = (e < nq) ? order_key(sc[q0 + e]) : 0u;
-    }
+    for (int i = 0; i < V; ++i) key[i] = (i * 64 + lane < nq) ? order_key(f[i]) : 0u;
     wave_select<V>(key, kk, ck[wave], ci[wave], [&](int pos, uint32_t k, int e) {
       cand_k[wave][pos] = k;
       cand_i[wave][pos] = q0 + e;

@@ -60,9 +60,12 @@ __device__ __forceinline__ u32x2 ld_tr16(const uint16_t* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
   return __builtin_bit_cast(u32x2, v);
 }
-// dS tile [column][key]: 8-key chunk c of row col at c ^ (col & 15).
-__device__ __forceinline__ int ds_off(int col, int key) {
-  return col * kBlock + 8 * (((key >> 3) ^ col) & 15) + (key & 7);
+// dS tile [key][column]: 4-column (8-byte) chunk c of row key at
+// c ^ ((key >> 1) & 6).  The writes (lane: key 16*w + m16, chunk 4*ct + q4) and
+// the transposing reads of dq (lane: key 32*kc + 8*q4 + (m16 >> 2) (+ 4),
+// chunk 4*ct + (m16 & 3)) then each reach 32 distinct bank pairs per half-wave.
+__device__ __forceinline__ int ds_off(int key, int chunk) {
+  return key * kBwdCols + 4 * (chunk ^ ((key >> 1) & 6));
 }
 
 template <int D>
@@ -74,7 +77,7 @@ struct BwdLds {
     } kv;                                              // the block, while its operands are loaded
     struct {
       uint16_t qr[kBwdCols * D], dor[kBwdCols * D];    // [column][d], qd_off
-      uint16_t ds[kBwdCols * kBlock];                  // [column][key]
+      uint16_t ds[kBlock * kBwdCols];                  // [key][column], ds_off
       // Read as 16-byte vectors of 4 consecutive columns.
       alignas(16) float lse2[kBwdCols];
       alignas(16) float dcol[kBwdCols];
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
   constexpr int G = 1 << LOG2G;
   constexpr int DC = D / 8;                            // 16-byte chunks per row
   constexpr int DT = D / 16;                           // 16-wide d tiles
-  constexpr int CTW = D / 64;                          // column tiles of dq per wave
+  constexpr int NDT = DT / 4;                          // d tiles of dq per wave (one column tile)
   constexpr int NST = 2 * 16 * DC;                     // staging threads: 2-column tiles of q and dout
   __shared__ BwdLds<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -168,12 +171,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
     kop[c] = ld16(&sm.kv.k[rt_off<D>(mykey, 4 * c + q4)]);
     vop[c] = ld16(&sm.kv.v[rt_off<D>(mykey, 4 * c + q4)]);
   }
-  // A operand of dq: row (MFMA m) = d 16*dtw + m16, contraction slots = keys
-  // 32*kc + 8*q4 + i.
-  const int dtw = w % DT, ct0 = (w / DT) * CTW;
-  u32x4 ktop[4];
-  {
-    const int d = 16 * dtw + m16;
+  // dq: wave w forms column tile w >> 2 for d tiles dt0 .. dt0 + NDT - 1, so
+  // each dS operand it reads feeds NDT products.  A operands: row (MFMA m) =
+  // d 16*(dt0 + n) + m16, contraction slots = keys 32*kc + 8*q4 + i.
+  const int dct = w >> 2, dt0 = (w & 3) * NDT;
+  u32x4 ktop[NDT][4];
+#pragma unroll
+  for (int n = 0; n < NDT; ++n) {
+    const int d = 16 * (dt0 + n) + m16;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
         const int key = 32 * kc + 8 * q4 + 2 * i;
         const uint32_t lo = sm.kv.k[rt_off<D>(key, d >> 3) + (d & 7)];
         const uint32_t hi = sm.kv.k[rt_off<D>(key + 1, d >> 3) + (d & 7)];
-        ktop[kc][i] = lo | (hi << 16);
+        ktop[n][kc][i] = lo | (hi << 16);
       }
   }
   __syncthreads();                                     // the LDS now holds column groups
@@ -326,25 +331,33 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
       }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sm.g.ds[ds_off(16 * ct + 4 * q4 + r, mykey)] =
-              (uint16_t)((r & 1) ? (dsa[2 * ct + (r >> 1)] >> 16) : (dsa[2 * ct + (r >> 1)] & 0xffffu));
+        *reinterpret_cast<u32x2*>(&sm.g.ds[ds_off(mykey, 4 * ct + q4)]) = u32x2{dsa[2 * ct], dsa[2 * ct + 1]};
       __syncthreads();
 
-      // dq slice: rows d 16*dtw + 4*q4 + r of column 16*ct + m16.
+      // dq slice: rows d 16*(dt0 + n) + 4*q4 + r of column 16*dct + m16.
+      {
+        f32x4 acc[NDT];
 #pragma unroll
-      for (int i = 0; i < CTW; ++i) {
-        const int ct = ct0 + i;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NDT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // B operand (column n = 16*dct + m16, contraction slots = keys
+        // 32*kc + 8*q4 + i) by two transposing reads of keys +0..3 and +4..7.
+        const int dkey = 8 * q4 + (m16 >> 2), dch = 4 * dct + (m16 & 3);
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          acc = mfma_16x16x32(ktop[kc], ld16(&sm.g.ds[ds_off(16 * ct + m16, 32 * kc + 8 * q4)]), acc);
-        const uint64_t prow = sm.g.prow[grp & 1][16 * ct + m16];
-        u32x2 o;
-        o[0] = pack_bf16x2(acc[0] * scale, acc[1] * scale);
-        o[1] = pack_bf16x2(acc[2] * scale, acc[3] * scale);
-        *reinterpret_cast<u32x2*>(part_dq + prow + 16 * dtw + 4 * q4) = o;
+        for (int kc = 0; kc < 4; ++kc) {
+          const u32x2 lo = ld_tr16(&sm.g.ds[ds_off(32 * kc + dkey, dch)]);
+          const u32x2 hi = ld_tr16(&sm.g.ds[ds_off(32 * kc + dkey + 4, dch)]);
+          const u32x4 bop = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int n = 0; n < NDT; ++n) acc[n] = mfma_16x16x32(ktop[n][kc], bop, acc[n]);
+        }
+        const uint64_t prow = sm.g.prow[grp & 1][16 * dct + m16];
+#pragma unroll
+        for (int n = 0; n < NDT; ++n) {
+          u32x2 o;
+          o[0] = pack_bf16x2(acc[n][0] * scale, acc[n][1] * scale);
+          o[1] = pack_bf16x2(acc[n][2] * scale, acc[n][3] * scale);
+          *reinterpret_cast<u32x2*>(part_dq + prow + 16 * (dt0 + n) + 4 * q4) = o;
+        }
       }
     }
   }

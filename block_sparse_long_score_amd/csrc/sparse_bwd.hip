@@ -354,8 +354,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
 #pragma unroll
         for (int n = 0; n < NDT; ++n) {
           u32x2 o;
-          o[0] = pack_bf16x2(acc[n][0] * scale, acc[n][1] * scale);
-          o[1] = pack_bf16x2(acc[n][2] * scale, acc[n][3] * scale);
+          o[0] = pack_bf16x2(acc[n][0], acc[n][1]);
+          o[1] = pack_bf16x2(acc[n][2], acc[n][3]);
           *reinterpret_cast<u32x2*>(part_dq + prow + 16 * (dt0 + n) + 4 * q4) = o;
         }
       }
@@ -375,12 +375,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
   }
 }
 
-// dq[t, h] = sum over the live slots of the row's partials.  Every slot is
-// loaded from an in-row address and dead ones are dropped with selects.
+// dq[t, h] = scale * (sum over the live slots of the row's partials): the
+// partials hold sum dS k unscaled, so the scale costs one multiply per
+// element here instead of one per partial element.  Every slot is loaded from
+// an in-row address and dead ones are dropped with selects.
 template <int D, int G>
 __global__ __launch_bounds__(256) void sum_dq_partials(const uint16_t* __restrict__ part_dq,
                                                        const int32_t* __restrict__ blk, uint16_t* __restrict__ dq,
-                                                       int64_t nrows, int n_q, int pos0, int h_q, int topk) {
+                                                       int64_t nrows, int n_q, int pos0, int h_q, int topk,
+                                                       float scale) {
   constexpr int TPR = D / 8;
   const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // (b * n_q + t) * h_q + h
   if (row >= nrows) return;
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(256) void sum_dq_partials(const uint16_t* __restric
   }
   u32x4 r;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+  for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e] * scale, acc[2 * e + 1] * scale);
   st16(dq + row * D + dl * 8, r);
 }
 
@@ -448,7 +451,7 @@ hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, const uint16_t* k, con
   if (nrows > 0) {
     LaunchTimer timer("sum_dq_partials", stream);
     hipLaunchKernelGGL((sum_dq_partials<D, G>), dim3((unsigned)row_wgs), dim3(256), 0, stream, part_dq, blk, dq,
-                       nrows, d.n_q, d.pos0, d.h_q, d.topk);
+                       nrows, d.n_q, d.pos0, d.h_q, d.topk, scale);
   }
   return hipGetLastError();
 }

@@ -9,11 +9,19 @@
 // gradient goes to its argmax token s* (the lowest position among equal
 // maxima):  dq_idx[row] += coef_s k_idx[s*],  dk_idx[s*] += coef_s q_idx[row].
 //
-// Three kernels: the per-row coefficients; a KV-outer pass, one workgroup per
-// (b, block), that recomputes the scores of every entry of the block's lists
-// (all groups share the index key) by MFMA, takes each entry's argmax and
-// accumulates dk_idx for the block's keys in LDS in list order (deterministic,
-// no atomics); and a per-row gather for dq_idx.
+// Kernels: the per-row coefficients; a KV-outer pass over (b, block) work
+// items that recomputes the scores of every entry of the block's lists (all
+// groups share the index key) by MFMA, takes each entry's argmax and
+// accumulates dk_idx for the block's keys on MFMA in registers, group by group
+// in list order; and a per-row gather for dq_idx.  A causal prefill's earliest
+// blocks are chosen by most later queries, so their lists hold several times
+// the average work of a CU: such a block is cut into up to kIbMaxPieces pieces
+// of consecutive column groups, the first writing dk_idx and the others a
+// partial that index_dk_combine adds in piece order.  The pass is persistent
+// (one workgroup per CU taking items from a counter, earliest blocks first):
+// launching one workgroup per item left CUs idle for tens of microseconds
+// between items.  Every sum runs in a fixed order, so results are
+// deterministic without atomics on the data.
 #include "launch.h"
 #include "msa_device.h"
 
@@ -22,6 +30,12 @@ namespace {
 
 constexpr int kIbThreads = 512;
 constexpr int kIbCols = 32;                            // entries per group
+// A block whose lists hold many column groups is split into up to
+// kIbMaxPieces workgroups of at least kIbPieceGroups groups each (a causal
+// prefill's earliest blocks are chosen by most later queries: their lists are
+// several times the average work per CU).
+constexpr int kIbMaxPieces = 8;
+constexpr int kIbPieceGroups = 128;
 
 // Max / min over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32,
 // l ^ 48): each gfx950 permlane swap exchanges halves between its two
@@ -74,13 +88,12 @@ constexpr int kIbMaxLists = 128;                       // h_kv <= 128
 
 template <int DI>
 struct IbLds {
-  float dk[kBlock * DI];                               // dk_idx of the block's keys
   union {
     uint16_t k[kBlock * DI];                           // the block's index keys, while loaded
     struct {
       // q rows and coefficients by group parity: the dk phase of one group
       // reads them while faster waves already stage the next group.
-      uint16_t qr[2][kIbCols * DI];                    // [entry][d] index queries
+      uint16_t qr[2][kIbCols * DI];                    // [entry][d] index queries, qd_off
       float coef[2][kIbCols];
       int plim[kIbCols];                               // last visible position, -1 for an empty column
       // ((b * n_q + t) * h_kv + g) * topk + slot, -1 if empty; by group parity
@@ -88,10 +101,14 @@ struct IbLds {
       int slot_row[2][kIbCols];
       float wmax[8][kIbCols];                          // each wave's max per column
       int wkey[8][kIbCols];                            // and the lowest key in the block that has it
+      // Per wave, per column: the coefficient as hi | mid << 16 and
+      // lo | key << 16 (three bf16 terms; key -1 when the column has none).
+      uint32_t whm[8][kIbCols], wlk[8][kIbCols];
     } g;
   };
-  int lstart[kIbMaxLists + 1];                         // flat column where group g's list starts
+  int lstart[kIbMaxLists];                             // flat column where group g's list starts
   int lbase[kIbMaxLists];                              // its first entry
+  int item;                                            // the work item being processed
 };
 
 // One column group in flight: this thread's 16-byte chunk of its column's
@@ -103,21 +120,43 @@ struct IbStage {
   int plim, srow, en_next, g_next;
 };
 
+// Bits of the bf16 nearest to x (round to nearest even).
+__device__ __forceinline__ uint32_t bf16_rn(float x) { return pack_bf16x2(x, 0.f) & 0xffffu; }
+
+// Column groups of the (b, block) lists of all groups, and the pieces they
+// are split into (1 .. npmax).
+__device__ __forceinline__ int ib_pieces(int ngroups, int npmax) {
+  return max(1, min(npmax, ngroups / kIbPieceGroups));
+}
+
+// One work item: piece `piece` of the (b, block) lists jb = block * batch + b.
 template <int DI>
-__global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const int* __restrict__ off,
-    const int* __restrict__ entries, const float* __restrict__ coef, int* __restrict__ amax_out, int sink,
-    float* __restrict__ dk_idx, int batch, int n_q, int n_kv, int pos0, int h_kv, int nblk, int topk) {
+__device__ __forceinline__ void ib_item(
+    IbLds<DI>& sm, const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    const int* __restrict__ off, const int* __restrict__ entries, const float* __restrict__ coef,
+    int* __restrict__ amax_out, int sink, float* __restrict__ dk_idx, float* __restrict__ dk_part, int npmax,
+    int batch, int n_q, int n_kv, int pos0, int h_kv, int nblk, int topk, int jb, int piece) {
   constexpr int DC = DI / 8;
+  constexpr int DT = DI / 16;                          // 16-wide d tiles of dk_idx
   constexpr int NST = kIbCols * DC;                    // staging threads (one chunk each)
-  __shared__ IbLds<DI> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m16 = lane & 15, q4 = lane >> 4;
-  const int j = blockIdx.x / batch, b = blockIdx.x % batch;   // early blocks (most entries) first
+  const int j = jb / batch, b = jb % batch;
   const int s0 = j * kBlock;
+  // Columns of the block's lists (uniform loads), and this workgroup's share.
+  int ncols = 0;
+  for (int g = 0; g < h_kv; ++g) {
+    const int list = (b * h_kv + g) * nblk + j;
+    ncols += off[list + 1] - off[list];
+  }
+  const int ngroups_all = (ncols + kIbCols - 1) / kIbCols;
+  const int npieces = ib_pieces(ngroups_all, npmax);
+  if (piece >= npieces) return;                        // workgroup-uniform: nothing of this block is left
+  const int per = (ngroups_all + npieces - 1) / npieces;
+  const int grp0 = piece * per;
+  const int ngroups = max(0, min(ngroups_all, grp0 + per) - grp0);
   const uint16_t* kb = k_idx + (int64_t)b * n_kv * DI;
 
-  for (int i = tid; i < kBlock * DI; i += kIbThreads) sm.dk[i] = 0.f;
   for (int it = tid; it < kBlock * DC; it += kIbThreads) {
     const int key = it / DC, ch = it % DC, s = s0 + key;
     st16(&sm.k[rt_off<DI>(key, ch)], s < n_kv ? ld16(kb + (int64_t)s * DI + ch * 8) : u32x4{0u, 0u, 0u, 0u});
@@ -130,28 +169,38 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
       sm.lbase[g] = off[list];
       run += off[list + 1] - off[list];
     }
-    sm.lstart[h_kv] = run;
   }
   __syncthreads();
-  // B operands of S^T: column (MFMA n) = this lane's key, contraction slots
+  // A operands of S^T: row (MFMA m) = this lane's key, contraction slots
   // 8*q4 + i = d 32*c + 8*q4 + i.
   const int mykey = 16 * w + m16;
   u32x4 kop[DI / 32];
 #pragma unroll
   for (int c = 0; c < DI / 32; ++c) kop[c] = ld16(&sm.k[rt_off<DI>(mykey, 4 * c + q4)]);
-  const int ncols = sm.lstart[h_kv];
   __syncthreads();                                     // the LDS now holds entry groups
-  const int skey = s0 + mykey;
-  const int ngroups = (ncols + kIbCols - 1) / kIbCols;
+  // dk_idx of this wave's 16 keys: lane holds keys 16*w + 4*q4 + r, d 16*dt + m16.
+  f32x4 dka[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dka[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (ngroups > 0) {
     // Staging role: column scol of each group, chunk sch of its query.
     // Threads beyond NST (d_idx = 64) mirror the first NST.
     const int st_id = tid % NST, scol = st_id / DC, sch = st_id % DC;
+    // Transposing-read offsets of the dk products (B operand: column n = d
+    // 16*dt + m16, contraction slot 8*q4 + i <-> column 4*q4 + i (i < 4) or
+    // 16 + 4*q4 + i - 4 (i >= 4)): rows 4*q4 + (m16 >> 2) and 16 + ..., chunk
+    // 2*dt + ((m16 & 3) >> 1), element 4*(m16 & 1).
+    const int tr_r1 = 4 * q4 + (m16 >> 2), tr_r2 = tr_r1 + 16;
+    const int tr_row1 = tr_r1 * DI, tr_row2 = tr_r2 * DI;
+    const int tr_x1 = qd_swz<DI>(tr_r1) ^ ((m16 & 3) >> 1), tr_x2 = qd_swz<DI>(tr_r2) ^ ((m16 & 3) >> 1);
+    const int tr_e = 4 * (m16 & 1);
     // Flat column f -> (entry value, group); f is clamped to a real column,
     // so no load of the loop sits behind a branch.
+    // Groups are numbered from this piece's first one (grp0).
+    const int cend = min(ncols, (grp0 + ngroups) * kIbCols);   // this piece's columns end here
     auto entry_at = [&](int grp, int& gout) {
-      const int f = min(grp * kIbCols + scol, ncols - 1);
+      const int f = min((grp0 + grp) * kIbCols + scol, cend - 1);
       int lo = 0, hi = h_kv;                           // largest g with lstart[g] <= f
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -163,7 +212,7 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
     };
     auto fetch = [&](IbStage& st, int grp, int en, int gc) {
       const int t = entry_token(en);
-      const bool live = grp * kIbCols + scol < ncols;
+      const bool live = (grp0 + grp) * kIbCols + scol < cend;
       const int64_t qrow = ((int64_t)b * n_q + t) * h_kv + gc;
       const int sr = (int)(qrow * topk + entry_slot(en));
       st.q = ld16(q_idx + qrow * DI + sch * 8);
@@ -182,11 +231,10 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
       sy.en_next = entry_at(3, g3);
       sy.g_next = g3;
     }
-    const auto fmax = [](float x, float y) { return vmax(x, y); };
     auto step = [&](IbStage& st, int grp) {
       const int par = grp & 1;
       // Every thread of a column writes the same per-column values.
-      st16(&sm.g.qr[par][rt_off<DI>(scol, sch)], st.q);
+      st16(&sm.g.qr[par][qd_off<DI>(scol, sch)], st.q);
       sm.g.coef[par][scol] = st.coef;
       sm.g.plim[scol] = st.plim;
       sm.g.slot_row[par][scol] = st.srow;
@@ -207,7 +255,7 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
         sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < DI / 32; ++c)
-          sacc[ct] = mfma_16x16x32(kop[c], ld16(&sm.g.qr[par][rt_off<DI>(16 * ct + m16, 4 * c + q4)]), sacc[ct]);
+          sacc[ct] = mfma_16x16x32(kop[c], ld16(&sm.g.qr[par][qd_off<DI>(16 * ct + m16, 4 * c + q4)]), sacc[ct]);
       }
       // Per column: the wave's max over its 16 keys (4 in the lane, then over
       // the lane's four rows) and the lowest key that has it.
@@ -243,22 +291,52 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
       const int sr = sm.g.slot_row[par][colm];
       key = sr < 0 ? -1 : key;
       if (w == 0) amax_out[(lane < 32 && sr >= 0) ? sr : sink] = key < 0 ? -1 : s0 + key;
-      // dk_idx rows of this wave's keys, columns in list order: a ballot over
-      // the 32 argmax keys picks this wave's columns.
+      // dk_idx[key] += coef q for each column, as one product per group: A
+      // (this wave's 16 keys x the 32 columns) holds a column's coefficient in
+      // its argmax key's row and 0 elsewhere, B is the column's index query.
+      // The fp32 coefficient is split exactly enough into three bf16 terms
+      // (hi + mid + lo within 2^-27 of it), and bf16 x bf16 products are exact
+      // in fp32, so the sum keeps fp32 accuracy.  Each wave writes its own
+      // copy of the per-column values (no barrier: one wave's LDS operations
+      // complete in order).
       {
-        uint64_t hits = ballot(lane < kIbCols && key >= 0 && (key >> 4) == w);
-        while (hits) {
-          const int col = __builtin_ctzll(hits);
-          hits &= hits - 1;
-          const int kc = __builtin_amdgcn_readlane(key, col);
-          const float cf = sm.g.coef[par][col];
-#pragma unroll
-          for (int d0 = 0; d0 < DI; d0 += 64) {
-            const int d = d0 + lane;
-            const float qv = bf16_to_f32(sm.g.qr[par][rt_off<DI>(col, d >> 3) + (d & 7)]);
-            sm.dk[kc * DI + d] = fmaf(cf, qv, sm.dk[kc * DI + d]);
-          }
+        const float cf = sm.g.coef[par][colm];
+        const uint32_t hi = bf16_rn(cf);
+        const float r1 = cf - bf16_to_f32(hi);
+        const uint32_t mid = bf16_rn(r1);
+        const uint32_t lo = bf16_rn(r1 - bf16_to_f32(mid));
+        if (lane < kIbCols) {
+          sm.g.whm[w][colm] = hi | (mid << 16);
+          sm.g.wlk[w][colm] = lo | ((uint32_t)key << 16);
         }
+      }
+      const u32x4 hm0 = *reinterpret_cast<const u32x4*>(&sm.g.whm[w][4 * q4]);
+      const u32x4 hm1 = *reinterpret_cast<const u32x4*>(&sm.g.whm[w][16 + 4 * q4]);
+      const u32x4 lk0 = *reinterpret_cast<const u32x4*>(&sm.g.wlk[w][4 * q4]);
+      const u32x4 lk1 = *reinterpret_cast<const u32x4*>(&sm.g.wlk[w][16 + 4 * q4]);
+      // Slot pair (2p, 2p + 1) of the A operands: columns of hm/lk elements
+      // 2p', 2p' + 1 of the first (p < 2) or second (p >= 2) half.
+      u32x4 ahi, amid, alo;
+      const uint32_t me = (uint32_t)mykey;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const u32x4& hm = p < 2 ? hm0 : hm1;
+        const u32x4& lk = p < 2 ? lk0 : lk1;
+        const int e0 = 2 * (p & 1), e1 = e0 + 1;
+        const uint32_t mask = ((lk[e0] >> 16) == me ? 0x0000ffffu : 0u) | ((lk[e1] >> 16) == me ? 0xffff0000u : 0u);
+        ahi[p] = ((hm[e0] & 0xffffu) | (hm[e1] << 16)) & mask;
+        amid[p] = ((hm[e0] >> 16) | (hm[e1] & 0xffff0000u)) & mask;
+        alo[p] = ((lk[e0] & 0xffffu) | (lk[e1] << 16)) & mask;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int o1 = tr_row1 + 8 * ((2 * dt) ^ tr_x1) + tr_e;
+        const int o2 = tr_row2 + 8 * ((2 * dt) ^ tr_x2) + tr_e;
+        const u32x2 qlo = ld_tr16(&sm.g.qr[par][o1]), qhi = ld_tr16(&sm.g.qr[par][o2]);
+        const u32x4 qb = {qlo[0], qlo[1], qhi[0], qhi[1]};
+        dka[dt] = mfma_16x16x32(ahi, qb, dka[dt]);
+        dka[dt] = mfma_16x16x32(amid, qb, dka[dt]);
+        dka[dt] = mfma_16x16x32(alo, qb, dka[dt]);
       }
     };
     __builtin_amdgcn_s_waitcnt(0);                     // drain the prologue (exact waits in the loop)
@@ -267,10 +345,117 @@ __global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
       step(sy, grp + 1);
     }
   }
+  // Rows 16*w + 4*q4 + r, d 16*dt + m16: piece 0 into dk_idx, the others into
+  // their partial slot (summed in piece order by index_dk_combine).
+  if (piece == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = s0 + 16 * w + 4 * q4 + r;
+      if (s >= n_kv) continue;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dk_idx[((int64_t)b * n_kv + s) * DI + 16 * dt + m16] = dka[dt][r];
+    }
+  } else {
+    float* dst = dk_part + ((((int64_t)(piece - 1) * batch + b) * nblk + j) * kBlock) * DI;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dst[(16 * w + 4 * q4 + r) * DI + 16 * dt + m16] = dka[dt][r];
+  }
+}
+
+// Persistent: one workgroup per CU takes work items (block, piece) in order,
+// earliest blocks first, from a counter that the launch zeroes beforehand
+// (one vector atomic per item, broadcast through LDS).  Every wave of a
+// workgroup sees the same item, so all leave the loop together once the
+// items run out.
+template <int DI>
+__global__ __launch_bounds__(kIbThreads, 1) void index_bwd_kv(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const int* __restrict__ off,
+    const int* __restrict__ entries, const float* __restrict__ coef, int* __restrict__ amax_out, int sink,
+    float* __restrict__ dk_idx, float* __restrict__ dk_part, int npmax, int batch, int n_q, int n_kv, int pos0,
+    int h_kv, int nblk, int topk, int* __restrict__ counter, const int* __restrict__ items) {
+  __shared__ IbLds<DI> sm;
+  const int nitems = items[0];
+  for (;;) {
+    if (threadIdx.x == 0) sm.item = atomicAdd(counter, 1);
+    __syncthreads();
+    const int v = sm.item;
+    if (v >= nitems) break;
+    const int it = items[1 + v];
+    ib_item<DI>(sm, q_idx, k_idx, off, entries, coef, amax_out, sink, dk_idx, dk_part, npmax, batch, n_q, n_kv,
+                pos0, h_kv, nblk, topk, it / npmax, it % npmax);
+    __syncthreads();                                   // the next item reuses the LDS
+  }
+}
+
+// The work items of index_bwd_kv: for every (b, block) in order (earliest
+// blocks first) its pieces jb * npmax + p, p < npieces, after the count in
+// items[0]; also zeroes the item counter.  One workgroup: each thread takes
+// a contiguous run of blocks, and a scan over the threads places them.
+constexpr int kPlanThreads = 1024;
+__global__ __launch_bounds__(kPlanThreads) void ib_plan(const int* __restrict__ off, int* __restrict__ counter,
+                                                          int* __restrict__ items, int npmax, int batch, int h_kv,
+                                                          int nblk) {
+  __shared__ int part[kPlanThreads];
+  const int tid = threadIdx.x;
+  const int nb = batch * nblk;
+  const int per = (nb + kPlanThreads - 1) / kPlanThreads;
+  const int jb0 = min(nb, tid * per), jb1 = min(nb, jb0 + per);
+  auto pieces = [&](int jb) {
+    const int j = jb / batch, b = jb % batch;
+    int ncols = 0;
+    for (int g = 0; g < h_kv; ++g) {
+      const int list = (b * h_kv + g) * nblk + j;
+      ncols += off[list + 1] - off[list];
+    }
+    return ib_pieces((ncols + kIbCols - 1) / kIbCols, npmax);
+  };
+  int mine = 0;
+  for (int jb = jb0; jb < jb1; ++jb) mine += pieces(jb);
+  part[tid] = mine;
   __syncthreads();
-  for (int i = tid; i < kBlock * DI; i += kIbThreads) {
-    const int s = s0 + i / DI;
-    if (s < n_kv) dk_idx[((int64_t)b * n_kv + s) * DI + (i % DI)] = sm.dk[i];
+  for (int d = 1; d < kPlanThreads; d <<= 1) {         // inclusive scan
+    const int x = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += x;
+    __syncthreads();
+  }
+  int at = part[tid] - mine;
+  for (int jb = jb0; jb < jb1; ++jb) {
+    const int np = pieces(jb);
+    for (int p = 0; p < np; ++p) items[1 + at + p] = jb * npmax + p;
+    at += np;
+  }
+  if (tid == kPlanThreads - 1) items[0] = part[tid];
+  if (tid == 0) *counter = 0;
+}
+
+// dk_idx of a split block += its pieces 1 .. npieces - 1, in piece order.
+// One workgroup per (b, block); blocks with one piece return at once.
+template <int DI>
+__global__ __launch_bounds__(256) void index_dk_combine(const int* __restrict__ off,
+                                                        const float* __restrict__ dk_part,
+                                                        float* __restrict__ dk_idx, int npmax, int batch,
+                                                        int n_kv, int h_kv, int nblk) {
+  const int j = blockIdx.x / batch, b = blockIdx.x % batch;
+  int ncols = 0;
+  for (int g = 0; g < h_kv; ++g) {
+    const int list = (b * h_kv + g) * nblk + j;
+    ncols += off[list + 1] - off[list];
+  }
+  const int npieces = ib_pieces((ncols + kIbCols - 1) / kIbCols, npmax);
+  if (npieces == 1) return;
+  const int s0 = j * kBlock;
+  const int keys = min(kBlock, n_kv - s0);
+  for (int i = threadIdx.x; i < keys * (DI / 4); i += 256) {
+    const int key = i / (DI / 4), d4 = i % (DI / 4);
+    f32x4* dst = reinterpret_cast<f32x4*>(dk_idx + ((int64_t)b * n_kv + s0 + key) * DI) + d4;
+    f32x4 acc = *dst;
+    for (int p = 1; p < npieces; ++p)
+      acc += *(reinterpret_cast<const f32x4*>(
+                  dk_part + ((((int64_t)(p - 1) * batch + b) * nblk + j) * kBlock + key) * DI) + d4);
+    *dst = acc;
   }
 }
 
@@ -333,11 +518,34 @@ hipError_t launch_index_bwd_t(const Dims& d, const uint16_t* q_idx, const uint16
   }
   hipError_t e = launch_csr(d, blk, ws, stream, true);    // sums run in list order
   if (e != hipSuccess) return e;
+  // Partial dk_idx of split blocks: after the argmax slots in the partial
+  // region, as many pieces per block as fit (at most kIbMaxPieces).
+  const size_t amax_bytes = align_up(sizeof(int) * (size_t)(nrows * d.topk + 1), 256);
+  const size_t region = (size_t)(L.entries_max + 1) * d.group() * d.d * 2;
+  const size_t per_piece = (size_t)d.batch * d.nblk() * kBlock * DI * sizeof(float);
+  int npmax = kIbMaxPieces;
+  auto items_size = [&](int np) { return align_up(sizeof(int) * (1 + (size_t)d.batch * d.nblk() * np), 256); };
+  while (npmax > 1 && amax_bytes + 256 + items_size(npmax) + (size_t)(npmax - 1) * per_piece > region) npmax /= 2;
+  const size_t items_bytes = items_size(npmax);
+  int* counter = reinterpret_cast<int*>(base + L.part_o + amax_bytes);
+  int* items = reinterpret_cast<int*>(base + L.part_o + amax_bytes + 256);
+  float* dk_part = reinterpret_cast<float*>(base + L.part_o + amax_bytes + 256 + items_bytes);
+  const int nitems_max = d.batch * d.nblk() * npmax;
+  {
+    LaunchTimer timer("ib_plan", stream);
+    hipLaunchKernelGGL(ib_plan, dim3(1), dim3(kPlanThreads), 0, stream, off, counter, items, npmax, d.batch, d.h_kv,
+                       d.nblk());
+  }
   {
     LaunchTimer timer("index_bwd_kv", stream);
-    hipLaunchKernelGGL(index_bwd_kv<DI>, dim3((unsigned)(d.batch * d.nblk())), dim3(kIbThreads), 0, stream, q_idx,
-                       k_idx, off, entries, coef, amax, (int)(nrows * d.topk), dk_idx, d.batch, d.n_q, d.n_kv,
-                       d.pos0, d.h_kv, d.nblk(), d.topk);
+    hipLaunchKernelGGL(index_bwd_kv<DI>, dim3((unsigned)min(device_cu_count(), nitems_max)), dim3(kIbThreads), 0,
+                       stream, q_idx, k_idx, off, entries, coef, amax, (int)(nrows * d.topk), dk_idx, dk_part, npmax,
+                       d.batch, d.n_q, d.n_kv, d.pos0, d.h_kv, d.nblk(), d.topk, counter, items);
+  }
+  if (npmax > 1) {
+    LaunchTimer timer("index_dk_combine", stream);
+    hipLaunchKernelGGL(index_dk_combine<DI>, dim3((unsigned)(d.batch * d.nblk())), dim3(256), 0, stream, off,
+                       dk_part, dk_idx, npmax, d.batch, d.n_kv, d.h_kv, d.nblk());
   }
   if (nrows > 0) {
     constexpr int TPR = DI / 8;

@@ -122,6 +122,41 @@ __device__ __forceinline__ int row_swz(int r) { return D == 128 ? (r & 15) : ((r
 template <int D>
 __device__ __forceinline__ int rt_off(int r, int chunk) { return r * D + 8 * (chunk ^ row_swz<D>(r)); }
 
+// Row-major [column][d] tiles of query-side rows (q, dout, index queries) read
+// both as MFMA rows and, transposed, as contraction rows: 16-byte chunk c of
+// row r sits at c ^ qd_swz(r).  The LDS has 64 four-byte banks; an 8-byte read (the
+// transposing one included) serves lanes 0-31 in one cycle and 32-63 in the
+// next, a 16-byte read serves in each cycle the 16 lanes with the same lane
+// index mod 4 (measured with the bank-conflict counter).  Two reads use these
+// tiles.  The S^T / dP^T operands: lane (q4, m16) reads row 16*ct + m16 at
+// chunk 4*c + q4, so for rows with equal bits 0-1, bits 2-3 of qd_swz must be a
+// bijection of row bits 2-3.  The dV / dK operands (transposing reads): lane
+// (q4, m16) reads row 4*q4 + (m16 >> 2) (+ 16) at chunk 2*dt + ((m16 & 3) >> 1),
+// so for rows with equal bit 3, bits 1-3 of qd_swz must be a bijection of row
+// bits 0-2.  With s0 = r3, s1 = r0, s2 = r1 ^ r2, s3 = r2 ^ r3 (d = 128) both
+// hold, and neither read has a bank conflict.  For d = 64 (rows of 128 bytes,
+// the row parity picks the half of the banks) the transposing reads are free of
+// conflicts and the S^T / dP^T reads conflict 2-way, as with any swizzle.
+template <int D>
+__device__ __forceinline__ int qd_swz(int r) {
+  if (D == 128)
+    return ((r >> 3) & 1) | ((r & 1) << 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 3);
+  return ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int qd_off(int r, int chunk) { return r * D + 8 * (chunk ^ qd_swz<D>(r)); }
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element i & 3 of the 8 bytes that lane 4r + (i >> 2)
+// addresses, as its element r (r = 0..3).
+__device__ __forceinline__ u32x2 ld_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 
 
 // Number of set bits of `mask` in lanes below this one.

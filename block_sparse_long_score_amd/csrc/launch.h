@@ -41,7 +41,7 @@ struct Dims {
 // Sparse-prefill workspace: CSR inversion of the block selection plus the
 // per-(query, group, slot) partial softmax results.  Offsets in bytes.
 struct PrefillWs {
-  size_t cnt, off, ccnt, entries, part_o, part_ml, total;
+  size_t cnt, off, ccnt, entries, part_o, part_ml, counter, total;
   int64_t lists, chunks, entries_max;
 };
 PrefillWs prefill_ws_layout(const Dims& d);

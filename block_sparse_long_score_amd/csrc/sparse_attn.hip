@@ -856,6 +856,7 @@ PrefillWs prefill_ws_layout(const Dims& d) {
   // partials per (entry, head), plus one sink row of G heads for idle columns
   L.part_o = take((size_t)(L.entries_max + 1) * d.group() * d.d * 2);
   L.part_ml = take((size_t)(L.entries_max + 1) * d.group() * 2 * sizeof(float));
+  L.counter = take(sizeof(int));                       // work-item counter of persistent kernels
   L.total = o;
   return L;
 }

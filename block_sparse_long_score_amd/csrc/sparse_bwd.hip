@@ -7,7 +7,8 @@
 //   dq    = scale sum_s dS k[s],   dk[s] = scale sum dS q.
 //
 // KV-outer, like the forward (lumi-systems summary: KV-outer sparse attention):
-// one workgroup per (b, g, block) list of the CSR inversion.  Its eight waves
+// one workgroup at a time per (b, g, block) list of the CSR inversion (a
+// persistent workgroup per CU takes the lists in order).  Its eight waves
 // each own 16 keys of the block: they keep those keys' K and V rows as MFMA
 // operands in registers, and their dk / dv rows as fp32 accumulators for the
 // whole list, so every key gradient is summed inside one workgroup in a fixed
@@ -57,6 +58,7 @@ struct BwdLds {
       uint64_t prow[2][kBwdCols];
     } g;
   };
+  int item;                                            // the list being processed
 };
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16x2(x, 0.f) & 0xffffu; }
@@ -94,25 +96,29 @@ struct BwdStage {
   int en[2], men;
 };
 
+// One (b, g, block) list; `item` numbers the lists block-major.
 template <int D, int LOG2G>
-__global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+__device__ __forceinline__ void bwd_list(
+    BwdLds<D>& sm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dcol,
     const int* __restrict__ off, const int* __restrict__ entries, uint16_t* __restrict__ part_dq,
     int64_t sink_off, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int batch, int n_q, int n_kv, int pos0,
-    int h_q, int h_kv, int nblk, int topk, float sl2, float scale) {
+    int h_q, int h_kv, int nblk, int topk, float sl2, float scale, int item) {
   constexpr int G = 1 << LOG2G;
   constexpr int DC = D / 8;                            // 16-byte chunks per row
   constexpr int DT = D / 16;                           // 16-wide d tiles
   constexpr int NDT = DT / 4;                          // d tiles of dq per wave (one column tile)
   constexpr int NST = 2 * 16 * DC;                     // staging threads: 2-column tiles of q and dout
-  __shared__ BwdLds<D> sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The thread index passes through an empty asm so that what derives from it
+  // is recomputed per list instead of being held across the whole loop.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, w = tid >> 6;
   const int m16 = lane & 15, q4 = lane >> 4;
-  // Grid order: block index outermost, so the earliest blocks (candidates for
-  // the most queries) start first.
+  // Block index outermost, so the earliest blocks (candidates for the most
+  // queries) start first.
   const int bgs = batch * h_kv;
-  const int j = blockIdx.x / bgs, bg = blockIdx.x % bgs;
+  const int j = item / bgs, bg = item % bgs;
   const int g = bg % h_kv, b = bg / h_kv;
   const int list = bg * nblk + j;
   const int e0 = off[list], e1 = off[list + 1];
@@ -342,6 +348,32 @@ __global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
   }
 }
 
+// Persistent: one workgroup per CU takes the lists in order from a counter
+// that the launch zeroes beforehand (one vector atomic per list, broadcast
+// through LDS); launching one workgroup per list left CUs idle between
+// workgroups.  Every wave of a workgroup sees the same item, so all leave the
+// loop together.
+template <int D, int LOG2G>
+__global__ __launch_bounds__(kBwdThreads, 1) void sparse_bwd_kv(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dcol,
+    const int* __restrict__ off, const int* __restrict__ entries, uint16_t* __restrict__ part_dq,
+    int64_t sink_off, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int batch, int n_q, int n_kv, int pos0,
+    int h_q, int h_kv, int nblk, int topk, float sl2, float scale, int* __restrict__ counter, int nlists) {
+  __shared__ BwdLds<D> sm;
+  for (;;) {
+    if (threadIdx.x == 0) sm.item = atomicAdd(counter, 1);
+    __syncthreads();
+    const int item = sm.item;
+    if (item >= nlists) break;
+    bwd_list<D, LOG2G>(sm, q, k, v, dout, lse, dcol, off, entries, part_dq, sink_off, dk, dv, batch, n_q, n_kv, pos0,
+                       h_q, h_kv, nblk, topk, sl2, scale, item);
+    __syncthreads();                                   // the next list reuses the LDS
+  }
+}
+
+__global__ void bwd_counter_reset(int* counter) { *counter = 0; }
+
 // dq[t, h] = scale * (sum over the live slots of the row's partials): the
 // partials hold sum dS k unscaled, so the scale costs one multiply per
 // element here instead of one per partial element.  Every slot is loaded from
@@ -409,11 +441,14 @@ hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, const uint16_t* k, con
   }
   hipError_t e = launch_csr(d, blk, ws, stream, true);    // sums run in list order
   if (e != hipSuccess) return e;
+  int* counter = reinterpret_cast<int*>(base + L.counter);
+  hipLaunchKernelGGL(bwd_counter_reset, dim3(1), dim3(1), 0, stream, counter);
   {
     LaunchTimer timer("sparse_bwd_kv", stream);
-    hipLaunchKernelGGL((sparse_bwd_kv<D, LOG2G>), dim3((unsigned)L.lists), dim3(kBwdThreads), 0, stream, q, k, v,
-                       dout, lse, dcol, off, entries, part_dq, L.entries_max * G * D, dk, dv, d.batch, d.n_q, d.n_kv,
-                       d.pos0, d.h_q, d.h_kv, d.nblk(), d.topk, scale * kLog2e, scale);
+    hipLaunchKernelGGL((sparse_bwd_kv<D, LOG2G>), dim3((unsigned)std::min<int64_t>(device_cu_count(), L.lists)),
+                       dim3(kBwdThreads), 0, stream, q, k, v, dout, lse, dcol, off, entries, part_dq,
+                       L.entries_max * G * D, dk, dv, d.batch, d.n_q, d.n_kv, d.pos0, d.h_q, d.h_kv, d.nblk(), d.topk,
+                       scale * kLog2e, scale, counter, (int)L.lists);
   }
   if (nrows > 0) {
     LaunchTimer timer("sum_dq_partials", stream);

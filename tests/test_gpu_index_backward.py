@@ -68,6 +68,12 @@ CASES = {
     "g8_chunk": (31, Shape(1, 700, 6000, 5300, 64, 8, 128, 128, topk=16), 1 / math.sqrt(128)),
     # one live slot per row (the sequence inside one block): every gradient is zero
     "single_partial_block": (27, Shape(1, 50, 50, 0, 8, 2, 128, 128, topk=16), 0.1),
+    # k = 16 >= the 16 blocks: every row keeps all its causal blocks, so block
+    # 0's lists (all 8 groups) hold 2,048 x 8 entries = 512 column groups of 32,
+    # block j's (16 - j) / 16 of that.  The kernel cuts a block of n >= 256
+    # groups into min(8, n / 128) pieces, so blocks here run as 4, 3, 2 and 1
+    # pieces and dk_idx goes through the in-order combine of the partials.
+    "g8_all_blocks_split": (43, Shape(1, 2048, 2048, 0, 8, 8, 128, 128, topk=16), 0.1),
 }
 
 

@@ -74,6 +74,10 @@ CASES = {
     # groups into min(8, n / 128) pieces, so blocks here run as 4, 3, 2 and 1
     # pieces and dk_idx goes through the in-order combine of the partials.
     "g8_all_blocks_split": (43, Shape(1, 2048, 2048, 0, 8, 8, 128, 128, topk=16), 0.1),
+    # the same with two sequences (work items interleave the sequences' blocks)
+    # and with d_idx = 64
+    "g8_all_blocks_split_batch2": (44, Shape(2, 2048, 2048, 0, 8, 8, 128, 128, topk=16), 0.1),
+    "g8_all_blocks_split_d64": (45, Shape(1, 2048, 2048, 0, 8, 8, 64, 64, topk=16), 0.1),
 }
 
 

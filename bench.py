@@ -17,6 +17,9 @@ index scoring + block max-pool (msa_index_scores), exponential-free top-k
   * the top-k kernel against torch.topk on the same candidates, and the top-k
     alone on 1,048,576 full rows of 1,023 candidates against torch.topk and
     torch.sort on the same rows,
+  * the index branch with the top-k fused into the scorer (no pooled scores in
+    memory) on the prefill inputs, its time and workspace beside the unfused
+    stages,
   * the other configurations: 32K prefill and the 8,192-query prefill chunk at
     1M (each with the dense comparison), decode of 64 sequences at 256K,
   * `cpu_baseline`: the fp64 oracle timed on a bounded sample of the workload,
@@ -56,6 +59,8 @@ def parse():
                     help="skip the whole 1M-token chunked prefill leg")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-topk-compare", action="store_true")
+    ap.add_argument("--no-fused-topk", action="store_true",
+                    help="skip the fused index top-k (msa_index_topk_fused) on the prefill workload")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other configurations' legs (32K prefill, the 1M prefill chunk, 256K x 64 decode)")
     ap.add_argument("--no-topk-full", action="store_true",
@@ -589,6 +594,28 @@ def main():
                                            "block); torch.topk reads whole rows, msa only the candidates; the "
                                            "equal-work comparison is the topk_full_rows leg"}
         log(f"top-k: msa {ms_topk:.3f} ms vs torch.topk {ms_torch:.3f} ms")
+
+    if not args.no_fused_topk and s.block == 128 and s.topk <= 16 and s.n_q * s.h_kv > 16:
+        # The index branch with the top-k fused into the scorer, on the same
+        # inputs: its time and workspace beside the two unfused stages above
+        # (msa_index_scores + msa_block_topk, with their pooled scores).
+        fblk = torch.empty_like(blk)
+        fws = M.alloc_workspace(M.MSA_OP_INDEX_TOPK_FUSED, s)
+        ms_f, _, kf = time_calls(torch, [lambda: M.msa_index_topk_fused(s, inp["q_idx"], inp["k_idx"], fblk, fws)],
+                                 3, 1, M)
+        same = bool(torch.equal(fblk, blk))
+        ktiled = kf.get("index_topk_tiled", (1, float("nan")))
+        result["index_topk_fused"] = {
+            "ms": ms_f, "unfused_ms": ms_idx + ms_topk,
+            "kernels": {name: {"launches": n, "avg_ms": tot / n} for name, (n, tot) in kf.items()},
+            "scorer_mfma_frac": f_idx / (ktiled[1] / ktiled[0] * 1e-3) / PEAK_BF16_FLOPS,
+            "workspace_bytes": int(fws.numel()),
+            "unfused_workspace_bytes": int(M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, s)),
+            "same_selection_as_unfused": same}
+        log(f"fused index top-k {ms_f:.3f} ms (unfused {ms_idx + ms_topk:.3f} ms), workspace "
+            f"{fws.numel() / 2**20:.0f} MiB against {result['index_topk_fused']['unfused_workspace_bytes'] / 2**20:.0f}"
+            f" MiB, same selection: {same}")
+        del fblk, fws
 
     if not args.no_target and s.block == 128:
         # Index-branch training target (forward only): msa_sparse_prefill plus

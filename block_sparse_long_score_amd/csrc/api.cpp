@@ -128,6 +128,7 @@ unsigned op_needs(msa_op op) {
     case MSA_OP_SPARSE_PREFILL: return kNeedD | kCsr;
     case MSA_OP_SPARSE_DECODE: return kNeedD | kDecode;
     case MSA_OP_DENSE_GQA: return kNeedD;
+    case MSA_OP_INDEX_TOPK_FUSED: return kNeedDIdx | kOnly128;
   }
   return 0u;
 }
@@ -152,7 +153,7 @@ size_t chunked_ws_bytes(const Dims& d, int chunk, size_t* prefill_off) {
 extern "C" {
 
 size_t msa_workspace_size(msa_op op, const msa_dims* dims) {
-  if (op < MSA_OP_INDEX_TOPK || op > MSA_OP_BLOCK_TOPK) return 0;
+  if (op < MSA_OP_INDEX_TOPK || op > MSA_OP_INDEX_TOPK_FUSED) return 0;
   if (check_dims(dims, op_needs(op)) != MSA_OK) return 0;
   const Dims d = to_dims(*dims);
   switch (op) {
@@ -161,6 +162,7 @@ size_t msa_workspace_size(msa_op op, const msa_dims* dims) {
     case MSA_OP_SPARSE_PREFILL: return prefill_ws_bytes(d);
     case MSA_OP_SPARSE_DECODE: return decode_ws_bytes(d);
     case MSA_OP_DENSE_GQA: return d.n_q == 1 ? msa::dense_decode_ws_layout(index128(d)).total : 0;
+    case MSA_OP_INDEX_TOPK_FUSED: return msa::index_topk_fused_applies(d) ? msa::index_topk_fused_ws_bytes(d) : 0;
   }
   return 0;
 }
@@ -204,6 +206,21 @@ msa_status msa_index_topk_noalloc(const msa_dims* dims, const uint16_t* q_idx, c
   void* ws = nullptr;
   if (msa::scratch_for_current_device(&ws) != hipSuccess) return MSA_ERR_HIP;
   return hip_status(run_index_topk(d, q_idx, k_idx, blk_idx, ws, static_cast<hipStream_t>(stream)));
+}
+
+msa_status msa_index_topk_fused(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
+                                int32_t* blk_idx, void* workspace, size_t workspace_bytes, msa_stream stream) {
+  msa_status st = check_dims(dims, op_needs(MSA_OP_INDEX_TOPK_FUSED));
+  if (st != MSA_OK) return st;
+  if (empty(*dims)) return MSA_OK;
+  const Dims d = to_dims(*dims);
+  if (!msa::index_topk_fused_applies(d)) return MSA_ERR_UNSUPPORTED;
+  if (!q_idx || !k_idx || !blk_idx) return MSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(k_idx) || misaligned(blk_idx)) return MSA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < msa::index_topk_fused_ws_bytes(d)) return MSA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_index_topk_fused(d, q_idx, k_idx, blk_idx, workspace,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 msa_status msa_index_scores(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,

@@ -24,6 +24,7 @@
 
 #include "launch.h"
 #include "msa_device.h"
+#include "msa_select.h"
 
 namespace msa {
 namespace {
@@ -252,6 +253,275 @@ __global__ __launch_bounds__(kTiledWaves * 64) void index_scores_tiled(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Index scores, block max-pool and top-k fused (k <= 16), for prefill-shaped
+// calls: the pooled scores never leave the chip.  A workgroup keeps, in LDS,
+// every one of its 1,024 rows' best k-1 blocks seen so far (score and block)
+// and, per lane, the row's current worst kept score; as the key blocks stream
+// by in increasing order, a block whose pooled score beats a row's worst kept
+// score (strictly, so that among equal scores the earlier, lower block stays)
+// replaces that worst entry.  When a workgroup has swept its share of a row
+// tile's blocks it writes each row's survivors, in block order, to the
+// workspace (survivor lists [batch][row][piece][16]: 15 entries, then the
+// count); topk_merge_pieces then selects each row's k-1 best among the
+// survivors of the (at most kFusedPiecesMax) workgroups that swept its tile,
+// adds the local block and writes the row ascending (yhxrc.cn article,
+// "第一步：索引分支"; lumi-systems summary: exponential-free top-k).
+constexpr int kFusedKk = 15;                             // k - 1 <= 15
+constexpr int kFusedPiecesMax = 16;
+constexpr int kFusedSlots = 256;                         // workgroup slots the piece count is chosen for
+constexpr int kCandStride = 16;                          // survivors + count per (row, piece)
+
+template <int DI>
+struct IndexTopkSmem {
+  static constexpr int S = DI + 8;
+  uint16_t k[2][kBlock * S];                             // double-buffered key block
+  float cs[kTiledRows * kFusedKk];                       // kept scores, [row][entry]
+  uint16_t cj[kTiledRows * kFusedKk];                    // their blocks
+};
+
+// Piece k of a row tile's pair swept (and wrote survivor lists for) the tile
+// when its range of the pair's block iterations meets the tile's blocks: the
+// long tile's [0, na), then the short tile's [na, na + nb).  With more pieces
+// than iterations some ranges are empty.
+struct TilePieces {
+  int total, na;
+  bool long_tile;
+  __device__ __forceinline__ bool covers(int k, int pieces) const {
+    const int lo = total * k / pieces, hi = total * (k + 1) / pieces;
+    return lo < hi && (long_tile ? lo < na : hi > na);
+  }
+};
+__device__ __forceinline__ TilePieces tile_pieces(int tile, int tiles, int64_t nrows, int h_kv, int pos0) {
+  const int p = tile < tiles - 1 - tile ? tile : tiles - 1 - tile;
+  const int ta = tiles - 1 - p, tb = p;
+  const int na = tile_blocks(ta, nrows, h_kv, pos0);
+  const int nb = ta != tb ? tile_blocks(tb, nrows, h_kv, pos0) : 0;
+  return TilePieces{na + nb, na, tile == ta};
+}
+
+// One segment: row tile `tile` of sequence b against key blocks [jb, je),
+// scored as in tiled_segment, each block's pooled score offered to the row's
+// kept list instead of being stored.
+template <int DI>
+__device__ __forceinline__ void tiled_segment_topk(IndexTopkSmem<DI>& sm, const uint16_t* __restrict__ q_idx,
+                                                   const uint16_t* __restrict__ k_idx, float* __restrict__ cand_s,
+                                                   int* __restrict__ cand_j, int b, int tile, int jb, int je,
+                                                   int n_kv, int pos0, int h_kv, int64_t nrows, int pieces,
+                                                   int piece, int kk) {
+  constexpr int KC = DI / 16;
+  constexpr int NT = kTiledWaves * 64;
+  using Smem = IndexTopkSmem<DI>;
+  const int64_t r0 = (int64_t)tile * kTiledRows;
+  const int64_t r_end = min(r0 + (int64_t)kTiledRows, nrows);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int64_t rw0 = r0 + (int64_t)wave * kTiledColsPerWave;
+  const bool wave_live = rw0 < r_end;
+  const int tw0 = wave_live ? (int)(rw0 / h_kv) : 0;
+  const int tw1 = wave_live ? (int)((min(rw0 + kTiledColsPerWave, r_end) - 1) / h_kv) : 0;
+  const int jw_max = (pos0 + tw1) / kBlock;
+  const int jw_mask = (pos0 + tw0 + 1) / kBlock;
+
+  u32x4 qb[4][KC];
+  int plim[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int64_t r = rw0 + ct * 32 + r32;
+    const bool valid = wave_live && r < r_end;
+    plim[ct] = valid ? pos0 + (int)(r / h_kv) : -1;
+    const uint16_t* qr = q_idx + ((int64_t)b * nrows + r) * DI;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      qb[ct][kc] = valid ? ld16(qr + kc * 16 + half * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  // This lane keeps the lists of rows ct = 2 half and 2 half + 1 of its column
+  // r32: per row the kept count and the entry of the worst kept score (packed
+  // count | entry << 8) and that score.  A row's candidates are its blocks
+  // j < jl = plim / 128 (none for a row past the tile, plim = -1).
+  int meta[2] = {0, 0};
+  float worst[2] = {-INFINITY, -INFINITY};
+  auto row_jl = [&](int u) {
+    const int pl = half ? plim[2 + u] : plim[u];
+    return pl >= 0 ? pl / kBlock : -1;
+  };
+  const int lrow0 = wave * kTiledColsPerWave + r32;      // + ct * 32: this lane's rows in the workgroup
+
+  constexpr int CHUNKS = kBlock * DI / 8;
+  constexpr int ITEMS = CHUNKS / NT;
+  static_assert(CHUNKS % NT == 0, "tile staging must divide evenly");
+  constexpr int KSTEP = NT / (DI / 8);
+  const uint16_t* kseq = k_idx + (int64_t)b * n_kv * DI;
+  const int skey0 = tid / (DI / 8);
+  const int goff0 = skey0 * DI + (tid % (DI / 8)) * 8;
+  const int loff0 = skey0 * Smem::S + (tid % (DI / 8)) * 8;
+  u32x4 pre[ITEMS];
+  auto fetch = [&](int j) {
+    const uint16_t* kb = kseq + (int64_t)j * kBlock * DI + goff0;
+    const int lim = n_kv - j * kBlock - skey0;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+      pre[i] = (i * KSTEP < lim) ? ld16(kb + i * KSTEP * DI) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto stash = [&](uint16_t* t) {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) st16(t + loff0 + i * KSTEP * Smem::S, pre[i]);
+  };
+
+  fetch(jb);
+  stash(sm.k[0]);
+  __syncthreads();
+
+  for (int j = jb; j < je; ++j) {
+    const int cur = (j - jb) & 1;
+    if (j + 1 < je) fetch(j + 1);
+    if (wave_live && j <= jw_max) {
+      float rm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (j >= jw_mask)
+        score_block<DI, true>(sm.k[cur], qb, j * kBlock, plim, rm);
+      else
+        score_block<DI, false>(sm.k[cur], qb, j * kBlock, plim, rm);
+      float m4[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) m4[ct] = vmax(rm[ct], shfl_xor_f(rm[ct], 32)) + 0.0f;   // + 0: -0 -> +0
+      const float mrow[2] = {half ? m4[2] : m4[0], half ? m4[3] : m4[1]};   // the two rows this lane keeps
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int cnt = meta[u] & 0xff;
+        const bool take = j < row_jl(u) && (cnt < kk || mrow[u] > worst[u]);
+        if (take) {                                      // rare once a row has k-1 entries
+          float* rs = sm.cs + (lrow0 + (2 * half + u) * 32) * kFusedKk;
+          uint16_t* rj = sm.cj + (lrow0 + (2 * half + u) * 32) * kFusedKk;
+          const int at = cnt < kk ? cnt : meta[u] >> 8;
+          rs[at] = mrow[u];
+          rj[at] = (uint16_t)j;
+          const int nc = min(cnt + 1, kk);
+          meta[u] = nc;
+          if (nc == kk) {                                // the worst kept entry: lowest score, then highest block
+            float ws = INFINITY;
+            int wj = -1, wp = 0;
+            for (int e = 0; e < kk; ++e) {
+              const float sc = rs[e];
+              const int bj = rj[e];
+              if (sc < ws || (sc == ws && bj > wj)) {
+                ws = sc;
+                wj = bj;
+                wp = e;
+              }
+            }
+            worst[u] = ws;
+            meta[u] = nc | (wp << 8);
+          }
+        }
+      }
+    }
+    if (j + 1 < je) stash(sm.k[cur ^ 1]);
+    __syncthreads();
+  }
+  // Each kept list goes out in block order: entry e's place is the number of
+  // kept blocks below its own (blocks are distinct).
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (row_jl(u) < 0) continue;
+    const int cnt = meta[u] & 0xff;
+    const int64_t r = rw0 + (2 * half + u) * 32 + r32;
+    const int64_t at = (((int64_t)b * nrows + r) * pieces + piece) * kCandStride;
+    const float* rs = sm.cs + (lrow0 + (2 * half + u) * 32) * kFusedKk;
+    const uint16_t* rj = sm.cj + (lrow0 + (2 * half + u) * 32) * kFusedKk;
+    for (int e = 0; e < cnt; ++e) {
+      const int bj = rj[e];
+      int rank = 0;
+      for (int f = 0; f < cnt; ++f) rank += rj[f] < bj ? 1 : 0;
+      cand_s[at + rank] = rs[e];
+      cand_j[at + rank] = bj;
+    }
+    cand_j[at + kCandStride - 1] = cnt;
+  }
+  __syncthreads();                                       // the lists are reused by the next segment
+}
+
+// The same decomposition as index_scores_tiled (tile pairs cut into equal
+// pieces), with the piece count chosen for kFusedSlots slots and capped at
+// kFusedPiecesMax so that the survivor workspace follows from the sizes alone.
+template <int DI>
+__global__ __launch_bounds__(kTiledWaves * 64) void index_topk_tiled(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, float* __restrict__ cand_s,
+    int* __restrict__ cand_j, int n_q, int n_kv, int pos0, int h_kv, int tiles, int pairs, int pieces, int kk) {
+  __shared__ IndexTopkSmem<DI> sm;
+  const int64_t nrows = (int64_t)n_q * h_kv;
+  const int w = blockIdx.x;
+  const int k = w % pieces;
+  const int p = (w / pieces) % pairs;
+  const int b = w / (pieces * pairs);
+  const int ta = tiles - 1 - p, tb = p;
+  const int na = tile_blocks(ta, nrows, h_kv, pos0);
+  const int nb = ta != tb ? tile_blocks(tb, nrows, h_kv, pos0) : 0;
+  const int total = na + nb;
+  const int lo = total * k / pieces, hi = total * (k + 1) / pieces;
+#pragma nounroll
+  for (int seg = 0; seg < 2; ++seg) {
+    const int tile = __builtin_amdgcn_readfirstlane(seg == 0 ? ta : tb);
+    const int jb = __builtin_amdgcn_readfirstlane(seg == 0 ? lo : max(lo, na) - na);
+    const int je = __builtin_amdgcn_readfirstlane(seg == 0 ? min(hi, na) : hi - na);
+    if (jb < je)
+      tiled_segment_topk<DI>(sm, q_idx, k_idx, cand_s, cand_j, b, tile, jb, je, n_kv, pos0, h_kv, nrows, pieces, k,
+                             kk);
+  }
+}
+
+// Each row's k-1 best among the survivor lists of the pieces that swept its
+// tile (in piece order, each list in block order: position order is block
+// order, so ties still go to the lower block), then the local block; one wave
+// per row, rows ascending.
+constexpr int kMergeRowsPerWg = 4;
+__global__ __launch_bounds__(kMergeRowsPerWg * 64) void topk_merge_pieces(
+    const float* __restrict__ cand_s, const int* __restrict__ cand_j, int32_t* __restrict__ blk, int64_t nrows_all,
+    int n_q, int pos0, int h_kv, int topk, int tiles, int pieces) {
+  constexpr int V = kFusedPiecesMax * kFusedKk / 64 + 1;   // 240 survivors at most
+  __shared__ uint32_t ck[kMergeRowsPerWg][64];
+  __shared__ int32_t ci[kMergeRowsPerWg][64];
+  __shared__ uint32_t gk[kMergeRowsPerWg][V * 64];
+  __shared__ int32_t gj[kMergeRowsPerWg][V * 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerWg + wave;   // (b * n_q + t) * h_kv + g
+  if (row >= nrows_all) return;
+  const int64_t nrows = (int64_t)n_q * h_kv;
+  const int64_t r = row % nrows;                        // row within its sequence
+  const int t = (int)(r / h_kv);
+  const int jl = (pos0 + t) / kBlock;
+  int32_t* out = blk + row * topk;
+  if (jl + 1 <= topk) {
+    for (int i = lane; i < topk; i += 64) out[i] = (i <= jl) ? i : -1;
+    return;
+  }
+  const int kk = topk - 1;
+  if (lane == 0) out[kk] = jl;
+  if (kk == 0) return;
+  const TilePieces tp = tile_pieces((int)(r / kTiledRows), tiles, nrows, h_kv, pos0);
+  int total = 0;
+  for (int k = 0; k < pieces; ++k) {
+    if (!tp.covers(k, pieces)) continue;
+    const int64_t at = (row * pieces + k) * kCandStride;
+    const int n = cand_j[at + kCandStride - 1];
+    if (lane < n) {
+      gk[wave][total + lane] = order_key(cand_s[at + lane]);
+      gj[wave][total + lane] = cand_j[at + lane];
+    }
+    total += n;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint32_t key[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = i * 64 + lane;
+    key[i] = e < total ? gk[wave][e] : 0u;
+  }
+  wave_select<V>(key, kk, ck[wave], ci[wave], [&](int pos, uint32_t, int e) { out[pos] = gj[wave][e]; });
+}
+
 // Decode-shaped calls: at most 16 (token, group) rows per sequence.  One key
 // block per wave: the scan is a pure HBM stream, and many short-lived waves
 // keep more of it in flight than fewer waves walking several blocks each
@@ -315,10 +585,10 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void index_scores_skinny(
 // Pieces per tile pair.  Workgroups carry equal work, so the launch runs in
 // ceil(W / slots) rounds of whole workgroups; the choice trades the idle part
 // of the last round against the fixed cost of each piece (query operand load
-// and pipeline fill, about kPieceCost block iterations).
-int choose_pieces(int64_t units, double pair_iters, int64_t slots) {
+// and pipeline fill, about kPieceCost block iterations).  At most kcap pieces.
+int choose_pieces(int64_t units, double pair_iters, int64_t slots, int kcap = 1024) {
   constexpr double kPieceCost = 4.0;
-  const int kmax = (int)std::max<double>(1.0, std::min<double>(1024.0, pair_iters));
+  const int kmax = (int)std::max<double>(1.0, std::min<double>((double)kcap, pair_iters));
   int best = 1;
   double best_score = -1.0;
   for (int k = 1; k <= kmax; ++k) {
@@ -366,7 +636,62 @@ hipError_t launch_index_scores_t(const Dims& d, const uint16_t* q_idx, const uin
   return hipGetLastError();
 }
 
+// Pieces per tile pair on the fused path: chosen for kFusedSlots workgroup
+// slots (not the device's count) and at most kFusedPiecesMax, so that the
+// survivor workspace follows from the sizes alone.
+int fused_pieces(const Dims& d) {
+  const int64_t nrows = (int64_t)d.n_q * d.h_kv;
+  const int64_t tiles = (nrows + kTiledRows - 1) / kTiledRows;
+  const int64_t pairs = (tiles + 1) / 2;
+  int64_t iters = 0;
+  for (int64_t t = 0; t < tiles; ++t) iters += tile_blocks((int)t, nrows, d.h_kv, d.pos0);
+  return choose_pieces(pairs * d.batch, (double)iters / pairs, kFusedSlots, kFusedPiecesMax);
+}
+
+template <int DI>
+hipError_t launch_index_topk_fused_t(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, int32_t* blk,
+                                     void* ws, hipStream_t stream) {
+  const int64_t nrows = (int64_t)d.n_q * d.h_kv;
+  const int64_t tiles = (nrows + kTiledRows - 1) / kTiledRows;
+  const int64_t pairs = (tiles + 1) / 2;
+  const int pieces = fused_pieces(d);
+  const size_t n = (size_t)d.batch * nrows * pieces * kCandStride;
+  float* cand_s = static_cast<float*>(ws);
+  int* cand_j = reinterpret_cast<int*>(static_cast<char*>(ws) + align_up(n * sizeof(float), 256));
+  {
+    LaunchTimer timer("index_topk_tiled", stream);
+    hipLaunchKernelGGL(index_topk_tiled<DI>, dim3((unsigned)(d.batch * pairs * pieces)), dim3(kTiledWaves * 64), 0,
+                       stream, q_idx, k_idx, cand_s, cand_j, d.n_q, d.n_kv, d.pos0, d.h_kv, (int)tiles, (int)pairs,
+                       pieces, d.topk - 1);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows_all = (int64_t)d.batch * nrows;
+  {
+    LaunchTimer timer("topk_merge_pieces", stream);
+    hipLaunchKernelGGL(topk_merge_pieces, dim3((unsigned)((rows_all + kMergeRowsPerWg - 1) / kMergeRowsPerWg)),
+                       dim3(kMergeRowsPerWg * 64), 0, stream, cand_s, cand_j, blk, rows_all, d.n_q, d.pos0, d.h_kv,
+                       d.topk, (int)tiles, pieces);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool index_topk_fused_applies(const Dims& d) {
+  return d.block == 128 && !d.seq_len && d.topk - 1 <= kFusedKk && (int64_t)d.n_q * d.h_kv > 16;
+}
+
+size_t index_topk_fused_ws_bytes(const Dims& d) {
+  const size_t n = (size_t)d.batch * d.n_q * d.h_kv * fused_pieces(d) * kCandStride;
+  return align_up(n * sizeof(float), 256) + align_up(n * sizeof(int), 256);
+}
+
+hipError_t launch_index_topk_fused(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, int32_t* blk,
+                                   void* ws, hipStream_t stream) {
+  if (d.d_idx == 128) return launch_index_topk_fused_t<128>(d, q_idx, k_idx, blk, ws, stream);
+  return launch_index_topk_fused_t<64>(d, q_idx, k_idx, blk, ws, stream);
+}
 
 hipError_t launch_index_scores(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,
                                hipStream_t stream) {

@@ -60,6 +60,14 @@ DecodeWs dense_decode_ws_layout(const Dims& d);
 hipError_t launch_index_scores(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,
                                hipStream_t stream);
 hipError_t launch_block_topk(const Dims& d, const float* bscore, int32_t* blk_idx, hipStream_t stream);
+// Index branch with the top-k fused into the tiled scorer (128-token blocks,
+// k <= 16, more than 16 (token, group) rows per sequence): no pooled scores in
+// memory; `ws` holds index_topk_fused_ws_bytes(d) bytes of per-row survivor
+// lists.
+bool index_topk_fused_applies(const Dims& d);
+size_t index_topk_fused_ws_bytes(const Dims& d);
+hipError_t launch_index_topk_fused(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, int32_t* blk_idx,
+                                   void* ws, hipStream_t stream);
 // log2 of the selection block size (128 or 256).
 inline int block_shift(const Dims& d) { return d.block == 256 ? 8 : 7; }
 // 256-token blocks from 128-token ones: pooled scores of pairs (rows of the

@@ -23,6 +23,7 @@ MSA_OP_SPARSE_PREFILL = 1
 MSA_OP_SPARSE_DECODE = 2
 MSA_OP_DENSE_GQA = 3
 MSA_OP_BLOCK_TOPK = 4
+MSA_OP_INDEX_TOPK_FUSED = 5
 
 STATUS = {
     0: "MSA_OK",
@@ -54,6 +55,7 @@ EXPORTED = (
     "msa_sparse_prefill_backward",
     "msa_index_backward",
     "msa_index_topk_noalloc",
+    "msa_index_topk_fused",
 )
 
 
@@ -96,6 +98,7 @@ def lib() -> ctypes.CDLL:
     L.msa_status_str.restype = ctypes.c_char_p
     L.msa_index_topk.argtypes = [D, P, P, P, P, S, VP]
     L.msa_index_topk_noalloc.argtypes = [D, P, P, P, VP]
+    L.msa_index_topk_fused.argtypes = [D, P, P, P, P, S, VP]
     L.msa_index_scores.argtypes = [D, P, P, P, VP]
     L.msa_block_topk.argtypes = [D, P, P, VP]
     L.msa_sparse_prefill.argtypes = [D, P, P, P, P, F, P, P, P, S, VP]
@@ -173,6 +176,18 @@ def msa_index_topk(s: Shape, q_idx, k_idx, blk_idx, workspace, stream=None) -> N
     wp, wb = _ws(workspace)
     st = lib().msa_index_topk(ctypes.byref(d), _ptr(q_idx), _ptr(k_idx), _ptr(blk_idx), wp, wb, _stream(stream))
     _raise(st, "msa_index_topk")
+
+
+def msa_index_topk_fused(s: Shape, q_idx, k_idx, blk_idx, workspace, stream=None) -> None:
+    """msa_index_topk with the top-k fused into the scorer (workspace: MSA_OP_INDEX_TOPK_FUSED)."""
+    _check(q_idx, "q_idx", torch.bfloat16, (s.batch, s.n_q, s.h_kv, s.d_idx))
+    _check(k_idx, "k_idx", torch.bfloat16, (s.batch, s.n_kv, s.d_idx))
+    _check(blk_idx, "blk_idx", torch.int32, (s.batch, s.n_q, s.h_kv, s.topk))
+    d = dims_of(s)
+    wp, wb = _ws(workspace)
+    st = lib().msa_index_topk_fused(ctypes.byref(d), _ptr(q_idx), _ptr(k_idx), _ptr(blk_idx), wp, wb,
+                                    _stream(stream))
+    _raise(st, "msa_index_topk_fused")
 
 
 def msa_index_topk_noalloc(s: Shape, q_idx, k_idx, blk_idx, stream=None) -> None:

@@ -96,7 +96,8 @@ typedef enum msa_op {
   MSA_OP_SPARSE_PREFILL = 1,
   MSA_OP_SPARSE_DECODE = 2,
   MSA_OP_DENSE_GQA = 3,
-  MSA_OP_BLOCK_TOPK = 4
+  MSA_OP_BLOCK_TOPK = 4,
+  MSA_OP_INDEX_TOPK_FUSED = 5
 } msa_op;
 
 typedef void* msa_stream; /* hipStream_t */
@@ -124,6 +125,29 @@ const char* msa_status_str(msa_status status);
  * <= 3 and d_idx <= 128 they are exact. */
 msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
                           int32_t* blk_idx, void* workspace, size_t workspace_bytes, msa_stream stream);
+
+/* The index branch with the top-k fused into the scoring kernel, so that the
+ * pooled block scores never reach memory (yhxrc.cn article, "第一步：索引分支":
+ * scores, block max-pool and top-k as one step; lumi-systems summary: the
+ * selection uses no exponential).  Same arguments and the same blk_idx as
+ * msa_index_topk, bit for bit; only the workspace differs:
+ *   workspace >= msa_workspace_size(MSA_OP_INDEX_TOPK_FUSED): per (token,
+ *           group) row P lists of up to 15 surviving blocks (P = 1..16
+ *           workgroups sweep each 1,024-row tile, chosen from the sizes
+ *           alone), batch * n_q * h_kv * P * 128 bytes; its contents on return
+ *           are unspecified.  At 131,072 tokens x 8 groups that is 128 MiB,
+ *           against 4 GiB of pooled scores for msa_index_topk.
+ * Each sweeping workgroup keeps every row's best k - 1 blocks so far in LDS as
+ * the key blocks stream by (a later block replaces the worst kept one only
+ * with a strictly larger score, so ties keep the lower block); a second kernel
+ * selects each row's k - 1 best among its lists and adds the local block.
+ * It trades time for memory: on MI355X it takes about 1.45x the time of
+ * msa_index_topk at 128K tokens.
+ *   - MSA_ERR_UNSUPPORTED for block 256, topk > 16, or n_q * h_kv <= 16 (a
+ *     decode-shaped call, whose pooled scores are small: use
+ *     msa_index_topk); msa_workspace_size then returns 0. */
+msa_status msa_index_topk_fused(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
+                                int32_t* blk_idx, void* workspace, size_t workspace_bytes, msa_stream stream);
 
 /* msa_index_topk without a workspace argument, for callers that cannot
  * allocate device memory: code being captured into a HIP graph, tight serving

@@ -318,3 +318,34 @@ def test_noalloc_index_topk_host_checks():
     # 2 * 2048 * 8 * 1024 fp32 pooled scores = 128 MiB
     assert call(dims(batch=2, n_q=2048, n_kv=131072, pos0=129024, h_q=64, h_kv=8)) == 7
     assert M.STATUS[7] == "MSA_ERR_TOO_LARGE"
+
+
+def test_fused_index_topk_host_checks():
+    """The fused index top-k validates like msa_index_topk, serves only
+    prefill-shaped calls with 128-token blocks and k <= 16, and sizes its
+    survivor lists at 1 to 16 lists of 128 bytes per (token, group) row."""
+    lib = M.lib()
+    call = lambda d, q=FAKE, k=FAKE, blk=FAKE, ws=FAKE, wsb=1 << 40: lib.msa_index_topk_fused(
+        ctypes.byref(d) if d is not None else None, q, k, blk, ws, wsb, None)
+    size = lambda d: lib.msa_workspace_size(M.MSA_OP_INDEX_TOPK_FUSED, ctypes.byref(d))
+    assert call(None) == NULL
+    assert call(dims(), k=None) == NULL
+    assert call(dims(), blk=ODD) == ALIGN
+    assert call(dims(), ws=ODD) == ALIGN
+    assert call(dims(), ws=None) == WS
+    assert call(dims(), wsb=size(dims()) - 1) == WS
+    assert call(dims(pos0=4000)) == SHAPE
+    assert call(dims(d_idx=96)) == UNSUP
+    for kw in (dict(topk=17), dict(block=256, topk=8), dict(n_q=2, pos0=4094, h_q=8, h_kv=8),
+               dict(n_q=1, pos0=4095)):
+        assert call(dims(**kw)) == UNSUP, kw
+        assert size(dims(**kw)) == 0, kw
+    assert call(dims(n_q=0), q=None, k=None, blk=None, ws=None) == OK
+    assert size(dims(n_q=3, pos0=4093, h_kv=8, h_q=8)) > 0                  # 24 rows: prefill-shaped
+    for name in ("prefill_32k", "prefill_128k", "prefill_chunk_1m", "tiny_prefill_4k"):
+        s = WORKLOADS[name][1]
+        rows = s.batch * s.n_q * s.h_kv
+        n = M.msa_workspace_size(M.MSA_OP_INDEX_TOPK_FUSED, s)
+        assert rows * 128 <= n <= 16 * rows * 128 + 512, (name, n)
+    s = WORKLOADS["prefill_128k"][1]
+    assert M.msa_workspace_size(M.MSA_OP_INDEX_TOPK_FUSED, s) * 32 == M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, s)

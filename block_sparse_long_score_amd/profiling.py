@@ -40,6 +40,8 @@ KERNEL_SOURCES = {
     "block_topk_rows": ["block_topk.hip", "msa_select.h", "msa_device.h"],
     "block_topk_wg": ["block_topk.hip", "msa_select.h", "msa_device.h"],
     "dense_prefill": ["dense_attn.hip", "msa_device.h"],
+    "index_topk_tiled": ["index_score.hip", "msa_select.h", "msa_device.h"],
+    "topk_merge_pieces": ["index_score.hip", "msa_select.h", "msa_device.h"],
 }
 
 

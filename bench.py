@@ -4,10 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 One step is one pass of the hot path over one batch of synthetic input:
-index scoring + block max-pool (msa_index_scores), exponential-free top-k
-(msa_block_topk) and block-sparse prefill attention (msa_sparse_prefill) on the
-131,072-token prefill workload (64 query heads on 8 K/V heads, d = d_idx = 128,
-128-token blocks, k = 16).  Inputs are resident in HBM before the timed region.
+index scoring, block max-pool and exponential-free top-k (msa_index_topk, which
+for this shape runs the top-k fused into the scoring kernel) and block-sparse
+prefill attention (msa_sparse_prefill) on the 131,072-token prefill workload
+(64 query heads on 8 K/V heads, d = d_idx = 128, 128-token blocks, k = 16).  Inputs are resident in HBM before the timed region.
 `value` is prefill tokens per second.  The same JSON line also carries:
   * per-stage times measured with HIP events on the stream the library runs on,
   * `roofline` for the dominant kernel (algorithmic flops or bytes per launch
@@ -17,9 +17,8 @@ index scoring + block max-pool (msa_index_scores), exponential-free top-k
   * the top-k kernel against torch.topk on the same candidates, and the top-k
     alone on 1,048,576 full rows of 1,023 candidates against torch.topk and
     torch.sort on the same rows,
-  * the index branch with the top-k fused into the scorer (no pooled scores in
-    memory) on the prefill inputs, its time and workspace beside the unfused
-    stages,
+  * the index branch as two separate calls on the prefill inputs (the scoring
+    kernel writes the pooled scores, msa_block_topk reads them), each timed,
   * the other configurations: 32K prefill and the 8,192-query prefill chunk at
     1M (each with the dense comparison), decode of 64 sequences at 256K,
   * `cpu_baseline`: the fp64 oracle timed on a bounded sample of the workload,
@@ -59,8 +58,6 @@ def parse():
                     help="skip the whole 1M-token chunked prefill leg")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-topk-compare", action="store_true")
-    ap.add_argument("--no-fused-topk", action="store_true",
-                    help="skip the fused index top-k (msa_index_topk_fused) on the prefill workload")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other configurations' legs (32K prefill, the 1M prefill chunk, 256K x 64 decode)")
     ap.add_argument("--no-topk-full", action="store_true",
@@ -299,24 +296,23 @@ def cpu_baseline(s, inp, seconds, seed=99):
 # ------------------------------------------------------ other configurations --
 
 def prefill_config_leg(torch, M, name, steps, warmup, dense_reps=2):
-    """One step of the prefill hot path (index scores, top-k, sparse prefill)
-    on another configuration's inputs, with the library's dense GQA on the
-    same inputs."""
+    """One step of the prefill hot path (msa_index_topk, then
+    msa_sparse_prefill) on another configuration's inputs, with the library's
+    dense GQA on the same inputs."""
     from block_sparse_long_score_amd.inputs import WORKLOADS, make_inputs
     cid, s = WORKLOADS[name]
     log(f"prefill leg {name}: {s}")
     inp = make_inputs(s, cid, device="cuda")
-    bscore = torch.empty((s.batch, s.n_q, s.h_kv, s.nblk), dtype=torch.float32, device="cuda")
     blk = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.int32, device="cuda")
     out = torch.empty((s.batch, s.n_q, s.h_q, s.d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((s.batch, s.n_q, s.h_q), dtype=torch.float32, device="cuda")
     ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
+    ws_i = M.alloc_workspace(M.MSA_OP_INDEX_TOPK, s)
     stages = [
-        lambda: M.msa_index_scores(s, inp["q_idx"], inp["k_idx"], bscore),
-        lambda: M.msa_block_topk(s, bscore, blk),
+        lambda: M.msa_index_topk(s, inp["q_idx"], inp["k_idx"], blk, ws_i),
         lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
     ]
-    ms, (mi, mt, msp) = time_calls(torch, stages, steps, warmup)
+    ms, (mi, msp) = time_calls(torch, stages, steps, warmup)
     st = step_stats()
     fi, fsp = index_flops(s), sparse_flops(s)
     tokens = s.batch * s.n_q
@@ -324,11 +320,10 @@ def prefill_config_leg(torch, M, name, steps, warmup, dense_reps=2):
            "ms_per_step": ms, "ms_per_step_median": st["median"], "ms_per_step_min": st["min"],
            "tok_s": tokens / (ms * 1e-3), "algorithmic_flops": fi + fsp,
            "end_to_end_mfma_frac": (fi + fsp) / (ms * 1e-3) / PEAK_BF16_FLOPS,
-           "stages_ms": {"index_scores": mi, "block_topk": mt, "sparse_prefill": msp},
-           "index_scores_mfma_frac": fi / (mi * 1e-3) / PEAK_BF16_FLOPS,
-           "block_topk_hbm_frac": topk_bytes(s) / (mt * 1e-3) / PEAK_HBM_BYTES,
+           "stages_ms": {"index_topk": mi, "sparse_prefill": msp},
+           "index_topk_mfma_frac": fi / (mi * 1e-3) / PEAK_BF16_FLOPS,
            "sparse_prefill_mfma_frac": fsp / (msp * 1e-3) / PEAK_BF16_FLOPS}
-    log(f"{name}: step {ms:.3f} ms (index {mi:.3f}, top-k {mt:.3f}, sparse {msp:.3f}) -> "
+    log(f"{name}: step {ms:.3f} ms (index top-k {mi:.3f}, sparse {msp:.3f}) -> "
         f"{leg['tok_s']:.4g} tok/s, {leg['end_to_end_mfma_frac']:.1%} of MFMA peak")
     if dense_reps:
         ms_d, _ = time_calls(torch, [lambda: M.msa_dense_gqa(s, inp["q"], inp["k"], inp["v"], out, lse)],
@@ -338,7 +333,7 @@ def prefill_config_leg(torch, M, name, steps, warmup, dense_reps=2):
                             "msa_speedup": ms_d / ms}
         log(f"{name}: dense GQA {ms_d:.2f} ms ({leg['dense_gqa']['mfma_frac']:.1%} of MFMA peak) -> "
             f"MSA {ms_d / ms:.2f}x faster")
-    del inp, bscore, blk, out, lse, ws
+    del inp, blk, out, lse, ws, ws_i
     torch.cuda.empty_cache()
     return leg
 
@@ -490,34 +485,26 @@ def main():
     ws = M.alloc_workspace(M.MSA_OP_SPARSE_PREFILL, s)
     torch.cuda.synchronize()
 
-    if s.block == 128:
-        stages = [
-            lambda: M.msa_index_scores(s, inp["q_idx"], inp["k_idx"], bscore),
-            lambda: M.msa_block_topk(s, bscore, blk),
-            lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
-        ]
-    else:
-        # 256-token blocks: msa_index_topk scores, pools in pairs and selects
-        # in one call (its time is reported under the index stage).
-        ws_idx = M.alloc_workspace(M.MSA_OP_INDEX_TOPK, s)
-        stages = [
-            lambda: M.msa_index_topk(s, inp["q_idx"], inp["k_idx"], blk, ws_idx),
-            lambda: None,
-            lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
-        ]
+    # The hot path as a caller runs it: msa_index_topk (for prefill-shaped calls
+    # with 128-token blocks and k <= 16 it runs the top-k fused into the
+    # scoring kernel, without pooled scores in memory; otherwise scores,
+    # pooling and top-k as separate kernels), then msa_sparse_prefill.
+    ws_idx = M.alloc_workspace(M.MSA_OP_INDEX_TOPK, s)
+    stages = [
+        lambda: M.msa_index_topk(s, inp["q_idx"], inp["k_idx"], blk, ws_idx),
+        lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out, lse, ws),
+    ]
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms_step, (ms_idx, ms_topk, ms_sparse), kern = time_calls(torch, stages, args.steps, args.warmup, M)
+    ms_step, (ms_it, ms_sparse), kern = time_calls(torch, stages, args.steps, args.warmup, M)
     prefill_steps = step_stats()
     tokens = s.batch * s.n_q
     value = tokens / (ms_step * 1e-3)
     f_idx, f_sp = index_flops(s), sparse_flops(s)
-    log(f"step {ms_step:.3f} ms: index {ms_idx:.3f}, top-k {ms_topk:.3f}, sparse {ms_sparse:.3f} -> {value:.4g} tok/s")
+    log(f"step {ms_step:.3f} ms: index top-k {ms_it:.3f}, sparse {ms_sparse:.3f} -> {value:.4g} tok/s")
 
     per_stage = {
-        "index_scores": {"ms": ms_idx, "bound": "mfma", "achieved": f_idx / (ms_idx * 1e-3) / 1e12,
-                         "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"},
-        "block_topk": {"ms": ms_topk, "bound": "hbm", "achieved": topk_bytes(s) / (ms_topk * 1e-3) / 1e9,
-                       "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s"},
+        "index_topk": {"ms": ms_it, "bound": "mfma", "achieved": f_idx / (ms_it * 1e-3) / 1e12,
+                       "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"},
         "sparse_prefill": {"ms": ms_sparse, "bound": "mfma", "achieved": f_sp / (ms_sparse * 1e-3) / 1e12,
                            "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s"},
     }
@@ -529,6 +516,7 @@ def main():
                for name, (n, tot) in kern.items()}
     algorithmic = {   # kernel -> (bound, algorithmic work of one launch, peak, unit scale, unit)
         "index_scores_tiled": ("mfma", f_idx, PEAK_BF16_FLOPS, 1e12, "TFLOP/s"),
+        "index_topk_tiled": ("mfma", f_idx, PEAK_BF16_FLOPS, 1e12, "TFLOP/s"),
         "sparse_kv_outer": ("mfma", f_sp, PEAK_BF16_FLOPS, 1e12, "TFLOP/s"),
         "block_topk_rows": ("hbm", topk_bytes(s), PEAK_HBM_BYTES, 1e9, "GB/s"),
         "block_topk_wg": ("hbm", topk_bytes(s), PEAK_HBM_BYTES, 1e9, "GB/s"),
@@ -576,6 +564,27 @@ def main():
         "ms_per_step_min": prefill_steps["min"],
     }
 
+    if s.block == 128:
+        # The index branch as two separate calls on the same inputs: the
+        # scoring kernel writes the pooled scores (the workspace msa_index_topk
+        # needs off the fused path), then the top-k reads them.
+        ublk = torch.empty_like(blk)
+        ms_u, (ms_idx, ms_topk), ku = time_calls(torch, [
+            lambda: M.msa_index_scores(s, inp["q_idx"], inp["k_idx"], bscore),
+            lambda: M.msa_block_topk(s, bscore, ublk)], 3, 1, M)
+        same = bool(torch.equal(ublk, blk))
+        result["index_unfused"] = {
+            "ms": ms_u, "index_scores_ms": ms_idx, "block_topk_ms": ms_topk,
+            "index_scores_mfma_frac": f_idx / (ms_idx * 1e-3) / PEAK_BF16_FLOPS,
+            "block_topk_hbm_frac": topk_bytes(s) / (ms_topk * 1e-3) / PEAK_HBM_BYTES,
+            "kernels": {name: {"launches": n, "avg_ms": tot / n} for name, (n, tot) in ku.items()},
+            "pooled_score_bytes": int(bscore.numel() * 4),
+            "index_topk_workspace_bytes": int(M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, s)),
+            "same_selection_as_index_topk": same}
+        log(f"index branch as separate calls: scores {ms_idx:.3f} ms + top-k {ms_topk:.3f} ms = {ms_u:.3f} ms "
+            f"(msa_index_topk {ms_it:.3f} ms), same selection: {same}")
+        del ublk
+
     if not args.no_topk_compare and s.block == 128:
         # torch.topk on the same candidates: entries at and past each row's
         # local block are set to -inf in a copy, so the library top-k makes
@@ -595,31 +604,10 @@ def main():
                                            "equal-work comparison is the topk_full_rows leg"}
         log(f"top-k: msa {ms_topk:.3f} ms vs torch.topk {ms_torch:.3f} ms")
 
-    if not args.no_fused_topk and s.block == 128 and s.topk <= 16 and s.n_q * s.h_kv > 16:
-        # The index branch with the top-k fused into the scorer, on the same
-        # inputs: its time and workspace beside the two unfused stages above
-        # (msa_index_scores + msa_block_topk, with their pooled scores).
-        fblk = torch.empty_like(blk)
-        fws = M.alloc_workspace(M.MSA_OP_INDEX_TOPK_FUSED, s)
-        ms_f, _, kf = time_calls(torch, [lambda: M.msa_index_topk_fused(s, inp["q_idx"], inp["k_idx"], fblk, fws)],
-                                 3, 1, M)
-        same = bool(torch.equal(fblk, blk))
-        ktiled = kf.get("index_topk_tiled", (1, float("nan")))
-        result["index_topk_fused"] = {
-            "ms": ms_f, "unfused_ms": ms_idx + ms_topk,
-            "kernels": {name: {"launches": n, "avg_ms": tot / n} for name, (n, tot) in kf.items()},
-            "scorer_mfma_frac": f_idx / (ktiled[1] / ktiled[0] * 1e-3) / PEAK_BF16_FLOPS,
-            "workspace_bytes": int(fws.numel()),
-            "unfused_workspace_bytes": int(M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, s)),
-            "same_selection_as_unfused": same}
-        log(f"fused index top-k {ms_f:.3f} ms (unfused {ms_idx + ms_topk:.3f} ms), workspace "
-            f"{fws.numel() / 2**20:.0f} MiB against {result['index_topk_fused']['unfused_workspace_bytes'] / 2**20:.0f}"
-            f" MiB, same selection: {same}")
-        del fblk, fws
-
     if not args.no_target and s.block == 128:
         # Index-branch training target (forward only): msa_sparse_prefill plus
-        # block_target_kl on the same inputs; block_target_kl's own time from
+        # block_target_kl on the same inputs (its pooled scores are the ones
+        # the separate-calls leg above wrote); block_target_kl's own time from
         # the library's event pairs.
         target = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.float32, device=dev)
         kl = torch.empty((s.batch, s.n_q, s.h_kv), dtype=torch.float32, device=dev)

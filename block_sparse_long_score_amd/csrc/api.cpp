@@ -75,9 +75,12 @@ Dims blocks128(const Dims& d) {
   return c;
 }
 
-// Pooled scores at offset 0 (the documented layout), for 256-token blocks
-// followed by the 128-token pooled scores they come from.
+// Prefill-shaped calls with 128-token blocks and k <= 16 take the fused
+// path (survivor lists, or nothing with one workgroup per row tile); the
+// others keep the pooled scores at offset 0, for 256-token blocks followed by
+// the 128-token pooled scores they come from.
 size_t index_ws_bytes(const Dims& d) {
+  if (msa::index_topk_fused_applies(d)) return msa::index_topk_fused_ws_bytes(d);
   const size_t own = msa::align_up(nrows(d) * d.nblk() * sizeof(float), 256);
   if (d.block == 128) return own;
   return own + msa::align_up(nrows(d) * index128(d).nblk() * sizeof(float), 256);
@@ -91,6 +94,7 @@ size_t decode_ws_bytes(const Dims& d) { return sel_bytes(d) + msa::sparse_decode
 
 hipError_t run_index_topk(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, int32_t* blk, void* ws,
                           hipStream_t s) {
+  if (msa::index_topk_fused_applies(d)) return msa::launch_index_topk_fused(d, q_idx, k_idx, blk, ws, s);
   float* bscore = static_cast<float*>(ws);
   hipError_t e;
   if (d.block == 128) {
@@ -137,13 +141,22 @@ msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_
 
 float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
 
-// Workspace of msa_prefill_chunked: pooled scores and the sparse-prefill
-// workspace of one chunk (one sequence, `chunk` queries).
+// Workspace of msa_prefill_chunked: the index workspace of the most
+// demanding chunk (its size follows each chunk's length and position on the
+// fused path) and the sparse-prefill workspace of a full chunk (one
+// sequence, `chunk` queries).
 size_t chunked_ws_bytes(const Dims& d, int chunk, size_t* prefill_off) {
   Dims c = d;
   c.batch = 1;
+  size_t idx = 0;
+  for (int t0 = 0; t0 < std::max(d.n_q, 1); t0 += chunk) {
+    c.n_q = std::min(chunk, std::max(d.n_q, 1) - t0);
+    c.pos0 = d.pos0 + t0;
+    idx = std::max(idx, index_ws_bytes(c));
+  }
+  idx = msa::align_up(idx, 256);
   c.n_q = chunk;
-  const size_t idx = index_ws_bytes(c);
+  c.pos0 = d.pos0;
   if (prefill_off) *prefill_off = idx;
   return idx + prefill_ws_bytes(c);
 }
@@ -189,8 +202,9 @@ msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uin
   if (!q_idx || !k_idx || !blk_idx) return MSA_ERR_NULL;
   if (misaligned(q_idx) || misaligned(k_idx) || misaligned(blk_idx)) return MSA_ERR_ALIGN;
   const Dims d = to_dims(*dims);
-  if (!workspace || workspace_bytes < index_ws_bytes(d)) return MSA_ERR_WORKSPACE;
-  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  const size_t need = index_ws_bytes(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MSA_ERR_WORKSPACE;
+  if (workspace && misaligned(workspace)) return MSA_ERR_ALIGN;
   return hip_status(run_index_topk(d, q_idx, k_idx, blk_idx, workspace, static_cast<hipStream_t>(stream)));
 }
 
@@ -217,8 +231,9 @@ msa_status msa_index_topk_fused(const msa_dims* dims, const uint16_t* q_idx, con
   if (!msa::index_topk_fused_applies(d)) return MSA_ERR_UNSUPPORTED;
   if (!q_idx || !k_idx || !blk_idx) return MSA_ERR_NULL;
   if (misaligned(q_idx) || misaligned(k_idx) || misaligned(blk_idx)) return MSA_ERR_ALIGN;
-  if (!workspace || workspace_bytes < msa::index_topk_fused_ws_bytes(d)) return MSA_ERR_WORKSPACE;
-  if (misaligned(workspace)) return MSA_ERR_ALIGN;
+  const size_t need = msa::index_topk_fused_ws_bytes(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MSA_ERR_WORKSPACE;
+  if (workspace && misaligned(workspace)) return MSA_ERR_ALIGN;
   return hip_status(msa::launch_index_topk_fused(d, q_idx, k_idx, blk_idx, workspace,
                                                  static_cast<hipStream_t>(stream)));
 }

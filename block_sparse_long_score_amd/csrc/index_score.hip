@@ -19,6 +19,7 @@
 //     index-key streaming: every wave pulls its key blocks straight from HBM into
 //     MFMA A operands (no LDS round trip), bound by HBM bandwidth.
 #include <algorithm>
+#include <climits>
 #include <atomic>
 #include <cmath>
 
@@ -276,8 +277,8 @@ template <int DI>
 struct IndexTopkSmem {
   static constexpr int S = DI + 8;
   uint16_t k[2][kBlock * S];                             // double-buffered key block
-  float cs[kTiledRows * kFusedKk];                       // kept scores, [row][entry]
-  uint16_t cj[kTiledRows * kFusedKk];                    // their blocks
+  uint32_t cs[kTiledRows * kFusedKk];                    // kept scores as order keys, [row][entry]
+  uint16_t cj[kTiledRows * kFusedKk];                    // 0xffff - their blocks
 };
 
 // Piece k of a row tile's pair swept (and wrote survivor lists for) the tile
@@ -306,9 +307,9 @@ __device__ __forceinline__ TilePieces tile_pieces(int tile, int tiles, int64_t n
 template <int DI>
 __device__ __forceinline__ void tiled_segment_topk(IndexTopkSmem<DI>& sm, const uint16_t* __restrict__ q_idx,
                                                    const uint16_t* __restrict__ k_idx, float* __restrict__ cand_s,
-                                                   int* __restrict__ cand_j, int b, int tile, int jb, int je,
-                                                   int n_kv, int pos0, int h_kv, int64_t nrows, int pieces,
-                                                   int piece, int kk) {
+                                                   int* __restrict__ cand_j, int32_t* __restrict__ blk, int b,
+                                                   int tile, int jb, int je, int n_kv, int pos0, int h_kv,
+                                                   int64_t nrows, int pieces, int piece, int kk) {
   constexpr int KC = DI / 16;
   constexpr int NT = kTiledWaves * 64;
   using Smem = IndexTopkSmem<DI>;
@@ -341,11 +342,20 @@ __device__ __forceinline__ void tiled_segment_topk(IndexTopkSmem<DI>& sm, const 
   // count | entry << 8) and that score.  A row's candidates are its blocks
   // j < jl = plim / 128 (none for a row past the tile, plim = -1).
   int meta[2] = {0, 0};
-  float worst[2] = {-INFINITY, -INFINITY};
-  auto row_jl = [&](int u) {
-    const int pl = half ? plim[2 + u] : plim[u];
-    return pl >= 0 ? pl / kBlock : -1;
-  };
+  uint32_t worst[2] = {0u, 0u};                        // order key of the worst kept score
+  // Selected by value (not by an index into plim) so that no private array
+  // is indexed by the lane's half.
+  const int pl0 = half ? plim[2] : plim[0], pl1 = half ? plim[3] : plim[1];
+  const int jlr[2] = {pl0 >= 0 ? pl0 / kBlock : -1, pl1 >= 0 ? pl1 / kBlock : -1};
+  auto row_jl = [&](int u) { return jlr[u]; };
+  // Empty slots hold the largest key, so the scan for the worst entry never
+  // picks a slot past k-1.
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    uint32_t* rs = sm.cs + (wave * kTiledColsPerWave + r32 + (2 * half + u) * 32) * kFusedKk;
+#pragma unroll
+    for (int e = 0; e < kFusedKk; ++e) rs[e] = 0xffffffffu;
+  }
   const int lrow0 = wave * kTiledColsPerWave + r32;      // + ct * 32: this lane's rows in the workgroup
 
   constexpr int CHUNKS = kBlock * DI / 8;
@@ -382,36 +392,41 @@ __device__ __forceinline__ void tiled_segment_topk(IndexTopkSmem<DI>& sm, const 
         score_block<DI, true>(sm.k[cur], qb, j * kBlock, plim, rm);
       else
         score_block<DI, false>(sm.k[cur], qb, j * kBlock, plim, rm);
-      float m4[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) m4[ct] = vmax(rm[ct], shfl_xor_f(rm[ct], 32)) + 0.0f;   // + 0: -0 -> +0
-      const float mrow[2] = {half ? m4[2] : m4[0], half ? m4[3] : m4[1]};   // the two rows this lane keeps
+      // The two rows this lane keeps, as values (+ 0 turns -0 into +0).
+      const float m0 = vmax(rm[0], shfl_xor_f(rm[0], 32)) + 0.0f, m1 = vmax(rm[1], shfl_xor_f(rm[1], 32)) + 0.0f;
+      const float m2 = vmax(rm[2], shfl_xor_f(rm[2], 32)) + 0.0f, m3 = vmax(rm[3], shfl_xor_f(rm[3], 32)) + 0.0f;
+      const float mrow[2] = {half ? m2 : m0, half ? m3 : m1};
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int cnt = meta[u] & 0xff;
-        const bool take = j < row_jl(u) && (cnt < kk || mrow[u] > worst[u]);
+        const uint32_t mk = order_key(mrow[u]);
+        const bool take = j < row_jl(u) && (cnt < kk || mk > worst[u]);
         if (take) {                                      // rare once a row has k-1 entries
-          float* rs = sm.cs + (lrow0 + (2 * half + u) * 32) * kFusedKk;
+          uint32_t* rs = sm.cs + (lrow0 + (2 * half + u) * 32) * kFusedKk;
           uint16_t* rj = sm.cj + (lrow0 + (2 * half + u) * 32) * kFusedKk;
           const int at = cnt < kk ? cnt : meta[u] >> 8;
-          rs[at] = mrow[u];
-          rj[at] = (uint16_t)j;
+          rs[at] = mk;
+          rj[at] = (uint16_t)(0xffff - j);
           const int nc = min(cnt + 1, kk);
           meta[u] = nc;
-          if (nc == kk) {                                // the worst kept entry: lowest score, then highest block
-            float ws = INFINITY;
-            int wj = -1, wp = 0;
-            for (int e = 0; e < kk; ++e) {
-              const float sc = rs[e];
-              const int bj = rj[e];
-              if (sc < ws || (sc == ws && bj > wj)) {
-                ws = sc;
-                wj = bj;
-                wp = e;
-              }
+          if (nc == kk) {
+            // The worst kept entry (lowest score, then highest block) is the
+            // smallest of the 64-bit keys (score key, 0xffff - block, slot);
+            // all 15 slots are read at once.
+            uint32_t ks[kFusedKk], ib[kFusedKk];
+#pragma unroll
+            for (int e = 0; e < kFusedKk; ++e) {
+              ks[e] = rs[e];
+              ib[e] = rj[e];
             }
-            worst[u] = ws;
-            meta[u] = nc | (wp << 8);
+            uint64_t best = ~0ull;
+#pragma unroll
+            for (int e = 0; e < kFusedKk; ++e) {
+              const uint64_t key = ((uint64_t)ks[e] << 32) | ((ib[e] << 4) | (uint32_t)e);
+              best = key < best ? key : best;
+            }
+            worst[u] = (uint32_t)(best >> 32);
+            meta[u] = nc | ((int)(best & 15u) << 8);
           }
         }
       }
@@ -420,23 +435,45 @@ __device__ __forceinline__ void tiled_segment_topk(IndexTopkSmem<DI>& sm, const 
     __syncthreads();
   }
   // Each kept list goes out in block order: entry e's place is the number of
-  // kept blocks below its own (blocks are distinct).
+  // kept blocks below its own (blocks are distinct).  With one piece per tile
+  // the segment has offered every candidate block j < jl of its rows, so the
+  // list is the row's selection: it goes straight to blk_idx, followed by the
+  // local block and -1 padding (a row with jl <= k-1 keeps all of 0 .. jl-1).
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    if (row_jl(u) < 0) continue;
+    const int jl = row_jl(u);
+    if (jl < 0) continue;
     const int cnt = meta[u] & 0xff;
     const int64_t r = rw0 + (2 * half + u) * 32 + r32;
     const int64_t at = (((int64_t)b * nrows + r) * pieces + piece) * kCandStride;
-    const float* rs = sm.cs + (lrow0 + (2 * half + u) * 32) * kFusedKk;
+    const int topk = kk + 1;
+    int32_t* out = blk + ((int64_t)b * nrows + r) * topk;
+    const uint32_t* rs = sm.cs + (lrow0 + (2 * half + u) * 32) * kFusedKk;
     const uint16_t* rj = sm.cj + (lrow0 + (2 * half + u) * 32) * kFusedKk;
-    for (int e = 0; e < cnt; ++e) {
-      const int bj = rj[e];
-      int rank = 0;
-      for (int f = 0; f < cnt; ++f) rank += rj[f] < bj ? 1 : 0;
-      cand_s[at + rank] = rs[e];
-      cand_j[at + rank] = bj;
+    int bjs[kFusedKk];
+#pragma unroll
+    for (int e = 0; e < kFusedKk; ++e) bjs[e] = e < cnt ? 0xffff - (int)rj[e] : INT_MAX;
+#pragma unroll
+    for (int e = 0; e < kFusedKk; ++e) {
+      if (e < cnt) {
+        int rank = 0;
+#pragma unroll
+        for (int f = 0; f < kFusedKk; ++f) rank += bjs[f] < bjs[e] ? 1 : 0;
+        if (pieces == 1) {
+          out[rank] = bjs[e];
+        } else {
+          const uint32_t k = rs[e];                      // back from the order key to the score
+          cand_s[at + rank] = __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+          cand_j[at + rank] = bjs[e];
+        }
+      }
     }
-    cand_j[at + kCandStride - 1] = cnt;
+    if (pieces == 1) {
+      out[cnt] = jl;
+      for (int i = cnt + 1; i < topk; ++i) out[i] = -1;
+    } else {
+      cand_j[at + kCandStride - 1] = cnt;
+    }
   }
   __syncthreads();                                       // the lists are reused by the next segment
 }
@@ -447,7 +484,8 @@ __device__ __forceinline__ void tiled_segment_topk(IndexTopkSmem<DI>& sm, const 
 template <int DI>
 __global__ __launch_bounds__(kTiledWaves * 64) void index_topk_tiled(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, float* __restrict__ cand_s,
-    int* __restrict__ cand_j, int n_q, int n_kv, int pos0, int h_kv, int tiles, int pairs, int pieces, int kk) {
+    int* __restrict__ cand_j, int32_t* __restrict__ blk, int n_q, int n_kv, int pos0, int h_kv, int tiles, int pairs,
+    int pieces, int kk) {
   __shared__ IndexTopkSmem<DI> sm;
   const int64_t nrows = (int64_t)n_q * h_kv;
   const int w = blockIdx.x;
@@ -465,8 +503,8 @@ __global__ __launch_bounds__(kTiledWaves * 64) void index_topk_tiled(
     const int jb = __builtin_amdgcn_readfirstlane(seg == 0 ? lo : max(lo, na) - na);
     const int je = __builtin_amdgcn_readfirstlane(seg == 0 ? min(hi, na) : hi - na);
     if (jb < je)
-      tiled_segment_topk<DI>(sm, q_idx, k_idx, cand_s, cand_j, b, tile, jb, je, n_kv, pos0, h_kv, nrows, pieces, k,
-                             kk);
+      tiled_segment_topk<DI>(sm, q_idx, k_idx, cand_s, cand_j, blk, b, tile, jb, je, n_kv, pos0, h_kv, nrows, pieces,
+                             k, kk);
   }
 }
 
@@ -474,11 +512,14 @@ __global__ __launch_bounds__(kTiledWaves * 64) void index_topk_tiled(
 // tile (in piece order, each list in block order: position order is block
 // order, so ties still go to the lower block), then the local block; one wave
 // per row, rows ascending.
+// V = slots per lane for the survivors: pieces * 15 <= 64 V.  A row whose
+// survivors number exactly k-1 (one piece held all its candidates) takes them
+// all, already in block order.
 constexpr int kMergeRowsPerWg = 4;
+template <int V>
 __global__ __launch_bounds__(kMergeRowsPerWg * 64) void topk_merge_pieces(
     const float* __restrict__ cand_s, const int* __restrict__ cand_j, int32_t* __restrict__ blk, int64_t nrows_all,
     int n_q, int pos0, int h_kv, int topk, int tiles, int pieces) {
-  constexpr int V = kFusedPiecesMax * kFusedKk / 64 + 1;   // 240 survivors at most
   __shared__ uint32_t ck[kMergeRowsPerWg][64];
   __shared__ int32_t ci[kMergeRowsPerWg][64];
   __shared__ uint32_t gk[kMergeRowsPerWg][V * 64];
@@ -513,6 +554,10 @@ __global__ __launch_bounds__(kMergeRowsPerWg * 64) void topk_merge_pieces(
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (total == kk) {
+    if (lane < kk) out[lane] = gj[wave][lane];
+    return;
+  }
   uint32_t key[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -655,23 +700,33 @@ hipError_t launch_index_topk_fused_t(const Dims& d, const uint16_t* q_idx, const
   const int64_t tiles = (nrows + kTiledRows - 1) / kTiledRows;
   const int64_t pairs = (tiles + 1) / 2;
   const int pieces = fused_pieces(d);
-  const size_t n = (size_t)d.batch * nrows * pieces * kCandStride;
-  float* cand_s = static_cast<float*>(ws);
-  int* cand_j = reinterpret_cast<int*>(static_cast<char*>(ws) + align_up(n * sizeof(float), 256));
+  // One piece per tile writes blk_idx directly and needs no workspace.
+  const size_t n = pieces > 1 ? (size_t)d.batch * nrows * pieces * kCandStride : 0;
+  float* cand_s = pieces > 1 ? static_cast<float*>(ws) : nullptr;
+  int* cand_j = pieces > 1 ? reinterpret_cast<int*>(static_cast<char*>(ws) + align_up(n * sizeof(float), 256))
+                           : nullptr;
   {
     LaunchTimer timer("index_topk_tiled", stream);
     hipLaunchKernelGGL(index_topk_tiled<DI>, dim3((unsigned)(d.batch * pairs * pieces)), dim3(kTiledWaves * 64), 0,
-                       stream, q_idx, k_idx, cand_s, cand_j, d.n_q, d.n_kv, d.pos0, d.h_kv, (int)tiles, (int)pairs,
-                       pieces, d.topk - 1);
+                       stream, q_idx, k_idx, cand_s, cand_j, blk, d.n_q, d.n_kv, d.pos0, d.h_kv, (int)tiles,
+                       (int)pairs, pieces, d.topk - 1);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || pieces == 1) return e;
   const int64_t rows_all = (int64_t)d.batch * nrows;
   {
     LaunchTimer timer("topk_merge_pieces", stream);
-    hipLaunchKernelGGL(topk_merge_pieces, dim3((unsigned)((rows_all + kMergeRowsPerWg - 1) / kMergeRowsPerWg)),
-                       dim3(kMergeRowsPerWg * 64), 0, stream, cand_s, cand_j, blk, rows_all, d.n_q, d.pos0, d.h_kv,
-                       d.topk, (int)tiles, pieces);
+    const dim3 grid((unsigned)((rows_all + kMergeRowsPerWg - 1) / kMergeRowsPerWg)), wg(kMergeRowsPerWg * 64);
+    const int survivors = pieces * kFusedKk;
+    if (survivors <= 64)
+      hipLaunchKernelGGL(topk_merge_pieces<1>, grid, wg, 0, stream, cand_s, cand_j, blk, rows_all, d.n_q, d.pos0,
+                         d.h_kv, d.topk, (int)tiles, pieces);
+    else if (survivors <= 128)
+      hipLaunchKernelGGL(topk_merge_pieces<2>, grid, wg, 0, stream, cand_s, cand_j, blk, rows_all, d.n_q, d.pos0,
+                         d.h_kv, d.topk, (int)tiles, pieces);
+    else
+      hipLaunchKernelGGL(topk_merge_pieces<4>, grid, wg, 0, stream, cand_s, cand_j, blk, rows_all, d.n_q, d.pos0,
+                         d.h_kv, d.topk, (int)tiles, pieces);
   }
   return hipGetLastError();
 }
@@ -683,7 +738,9 @@ bool index_topk_fused_applies(const Dims& d) {
 }
 
 size_t index_topk_fused_ws_bytes(const Dims& d) {
-  const size_t n = (size_t)d.batch * d.n_q * d.h_kv * fused_pieces(d) * kCandStride;
+  const int pieces = fused_pieces(d);
+  if (pieces == 1) return 0;
+  const size_t n = (size_t)d.batch * d.n_q * d.h_kv * pieces * kCandStride;
   return align_up(n * sizeof(float), 256) + align_up(n * sizeof(int), 256);
 }
 

@@ -117,10 +117,16 @@ const char* msa_status_str(msa_status status);
  *           all blocks 0..jl when jl + 1 <= topk (then -1 padding), else jl
  *           plus the topk-1 earlier blocks with the largest pooled score, ties
  *           to the lower block index.
- *   workspace >= msa_workspace_size(MSA_OP_INDEX_TOPK).  On return it holds, at
- *           offset 0, the pooled block scores bscore[batch][n_q][h_kv][nblk]
- *           (fp32): entry j <= jl is max over tokens s of block j with s <= p of
- *           q_idx . k_idx[s]; entries j > jl are unspecified.
+ *   workspace >= msa_workspace_size(MSA_OP_INDEX_TOPK), which may be 0 (then
+ *           workspace may be NULL).  Calls with 128-token blocks, topk <= 16
+ *           and more than 16 (token, group) rows per sequence run the top-k
+ *           fused into the scoring kernel (as msa_index_topk_fused below: no
+ *           pooled scores in memory) and leave the workspace's contents
+ *           unspecified.  Every other call leaves, at offset 0, the pooled
+ *           block scores bscore[batch][n_q][h_kv][nblk] (fp32): entry j <= jl
+ *           is max over tokens s of block j with s <= p of q_idx . k_idx[s];
+ *           entries j > jl are unspecified.  msa_index_scores gives the pooled
+ *           scores of any call.
  * Scores accumulate in fp32; with integer-valued index inputs of magnitude
  * <= 3 and d_idx <= 128 they are exact. */
 msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
@@ -129,36 +135,40 @@ msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uin
 /* The index branch with the top-k fused into the scoring kernel, so that the
  * pooled block scores never reach memory (yhxrc.cn article, "第一步：索引分支":
  * scores, block max-pool and top-k as one step; lumi-systems summary: the
- * selection uses no exponential).  Same arguments and the same blk_idx as
- * msa_index_topk, bit for bit; only the workspace differs:
+ * selection uses no exponential).  msa_index_topk takes this path by itself
+ * whenever it applies; this entry point guarantees it (MSA_ERR_UNSUPPORTED
+ * otherwise).  Same arguments and the same blk_idx as msa_index_topk, bit for
+ * bit:
  *   workspace >= msa_workspace_size(MSA_OP_INDEX_TOPK_FUSED): per (token,
- *           group) row P lists of up to 15 surviving blocks (P = 1..16
- *           workgroups sweep each 1,024-row tile, chosen from the sizes
- *           alone), batch * n_q * h_kv * P * 128 bytes; its contents on return
- *           are unspecified.  At 131,072 tokens x 8 groups that is 128 MiB,
- *           against 4 GiB of pooled scores for msa_index_topk.
+ *           group) row, P lists of up to 15 surviving blocks, where P = 1..16
+ *           workgroups sweep each 1,024-row tile (chosen from the sizes alone):
+ *           batch * n_q * h_kv * P * 128 bytes, and none when P = 1 (the
+ *           workgroup then writes blk_idx itself; workspace may be NULL).  Its
+ *           contents on return are unspecified.  At 131,072 tokens x 8 groups
+ *           P = 1, against 4 GiB of pooled scores on the unfused path.
  * Each sweeping workgroup keeps every row's best k - 1 blocks so far in LDS as
  * the key blocks stream by (a later block replaces the worst kept one only
- * with a strictly larger score, so ties keep the lower block); a second kernel
- * selects each row's k - 1 best among its lists and adds the local block.
- * It trades time for memory: on MI355X it takes about 1.45x the time of
- * msa_index_topk at 128K tokens.
+ * with a strictly larger score, so ties keep the lower block); with P > 1 a
+ * second kernel selects each row's k - 1 best among its P lists and adds the
+ * local block.
  *   - MSA_ERR_UNSUPPORTED for block 256, topk > 16, or n_q * h_kv <= 16 (a
- *     decode-shaped call, whose pooled scores are small: use
- *     msa_index_topk); msa_workspace_size then returns 0. */
+ *     decode-shaped call, whose pooled scores are small); msa_workspace_size
+ *     then returns 0. */
 msa_status msa_index_topk_fused(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,
                                 int32_t* blk_idx, void* workspace, size_t workspace_bytes, msa_stream stream);
 
 /* msa_index_topk without a workspace argument, for callers that cannot
  * allocate device memory: code being captured into a HIP graph, tight serving
  * loops, harnesses that forbid allocation.  Same arguments (minus the
- * workspace), same checks and the same blk_idx, bit for bit.  The pooled
- * scores go to a scratch array of 64 MiB that the library keeps in its code
- * object: every GPU the library runs on holds its own copy from the first use
- * until the process ends.  The call itself allocates nothing.
+ * workspace), same checks and the same blk_idx, bit for bit.  What
+ * msa_index_topk keeps in its workspace (pooled scores, or survivor lists on
+ * the fused path) goes to a scratch array of 64 MiB that the library keeps in
+ * its code object: every GPU the library runs on holds its own copy from the
+ * first use until the process ends.  The call itself allocates nothing.
  *   - Returns MSA_ERR_TOO_LARGE when the call needs more than 64 MiB, i.e.
  *     msa_workspace_size(MSA_OP_INDEX_TOPK, dims) > 64 << 20 (for example
- *     batch * n_q * h_kv * nblk > 16,777,216 with 128-token blocks).
+ *     batch * n_q * h_kv * nblk > 16,777,216 pooled scores with 128-token
+ *     blocks and topk > 16).
  *   - Every call on one GPU uses that GPU's single array, which keeps the last
  *     call's contents: calls whose work overlaps on one GPU (other streams,
  *     other threads) race and give undefined results.  Calls ordered on one

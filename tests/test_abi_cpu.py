@@ -129,10 +129,19 @@ def test_empty_calls_are_noops():
     assert prefill_call(dims(batch=0), q=None, k=None, v=None, blk=None, out=None, ws=None) == OK
 
 
+def fused_path(s) -> bool:
+    """msa_index_topk runs the top-k fused into the scorer for prefill-shaped
+    calls with 128-token blocks and k <= 16."""
+    return s.block == 128 and s.topk <= 16 and s.n_q * s.h_kv > 16
+
+
 def test_workspace_sizes_cover_their_buffers():
     for name, (_, s) in WORKLOADS.items():
         n_idx = M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, s)
-        assert n_idx >= s.batch * s.n_q * s.h_kv * s.nblk * 4, name
+        if fused_path(s):
+            assert n_idx == M.msa_workspace_size(M.MSA_OP_INDEX_TOPK_FUSED, s), name
+        else:
+            assert n_idx >= s.batch * s.n_q * s.h_kv * s.nblk * 4, name
         if s.n_q == 1:
             assert M.msa_workspace_size(M.MSA_OP_SPARSE_DECODE, s) >= s.batch * s.h_kv * s.topk * s.group * (s.d * 2 + 8)
             assert M.msa_workspace_size(M.MSA_OP_DENSE_GQA, s) > 0
@@ -276,7 +285,8 @@ def test_block256_rules():
     assert lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d33)) == 0
     assert prefill_call(d33) == UNSUP
     # index workspace holds the 256-token pooled scores and the 128-token ones
-    d128 = dims(block=128, topk=16)
+    # (compared with a 128-token call off the fused path: k = 17)
+    d128 = dims(block=128, topk=17)
     w256 = lib.msa_workspace_size(M.MSA_OP_INDEX_TOPK, ctypes.byref(d))
     w128 = lib.msa_workspace_size(M.MSA_OP_INDEX_TOPK, ctypes.byref(d128))
     assert w256 >= w128 + w128 // 2
@@ -315,8 +325,8 @@ def test_noalloc_index_topk_host_checks():
     assert call(dims(h_q=6, h_kv=4)) == SHAPE
     assert call(dims(d_idx=96)) == UNSUP
     assert call(dims(batch=0)) == OK
-    # 2 * 2048 * 8 * 1024 fp32 pooled scores = 128 MiB
-    assert call(dims(batch=2, n_q=2048, n_kv=131072, pos0=129024, h_q=64, h_kv=8)) == 7
+    # 2 * 2048 * 8 * 1024 fp32 pooled scores = 128 MiB (k = 32: not the fused path)
+    assert call(dims(batch=2, n_q=2048, n_kv=131072, pos0=129024, h_q=64, h_kv=8, topk=32)) == 7
     assert M.STATUS[7] == "MSA_ERR_TOO_LARGE"
 
 
@@ -342,10 +352,14 @@ def test_fused_index_topk_host_checks():
         assert size(dims(**kw)) == 0, kw
     assert call(dims(n_q=0), q=None, k=None, blk=None, ws=None) == OK
     assert size(dims(n_q=3, pos0=4093, h_kv=8, h_q=8)) > 0                  # 24 rows: prefill-shaped
-    for name in ("prefill_32k", "prefill_128k", "prefill_chunk_1m", "tiny_prefill_4k"):
+    for name in ("prefill_32k", "prefill_chunk_1m", "tiny_prefill_4k"):
         s = WORKLOADS[name][1]
         rows = s.batch * s.n_q * s.h_kv
         n = M.msa_workspace_size(M.MSA_OP_INDEX_TOPK_FUSED, s)
-        assert rows * 128 <= n <= 16 * rows * 128 + 512, (name, n)
-    s = WORKLOADS["prefill_128k"][1]
-    assert M.msa_workspace_size(M.MSA_OP_INDEX_TOPK_FUSED, s) * 32 == M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, s)
+        assert 2 * rows * 128 <= n <= 16 * rows * 128 + 512, (name, n)
+    # one workgroup per row tile (512 tile pairs at 131,072 tokens x 8 groups,
+    # 4,096 for the whole 1M-token sequence): the selection is written directly
+    for name in ("prefill_128k", "prefill_1m_full"):
+        assert M.msa_workspace_size(M.MSA_OP_INDEX_TOPK_FUSED, WORKLOADS[name][1]) == 0, name
+    d0 = dims(batch=64, n_q=4096, n_kv=4096, pos0=0, h_q=64, h_kv=8)
+    assert size(d0) == 0 and lib.msa_workspace_size(M.MSA_OP_INDEX_TOPK, ctypes.byref(d0)) == 0

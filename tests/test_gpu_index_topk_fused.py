@@ -8,9 +8,11 @@ Every call is checked two ways: sampled rows bit for bit against the oracle
 (oracle.index_topk_row: pooled scores by brute force, repeated first-occurrence
 argmax), and every row against msa_block_topk on pooled scores from a separate
 msa_index_scores call.  Shapes cover 1 to 16 workgroups per tile (the count the
-host picks, capped at 16), several sequences, partial tiles and partial last
-blocks, d_idx 64 and 128, k = 1, 2, 4, 8 and 16, rows made entirely of ties,
-and the 131,072-token workload at full size."""
+host picks, capped at 16; with one, the workgroup writes the selection itself),
+several sequences, partial tiles and partial last blocks, d_idx 64 and 128,
+k = 1, 2, 4, 5, 8 and 16, rows made entirely of ties, and the 131,072-token
+workload at full size.  msa_index_topk takes the same path for these shapes,
+so every prefill parity test with k <= 16 exercises it as well."""
 
 import numpy as np
 import pytest
@@ -32,14 +34,16 @@ CASES = {
     "sixteen_pieces_batch3": (77, Shape(3, 4096, 70000, 65904, 16, 8, 128, 128, topk=16)),
     "eleven_pieces_small_k4": (79, Shape(1, 300, 1000, 700, 8, 8, 64, 64, topk=4)),
     "one_tile_capped_at_16": (80, Shape(1, 100, 131072, 130972, 16, 8, 128, 128, topk=16)),
+    "one_piece_direct_batch64": (81, Shape(64, 4096, 4096, 0, 64, 8, 128, 128, topk=16)),
+    "one_piece_direct_k5_d64": (82, Shape(48, 2500, 7000, 4500, 8, 8, 64, 64, topk=5)),
 }
 
 
 def pieces_of(s: Shape) -> int:
     """Workgroups per row tile, read back from the workspace size (128 bytes
-    per row and piece)."""
+    per row and piece; none with one piece, which writes blk_idx itself)."""
     rows = s.batch * s.n_q * s.h_kv
-    return M.msa_workspace_size(M.MSA_OP_INDEX_TOPK_FUSED, s) // (rows * 128)
+    return max(1, M.msa_workspace_size(M.MSA_OP_INDEX_TOPK_FUSED, s) // (rows * 128))
 
 
 def run_fused(s: Shape, q_idx, k_idx):
@@ -99,8 +103,9 @@ def test_fused_index_topk_all_ties():
 
 def test_fused_index_topk_128k():
     """The 131,072-token workload (8 groups, d_idx 128, k 16) at full size:
-    one workgroup per row tile, 128 MiB of survivor lists against 4 GiB of
-    pooled scores; every row equals msa_block_topk, sampled rows the oracle."""
+    one workgroup per row tile writes the selection itself (no workspace,
+    against 4 GiB of pooled scores unfused); every row equals msa_block_topk,
+    sampled rows the oracle."""
     cid, s = WORKLOADS["prefill_128k"]
     print(f"case prefill_128k fused: {s}, pieces {pieces_of(s)}", flush=True)
     inp = make_inputs(s, cid, device="cuda", which=("q_idx", "k_idx"))

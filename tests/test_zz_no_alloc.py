@@ -43,18 +43,16 @@ def test_noalloc_equals_index_topk_on_two_calls_the_second_smaller():
         # and the oracle on a few rows (indices are bit-exact on integer index inputs)
         if s.block == 128:
             rows = [(0, 0), (1, s.n_q // 2), (s.batch - 1, s.n_q - 1)]
-            ws = M.alloc_workspace(M.MSA_OP_INDEX_TOPK, s)
-            blk2 = torch.empty_like(ref)
-            M.msa_index_topk(s, inp["q_idx"], inp["k_idx"], blk2, ws)
-            n = s.batch * s.n_q * s.h_kv * s.nblk
-            bscore = ws[: n * 4].view(torch.float32).view(s.batch, s.n_q, s.h_kv, s.nblk)
+            bscore = torch.empty((s.batch, s.n_q, s.h_kv, s.nblk), dtype=torch.float32, device="cuda")
+            M.msa_index_scores(s, inp["q_idx"], inp["k_idx"], bscore)
+            torch.cuda.synchronize()
             kseq = {b: U.to64(inp["k_idx"][b]) for b in range(s.batch)}
             U.check_index_rows(s, U.to64(inp["q_idx"]), lambda b: kseq[b], got, bscore, rows)
 
 
 def test_noalloc_rejects_a_call_beyond_the_scratch():
-    # 2 * 2048 * 8 * 1024 pooled scores = 128 MiB > 64 MiB
-    s = Shape(2, 2048, 131072, 129024, 64, 8, 128, 128)
+    # 2 * 2048 * 8 * 1024 pooled scores = 128 MiB > 64 MiB (k = 32: off the fused path)
+    s = Shape(2, 2048, 131072, 129024, 64, 8, 128, 128, topk=32)
     q_idx = torch.zeros((s.batch, s.n_q, s.h_kv, s.d_idx), dtype=torch.bfloat16, device="cuda")
     k_idx = torch.zeros((s.batch, s.n_kv, s.d_idx), dtype=torch.bfloat16, device="cuda")
     blk = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.int32, device="cuda")

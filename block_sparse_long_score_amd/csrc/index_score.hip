@@ -257,14 +257,15 @@ __global__ __launch_bounds__(kTiledWaves * 64) void index_scores_tiled(
 // ---------------------------------------------------------------------------
 // Index scores, block max-pool and top-k fused (k <= 16), for prefill-shaped
 // calls: the pooled scores never leave the chip.  A workgroup keeps, in LDS,
-// every one of its 1,024 rows' best k-1 blocks seen so far (score and block)
-// and, per lane, the row's current worst kept score; as the key blocks stream
-// by in increasing order, a block whose pooled score beats a row's worst kept
-// score (strictly, so that among equal scores the earlier, lower block stays)
-// replaces that worst entry.  When a workgroup has swept its share of a row
-// tile's blocks it writes each row's survivors, in block order, to the
-// workspace (survivor lists [batch][row][piece][16]: 15 entries, then the
-// count); topk_merge_pieces then selects each row's k-1 best among the
+// every one of its 1,024 rows' best k-1 blocks seen so far (the score's order
+// key and 0xffff - block) and, per lane, the row's current worst kept key; as
+// the key blocks stream by in increasing order, a block whose pooled score
+// beats a row's worst kept score (strictly, so that among equal scores the
+// earlier, lower block stays) replaces that worst entry.  When one workgroup
+// sweeps a whole row tile, its lists are the selection and it writes blk_idx
+// itself.  Otherwise each workgroup writes its rows' survivors, in block
+// order, to the workspace (survivor lists [batch][row][piece][16]: 15 entries,
+// then the count), and topk_merge_pieces selects each row's k-1 best among the
 // survivors of the (at most kFusedPiecesMax) workgroups that swept its tile,
 // adds the local block and writes the row ascending (yhxrc.cn article,
 // "第一步：索引分支"; lumi-systems summary: exponential-free top-k).
@@ -339,8 +340,8 @@ __device__ __forceinline__ void tiled_segment_topk(IndexTopkSmem<DI>& sm, const 
   }
   // This lane keeps the lists of rows ct = 2 half and 2 half + 1 of its column
   // r32: per row the kept count and the entry of the worst kept score (packed
-  // count | entry << 8) and that score.  A row's candidates are its blocks
-  // j < jl = plim / 128 (none for a row past the tile, plim = -1).
+  // count | entry << 8) and that score's order key.  A row's candidates are its
+  // blocks j < jl = plim / 128 (none for a row past the tile, plim = -1).
   int meta[2] = {0, 0};
   uint32_t worst[2] = {0u, 0u};                        // order key of the worst kept score
   // Selected by value (not by an index into plim) so that no private array

@@ -397,40 +397,54 @@ __device__ __forceinline__ void tiled_segment_topk(IndexTopkSmem<DI>& sm, const 
       const float m0 = vmax(rm[0], shfl_xor_f(rm[0], 32)) + 0.0f, m1 = vmax(rm[1], shfl_xor_f(rm[1], 32)) + 0.0f;
       const float m2 = vmax(rm[2], shfl_xor_f(rm[2], 32)) + 0.0f, m3 = vmax(rm[3], shfl_xor_f(rm[3], 32)) + 0.0f;
       const float mrow[2] = {half ? m2 : m0, half ? m3 : m1};
+      // Offer the block to the lane's two rows.  A lane that takes it into
+      // one row goes through the insertion once with that row's state; only
+      // lanes that take it into both rows go through it a second time, so a
+      // wave pays two passes only when some lane needs both.
+      const uint32_t mk0 = order_key(mrow[0]), mk1 = order_key(mrow[1]);
+      const bool t0 = j < row_jl(0) && ((meta[0] & 0xff) < kk || mk0 > worst[0]);
+      const bool t1 = j < row_jl(1) && ((meta[1] & 0xff) < kk || mk1 > worst[1]);
+      // Insert key mk into the row held at LDS row `lrow` with state (m, w).
+      auto insert = [&](int lrow, uint32_t mk, int& m, uint32_t& w) {
+        uint32_t* rs = sm.cs + lrow * kFusedKk;
+        uint16_t* rj = sm.cj + lrow * kFusedKk;
+        const int cnt = m & 0xff;
+        const int at = cnt < kk ? cnt : m >> 8;
+        rs[at] = mk;
+        rj[at] = (uint16_t)(0xffff - j);
+        const int nc = min(cnt + 1, kk);
+        m = nc;
+        if (nc == kk) {
+          // The worst kept entry (lowest score, then highest block) is the
+          // smallest of the 64-bit keys (score key, 0xffff - block, slot);
+          // all 15 slots are read at once.
+          uint32_t ks[kFusedKk], ib[kFusedKk];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int cnt = meta[u] & 0xff;
-        const uint32_t mk = order_key(mrow[u]);
-        const bool take = j < row_jl(u) && (cnt < kk || mk > worst[u]);
-        if (take) {                                      // rare once a row has k-1 entries
-          uint32_t* rs = sm.cs + (lrow0 + (2 * half + u) * 32) * kFusedKk;
-          uint16_t* rj = sm.cj + (lrow0 + (2 * half + u) * 32) * kFusedKk;
-          const int at = cnt < kk ? cnt : meta[u] >> 8;
-          rs[at] = mk;
-          rj[at] = (uint16_t)(0xffff - j);
-          const int nc = min(cnt + 1, kk);
-          meta[u] = nc;
-          if (nc == kk) {
-            // The worst kept entry (lowest score, then highest block) is the
-            // smallest of the 64-bit keys (score key, 0xffff - block, slot);
-            // all 15 slots are read at once.
-            uint32_t ks[kFusedKk], ib[kFusedKk];
-#pragma unroll
-            for (int e = 0; e < kFusedKk; ++e) {
-              ks[e] = rs[e];
-              ib[e] = rj[e];
-            }
-            uint64_t best = ~0ull;
-#pragma unroll
-            for (int e = 0; e < kFusedKk; ++e) {
-              const uint64_t key = ((uint64_t)ks[e] << 32) | ((ib[e] << 4) | (uint32_t)e);
-              best = key < best ? key : best;
-            }
-            worst[u] = (uint32_t)(best >> 32);
-            meta[u] = nc | ((int)(best & 15u) << 8);
+          for (int e = 0; e < kFusedKk; ++e) {
+            ks[e] = rs[e];
+            ib[e] = rj[e];
           }
+          uint64_t best = ~0ull;
+#pragma unroll
+          for (int e = 0; e < kFusedKk; ++e) {
+            const uint64_t key = ((uint64_t)ks[e] << 32) | ((ib[e] << 4) | (uint32_t)e);
+            best = key < best ? key : best;
+          }
+          w = (uint32_t)(best >> 32);
+          m = nc | ((int)(best & 15u) << 8);
         }
+      };
+      if (t0 || t1) {
+        // Row 0 if it takes the block, else row 1 (state selected by value).
+        int m = t0 ? meta[0] : meta[1];
+        uint32_t w = t0 ? worst[0] : worst[1];
+        insert(lrow0 + (2 * half + (t0 ? 0 : 1)) * 32, t0 ? mk0 : mk1, m, w);
+        meta[0] = t0 ? m : meta[0];
+        worst[0] = t0 ? w : worst[0];
+        meta[1] = t0 ? meta[1] : m;
+        worst[1] = t0 ? worst[1] : w;
       }
+      if (t0 && t1) insert(lrow0 + (2 * half + 1) * 32, mk1, meta[1], worst[1]);
     }
     if (j + 1 < je) stash(sm.k[cur ^ 1]);
     __syncthreads();

@@ -202,6 +202,27 @@ def test_chunked_prefill_argument_checks():
     assert call(dims(n_q=0), qi=None, q=None, blk=None, ws=None) == OK
 
 
+def test_chunked_workspace_covers_every_chunk():
+    """On the fused index path a chunk's index workspace follows its length
+    and position: a full chunk swept by one workgroup per row tile needs none,
+    a short tail chunk needs survivor lists.  The chunked workspace must hold
+    the largest chunk's index workspace and one full chunk's sparse workspace."""
+    lib = M.lib()
+    for n_q, chunk, pos0, n_kv in ((65536 + 1000, 65536, 0, 70000), (8192 * 3 + 100, 8192, 5000, 40000),
+                                   (3000, 1024, 0, 3000)):
+        base = Shape(1, n_q, n_kv, pos0, 64, 8, 128, 128)
+        total = M.lib().msa_prefill_chunked_workspace_size(ctypes.byref(M.dims_of(base)), chunk)
+        idx_max = 0
+        for t0 in range(0, n_q, chunk):
+            c = base.replace(n_q=min(chunk, n_q - t0), pos0=pos0 + t0)
+            idx_max = max(idx_max, M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, c))
+        pre = M.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, base.replace(n_q=chunk))
+        assert total >= idx_max + pre, (n_q, chunk, total, idx_max, pre)
+        first = M.msa_workspace_size(M.MSA_OP_INDEX_TOPK, base.replace(n_q=chunk))
+        if n_q == 65536 + 1000:
+            assert first == 0 < idx_max, (first, idx_max)     # the tail chunk needs more than the first
+
+
 def test_target_argument_checks():
     lib = M.lib()
     d = dims()

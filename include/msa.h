@@ -185,8 +185,8 @@ msa_status msa_index_topk_noalloc(const msa_dims* dims, const uint16_t* q_idx, c
 msa_status msa_index_scores(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx, float* bscore,
                             msa_stream stream);
 
-/* The top-k step alone, on pooled scores in the layout msa_index_topk leaves in
- * its workspace (lumi-systems summary: exponential-free top-k).
+/* The top-k step alone, on pooled scores in the layout msa_index_scores writes
+ * (lumi-systems summary: exponential-free top-k).
  *   bscore  [batch][n_q][h_kv][nblk] fp32 (only entries j < jl are read)
  *   blk_idx [batch][n_q][h_kv][topk] int32 out, as for msa_index_topk. */
 msa_status msa_block_topk(const msa_dims* dims, const float* bscore, int32_t* blk_idx, msa_stream stream);
@@ -305,9 +305,10 @@ msa_status msa_sparse_decode(const msa_dims* dims, const uint16_t* q, const uint
  * article, "第一步：索引分支" and "第二步：稀疏分支").  Every query row's
  * result depends only on its own row, so the outputs equal those of
  * msa_index_topk followed by msa_sparse_prefill on the whole call, while the
- * workspace holds one chunk's pooled scores and partials: a 1,048,576-token
- * prefill, whose one-shot pooled scores alone would take 256 GiB, runs in
- * chunks of 8,192 queries (64 heads) in about 4.1 GiB.
+ * workspace holds one chunk's index workspace (the largest over the chunks)
+ * and partials: a 1,048,576-token prefill in chunks of 8,192 queries (64 heads)
+ * runs in about 2.2 GiB, where one-shot sparse-prefill partials alone would
+ * take 264 GiB.
  *   q_idx, k_idx, q, k, v, blk_idx, out, lse   as for msa_index_topk and
  *            msa_sparse_prefill (blk_idx is an output here, lse may be NULL)
  *   chunk    >= 1 query tokens per chunk (MSA_ERR_SHAPE otherwise)

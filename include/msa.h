@@ -126,7 +126,9 @@ const char* msa_status_str(msa_status status);
  *           block scores bscore[batch][n_q][h_kv][nblk] (fp32): entry j <= jl
  *           is max over tokens s of block j with s <= p of q_idx . k_idx[s];
  *           entries j > jl are unspecified.  msa_index_scores gives the pooled
- *           scores of any call.
+ *           scores of any call (a caller that needs them, as the training
+ *           calls below do, runs msa_index_scores + msa_block_topk: one
+ *           scoring pass for both).
  * Scores accumulate in fp32; with integer-valued index inputs of magnitude
  * <= 3 and d_idx <= 128 they are exact. */
 msa_status msa_index_topk(const msa_dims* dims, const uint16_t* q_idx, const uint16_t* k_idx,

@@ -202,49 +202,17 @@ struct KVTile {
   }
 };
 
-template <int D, int NT>
-__device__ __forceinline__ void stage_kv_block(KVTile<D>& t, const uint16_t* __restrict__ kbase,
-                                               const uint16_t* __restrict__ vbase, int64_t row_stride,
-                                               int s0, int n_kv, int tid) {
-  constexpr int DC = D / 8;                 // 16-byte chunks per row
-  // K: one 16-byte chunk per work item.
-  for (int w = tid; w < kBlock * DC; w += NT) {
-    const int key = w / DC, dc = w % DC;
-    const int s = s0 + key;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (s < n_kv) val = ld16(kbase + (int64_t)s * row_stride + dc * 8);
-    st16(&t.k[key * D + 8 * (dc ^ (tile_swz(key) & (DC - 1)))], val);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // V: an 8-key x 8-dim tile per work item (16 lanes read one 256-byte row),
-  // transposed in registers into 8 rows of 8 keys.
-  for (int w = tid; w < (kBlock / 8) * DC; w += NT) {
-    const int kg = w / DC, dg = w % DC;
-    u32x4 r[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = s0 + kg * 8 + i;
-      r[i] = (s < n_kv) ? ld16(vbase + (int64_t)s * row_stride + dg * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int word = e >> 1, sh = (e & 1) * 16;
-      u32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[j] = ((r[2 * j][word] >> sh) & 0xffffu) | (((r[2 * j + 1][word] >> sh) & 0xffffu) << 16);
-      const int d = dg * 8 + e;
-      st16(&t.vt[d * kBlock + 8 * (kg ^ tile_swz(d))], o);
-    }
-  }
-}
-
 // Staging of one K/V block by a 512-thread workgroup through registers, so the
 // next block's loads can be in flight while the current block is used.
 constexpr int kKvThreads = 512;
 
 // Registers of one K/V block in flight: K as 16-byte chunks, V as 4-key x
 // 8-dim tiles that are transposed into the vt rows when written to LDS.
+// V tile w covers keys 4*kq .. 4*kq + 3 and dims 8*dg .. 8*dg + 7; each group
+// of 16 consecutive threads takes 4 key quads x 4 dim groups, so its loads
+// read 64-byte runs of 4 rows and its transposed 8-byte writes (rows
+// 8*dg + e) reach 16 different 8-byte slots of the 64 banks (16 dim groups
+// of one key quad, the plain order, hit only 4).
 template <int D>
 struct KVPrefetch {
   static constexpr int DC = D / 8;
@@ -252,8 +220,15 @@ struct KVPrefetch {
   static constexpr int VQ = (kBlock / 4) * DC;                    // V tiles per block
   static constexpr int VI = (VQ + kKvThreads - 1) / kKvThreads;   // V tiles per thread
   static_assert(KI * kKvThreads == kBlock * DC, "K staging must divide evenly");
+  static_assert(DC % 4 == 0 && VQ % 16 == 0, "V tiles go in groups of 4 key quads x 4 dim groups");
   u32x4 kr[KI];
   u32x4 vr[VI][4];
+
+  __device__ __forceinline__ static void v_tile(int w, int& kq, int& dg) {
+    const int g = w >> 4, l = w & 15;
+    kq = (g / (DC / 4)) * 4 + (l >> 2);
+    dg = (g % (DC / 4)) * 4 + (l & 3);
+  }
 
   __device__ __forceinline__ void fetch(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
                                         int64_t rs, int s0, int n_kv, int tid) {
@@ -265,7 +240,9 @@ struct KVPrefetch {
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
-      const int w = tid + i * kKvThreads, kq = w / DC, dg = w % DC;
+      const int w = tid + i * kKvThreads;
+      int kq, dg;
+      v_tile(w, kq, dg);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = s0 + 4 * kq + r;
@@ -282,8 +259,10 @@ struct KVPrefetch {
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
-      const int w = tid + i * kKvThreads, kq = w / DC, dg = w % DC;
+      const int w = tid + i * kKvThreads;
       if (w >= VQ) continue;
+      int kq, dg;
+      v_tile(w, kq, dg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int word = e >> 1, sh = (e & 1) * 16, d = dg * 8 + e;

@@ -90,30 +90,41 @@ __global__ __launch_bounds__(kKvThreads, 1) void dense_prefill(const uint16_t* _
     pf.fetch(k + head0, v + head0, row_stride, 0, n_kv, tid);
     pf.stash(tile[0], tid);
     __syncthreads();
-    if (jmax >= 1) pf.fetch(k + head0, v + head0, row_stride, kBlock, n_kv, tid);
 #pragma unroll 1
     for (int j = 0; j <= jmax; ++j) {
       const KVTile<D>& tl = tile[j & 1];
-      if (j <= jw) {
+      // Block j + 1's loads are issued after the scores of block j (the
+      // kernel's register peak) and are in flight during its P*V.
+      const bool live = j <= jw;
+      float m_old[2] = {mref[0], mref[1]};
+      float bmax[2], bsum[2];
+      u32x4 pb[2][4];
+      if (live) {
         const bool need_mask = (j * kBlock + kBlock - 1) > (pos0 + twmin);
-        float m_old[2] = {mref[0], mref[1]};
-        float bmax[2], bsum[2];
-        u32x4 pb[2][4];
         block_scores_softmax<D>(tl, qb, sl2, j * kBlock, plim, need_mask, bmax, bsum, pb, mref, true);
+      }
+      if (j + 1 <= jmax) pf.fetch(k + head0, v + head0, row_stride, (j + 1) * kBlock, n_kv, tid);
+      if (live) {
+        float alpha[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const float alpha = __builtin_amdgcn_exp2f(m_old[ct] - mref[ct]);   // 0 on the first block
-          lrun[ct] = lrun[ct] * alpha + bsum[ct];
+          alpha[ct] = __builtin_amdgcn_exp2f(m_old[ct] - mref[ct]);   // 0 on the first block
+          lrun[ct] = lrun[ct] * alpha[ct] + bsum[ct];
+        }
+        // The accumulators are rescaled only when some column's running max
+        // moved: otherwise every factor is exactly 1.
+        if (ballot(m_old[0] != mref[0] || m_old[1] != mref[1])) {
 #pragma unroll
-          for (int pp = 0; pp < D / 32; ++pp)
+          for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) acc[ct][pp][h] *= alpha;
+            for (int pp = 0; pp < D / 32; ++pp)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) acc[ct][pp][h] *= alpha[ct];
         }
         block_pv<D>(tl, pb, acc);
       }
       if (j + 1 <= jmax) pf.stash(tile[(j + 1) & 1], tid);   // read last in block j - 1, before the barrier
       __syncthreads();
-      if (j + 2 <= jmax) pf.fetch(k + head0, v + head0, row_stride, (j + 2) * kBlock, n_kv, tid);
     }
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {

@@ -103,7 +103,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void dense_prefill(const uint16_t* _
         const bool need_mask = (j * kBlock + kBlock - 1) > (pos0 + twmin);
         block_scores_softmax<D>(tl, qb, sl2, j * kBlock, plim, need_mask, bmax, bsum, pb, mref, true);
       }
-      if (j + 1 <= jmax) pf.fetch(k + head0, v + head0, row_stride, (j + 1) * kBlock, n_kv, tid);
+      if (j + 1 <= jmax) {
+        if ((j + 2) * kBlock <= n_kv) pf.fetch_full(k + head0, v + head0, row_stride, (j + 1) * kBlock, tid);
+        else pf.fetch(k + head0, v + head0, row_stride, (j + 1) * kBlock, n_kv, tid);
+      }
       if (live) {
         float alpha[2];
 #pragma unroll

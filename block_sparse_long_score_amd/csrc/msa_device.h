@@ -205,6 +205,8 @@ struct KVTile {
 // Staging of one K/V block by a 512-thread workgroup through registers, so the
 // next block's loads can be in flight while the current block is used.
 constexpr int kKvThreads = 512;
+// Third word of a buffer descriptor: raw 32-bit data, no swizzle or stride.
+constexpr int kBufferWord3 = 0x00020000;
 
 // Registers of one K/V block in flight: K as 16-byte chunks, V as 4-key x
 // 8-dim tiles that are transposed into the vt rows when written to LDS.
@@ -247,6 +249,39 @@ struct KVPrefetch {
       for (int r = 0; r < 4; ++r) {
         const int s = s0 + 4 * kq + r;
         vr[i][r] = (w < VQ && s < n_kv) ? ld16(vb + (int64_t)s * rs + dg * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  // A block whose 128 keys all exist (s0 + kBlock <= n_kv): every address is
+  // a wave-uniform base plus a 32-bit per-thread offset, so the loads go
+  // through a buffer descriptor of the block (scalar base, vector offset)
+  // and cost no 64-bit vector arithmetic.
+  __device__ __forceinline__ void fetch_full(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                             int64_t rs, int s0, int tid) {
+    static_assert(kKvThreads % DC == 0, "a thread's K chunks are whole key rows apart");
+    const uint32_t rsb = (uint32_t)rs * 2u;                        // key row stride in bytes
+    const int span = (int)(rsb * (kBlock - 1) + D * 2);            // bytes from the block's first row to its end
+    const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kb + (int64_t)s0 * rs), (short)0, span, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vb + (int64_t)s0 * rs), (short)0, span, kBufferWord3);
+    const uint32_t koff = (uint32_t)(tid / DC) * rsb + (uint32_t)(tid % DC) * 16u;
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr_, koff, i * (kKvThreads / DC) * rsb, 0));
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int w = tid + i * kKvThreads;
+      int kq, dg;
+      v_tile(w, kq, dg);
+      const uint32_t voff = (uint32_t)(4 * kq) * rsb + (uint32_t)dg * 16u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (VI * kKvThreads == VQ || w < VQ)
+          vr[i][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr_, voff, r * rsb, 0));
+        else
+          vr[i][r] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   }

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void dense_prefill(const uint16_t* _
         for (int h = 0; h < 2; ++h) acc[ct][pp][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (seg == 1) __syncthreads();                     // the first tile's last block is no longer read
-    pf.fetch(k + head0, v + head0, row_stride, 0, n_kv, tid);
+    pf.fetch_buf(k + head0, v + head0, row_stride, 0, n_kv, tid);
     pf.stash(tile[0], tid);
     __syncthreads();
 #pragma unroll 1
@@ -103,10 +103,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void dense_prefill(const uint16_t* _
         const bool need_mask = (j * kBlock + kBlock - 1) > (pos0 + twmin);
         block_scores_softmax<D>(tl, qb, sl2, j * kBlock, plim, need_mask, bmax, bsum, pb, mref, true);
       }
-      if (j + 1 <= jmax) {
-        if ((j + 2) * kBlock <= n_kv) pf.fetch_full(k + head0, v + head0, row_stride, (j + 1) * kBlock, tid);
-        else pf.fetch(k + head0, v + head0, row_stride, (j + 1) * kBlock, n_kv, tid);
-      }
+      if (j + 1 <= jmax) pf.fetch_buf(k + head0, v + head0, row_stride, (j + 1) * kBlock, n_kv, tid);
       if (live) {
         float alpha[2];
 #pragma unroll

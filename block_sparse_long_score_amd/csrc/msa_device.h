@@ -253,23 +253,69 @@ struct KVPrefetch {
     }
   }
 
-  // A block whose 128 keys all exist (s0 + kBlock <= n_kv): every address is
-  // a wave-uniform base plus a 32-bit per-thread offset, so the loads go
-  // through a buffer descriptor of the block (scalar base, vector offset)
-  // and cost no 64-bit vector arithmetic.
-  __device__ __forceinline__ void fetch_full(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
-                                             int64_t rs, int s0, int tid) {
+  // Loads through buffer descriptors (scalar base, one 32-bit vector offset
+  // per thread, no 64-bit vector arithmetic).  A descriptor covers only keys
+  // below n_kv, and the hardware returns zeros for a load whose vector offset
+  // is past its range, so a partial last block and a block past the end (no
+  // key in range, no memory touched) need no branch.  The range check does
+  // not see the scalar offset, so each group of rows a thread loads with one
+  // vector offset gets a descriptor of its own, based at the group's first
+  // row.  Key rows are at least D elements apart, so a 16-byte piece of a row
+  // is either wholly inside a range or wholly past it.
+  //   rsrc(base, rs, first, stride_rows, n_kv): rows first + stride_rows * m
+  //   of the block are in range for m * stride_rows <= n_kv - 1 - first.
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t rs, int first,
+                                                                     int n_kv) {
+    const int rows = n_kv - first;                                     // keys at or after `first`
+    const int bytes = rows > 0 ? (rows - 1) * (int)rs * 2 + D * 2 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + (int64_t)first * rs), (short)0, bytes,
+                                             kBufferWord3);
+  }
+
+  __device__ __forceinline__ void fetch_k_buf(const uint16_t* __restrict__ kb, int64_t rs, int s0, int n_kv,
+                                              int tid) {
     static_assert(kKvThreads % DC == 0, "a thread's K chunks are whole key rows apart");
     const uint32_t rsb = (uint32_t)rs * 2u;                        // key row stride in bytes
-    const int span = (int)(rsb * (kBlock - 1) + D * 2);            // bytes from the block's first row to its end
-    const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kb + (int64_t)s0 * rs), (short)0, span, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(vb + (int64_t)s0 * rs), (short)0, span, kBufferWord3);
+    const uint32_t koff = (uint32_t)(tid / DC) * rsb + (uint32_t)(tid % DC) * 16u;
+    const int lim = min(n_kv, s0 + kBlock);                        // keys of this block below n_kv
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rows_rsrc(kb, rs, s0 + i * (kKvThreads / DC), lim), koff, 0, 0));
+  }
+
+  __device__ __forceinline__ void fetch_v_buf(const uint16_t* __restrict__ vb, int64_t rs, int s0, int n_kv,
+                                              int tid) {
+    const uint32_t rsb = (uint32_t)rs * 2u;
+    const int lim = min(n_kv, s0 + kBlock);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int w = tid + i * kKvThreads;
+      int kq, dg;
+      v_tile(w, kq, dg);
+      const uint32_t voff = (uint32_t)(4 * kq) * rsb + (uint32_t)dg * 16u;   // row 4 kq of the group
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        if (VI * kKvThreads == VQ || w < VQ)
+          vr[i][rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rows_rsrc(vb, rs, s0 + rr, lim), voff, 0, 0));
+        else
+          vr[i][rr] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  // A block whose 128 keys are all below n_kv: one descriptor per tensor, the
+  // row steps in the scalar offset (nothing to range-check).
+  __device__ __forceinline__ void fetch_full(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                             int64_t rs, int s0, int tid) {
+    const uint32_t rsb = (uint32_t)rs * 2u;
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kb, rs, s0, s0 + kBlock);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vb, rs, s0, s0 + kBlock);
     const uint32_t koff = (uint32_t)(tid / DC) * rsb + (uint32_t)(tid % DC) * 16u;
 #pragma unroll
     for (int i = 0; i < KI; ++i)
-      kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr_, koff, i * (kKvThreads / DC) * rsb, 0));
+      kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, i * (kKvThreads / DC) * rsb, 0));
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int w = tid + i * kKvThreads;
@@ -277,12 +323,22 @@ struct KVPrefetch {
       v_tile(w, kq, dg);
       const uint32_t voff = (uint32_t)(4 * kq) * rsb + (uint32_t)dg * 16u;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int rr = 0; rr < 4; ++rr) {
         if (VI * kKvThreads == VQ || w < VQ)
-          vr[i][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr_, voff, r * rsb, 0));
+          vr[i][rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, rr * rsb, 0));
         else
-          vr[i][r] = u32x4{0u, 0u, 0u, 0u};
+          vr[i][rr] = u32x4{0u, 0u, 0u, 0u};
       }
+    }
+  }
+
+  __device__ __forceinline__ void fetch_buf(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                            int64_t rs, int s0, int n_kv, int tid) {
+    if (s0 + kBlock <= n_kv) {
+      fetch_full(kb, vb, rs, s0, tid);
+    } else {
+      fetch_k_buf(kb, rs, s0, n_kv, tid);
+      fetch_v_buf(vb, rs, s0, n_kv, tid);
     }
   }
 

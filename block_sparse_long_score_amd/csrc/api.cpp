@@ -90,6 +90,21 @@ size_t sel_bytes(const Dims& d) {
   return d.block == 128 ? 0 : msa::align_up(nrows(d) * 2 * d.topk * sizeof(int32_t), 256);
 }
 size_t prefill_ws_bytes(const Dims& d) { return sel_bytes(d) + msa::prefill_ws_layout(blocks128(d)).total; }
+// The largest number of queries of one sequence whose sparse-prefill
+// workspace fits in `bytes` (0 if not even one query's does).
+int prefill_chunk_fitting(const Dims& d, size_t bytes) {
+  Dims c = d;
+  c.batch = 1;
+  auto fits = [&](int n) { c.n_q = n; return prefill_ws_bytes(c) <= bytes; };
+  if (!fits(1)) return 0;
+  int lo = 1, hi = std::max(d.n_q, 1);                  // fits(lo) holds
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (fits(mid)) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
 size_t decode_ws_bytes(const Dims& d) { return sel_bytes(d) + msa::sparse_decode_ws_layout(blocks128(d)).total; }
 
 hipError_t run_index_topk(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, int32_t* blk, void* ws,
@@ -268,10 +283,34 @@ msa_status msa_sparse_prefill(const msa_dims* dims, const uint16_t* q, const uin
       (lse && misaligned(lse)))
     return MSA_ERR_ALIGN;
   const Dims d = to_dims(*dims);
-  if (!workspace || workspace_bytes < prefill_ws_bytes(d)) return MSA_ERR_WORKSPACE;
+  if (!workspace) return MSA_ERR_WORKSPACE;
+  const float sc = resolve_scale(scale, d.d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (workspace_bytes >= prefill_ws_bytes(d)) {
+    if (misaligned(workspace)) return MSA_ERR_ALIGN;
+    return hip_status(run_sparse(d, false, q, k, v, blk_idx, sc, out, lse, workspace, s));
+  }
+  // A smaller workspace: each sequence's queries in the largest chunks whose
+  // workspace fits (every query's output depends only on its own selection,
+  // so the chunks are independent; each re-stages the blocks it selects).
+  const int cq = prefill_chunk_fitting(d, workspace_bytes);
+  if (cq < 1) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
-  return hip_status(run_sparse(d, false, q, k, v, blk_idx, resolve_scale(scale, d.d), out, lse, workspace,
-                               static_cast<hipStream_t>(stream)));
+  for (int b = 0; b < d.batch; ++b) {
+    for (int t0 = 0; t0 < d.n_q; t0 += cq) {
+      Dims c = d;
+      c.batch = 1;
+      c.n_q = std::min(cq, d.n_q - t0);
+      c.pos0 = d.pos0 + t0;
+      const int64_t row = (int64_t)b * d.n_q + t0;      // first (sequence, query) row of the chunk
+      const int64_t kv_off = (int64_t)b * d.n_kv * d.h_kv * d.d;
+      st = hip_status(run_sparse(c, false, q + row * d.h_q * d.d, k + kv_off, v + kv_off,
+                                 blk_idx + row * d.h_kv * d.topk, sc, out + row * d.h_q * d.d,
+                                 lse ? lse + row * d.h_q : nullptr, workspace, s));
+      if (st != MSA_OK) return st;
+    }
+  }
+  return MSA_OK;
 }
 
 msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,

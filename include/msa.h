@@ -205,7 +205,14 @@ msa_status msa_block_topk(const msa_dims* dims, const float* bscore, int32_t* bl
  *   scale   softmax scale; <= 0 means 1/sqrt(d)
  *   out [batch][n_q][h_q][d] bf16 (fp32 accumulation, round-to-nearest-even)
  *   lse [batch][n_q][h_q] fp32 natural-log normaliser of the scaled logits, or NULL
- *   workspace >= msa_workspace_size(MSA_OP_SPARSE_PREFILL). */
+ *   workspace: msa_workspace_size(MSA_OP_SPARSE_PREFILL, dims) bytes run the
+ *           call in one pass.  A smaller workspace is accepted as long as it
+ *           holds the workspace of one query of one sequence
+ *           (msa_workspace_size(MSA_OP_SPARSE_PREFILL) of dims with batch = 1,
+ *           n_q = 1): the call then takes each sequence's queries in the
+ *           largest chunks whose workspace fits, one after another on the
+ *           stream (the same outputs bit for bit; each chunk re-reads the
+ *           K/V blocks it selects).  Below that: MSA_ERR_WORKSPACE. */
 msa_status msa_sparse_prefill(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const int32_t* blk_idx, float scale, uint16_t* out, float* lse, void* workspace,
                               size_t workspace_bytes, msa_stream stream);

@@ -117,8 +117,13 @@ def test_alignment_and_workspace():
     need = M.lib().msa_workspace_size(M.MSA_OP_INDEX_TOPK, ctypes.byref(dims()))
     assert need >= 256 * 2 * 32 * 4
     assert index_call(dims(), wsb=need - 1) == WS
+    # msa_sparse_prefill takes a smaller workspace in query chunks, down to
+    # one query of one sequence
+    one = M.lib().msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(dims(batch=1, n_q=1)))
     need_p = M.lib().msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(dims()))
-    assert prefill_call(dims(), wsb=need_p - 1) == WS
+    assert 0 < one < need_p
+    assert prefill_call(dims(), wsb=one - 1) == WS
+    assert prefill_call(dims(), ws=None) == WS
     d1 = dims(n_q=1, pos0=4095)
     assert dense_call(d1, ws=None) == WS
     assert dense_call(d1, wsb=M.lib().msa_workspace_size(M.MSA_OP_DENSE_GQA, ctypes.byref(d1)) - 1) == WS

@@ -585,6 +585,25 @@ def main():
             f"(msa_index_topk {ms_it:.3f} ms), same selection: {same}")
         del ublk
 
+    if s.n_q > 1:
+        # msa_sparse_prefill with an eighth of its one-pass workspace: the call
+        # takes the queries in chunks whose workspace fits.
+        small = max(M.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, s.replace(batch=1, n_q=1)),
+                    M.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, s) // 8)
+        ws_small = torch.empty(small, dtype=torch.uint8, device=dev)
+        out2 = torch.empty_like(out)
+        lse2 = torch.empty_like(lse)
+        ms_small, _ = time_calls(torch, [
+            lambda: M.msa_sparse_prefill(s, inp["q"], inp["k"], inp["v"], blk, out2, lse2, ws_small)], 3, 1)
+        same = bool(torch.equal(out2.view(torch.int16), out.view(torch.int16)) and
+                    torch.equal(lse2.view(torch.int32), lse.view(torch.int32)))
+        result["sparse_prefill_small_workspace"] = {
+            "workspace_bytes": int(small), "one_pass_workspace_bytes": int(M.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, s)),
+            "ms": ms_small, "one_pass_ms": ms_sparse, "same_outputs": same}
+        log(f"sparse prefill with {small / 2**30:.2f} GiB of workspace: {ms_small:.3f} ms "
+            f"(one pass {ms_sparse:.3f} ms), same outputs: {same}")
+        del ws_small, out2, lse2
+
     if not args.no_topk_compare and s.block == 128:
         # torch.topk on the same candidates: entries at and past each row's
         # local block are set to -inf in a copy, so the library top-k makes

@@ -13,6 +13,10 @@
         kernel and workload, with a hash of the kernel's sources: bench.py
         reports the figure only while those sources are unchanged.
 
+    python -m block_sparse_long_score_amd.profiling counters DIR [--kernel NAME ...]
+        Markdown table of every counter in a `rocprofv3 --pmc` run: the mean
+        value per dispatch (summed over the chip) for each kernel.
+
 Host-side bookkeeping only; nothing here runs on the GPU.
 """
 
@@ -135,6 +139,23 @@ def cmd_traffic(a) -> None:
     print(json.dumps({a.kernel: {a.workload: entry}}, indent=2))
 
 
+def cmd_counters(a) -> None:
+    names = set()
+    for f in _csvs(a.dir, "*counter_collection.csv"):
+        with open(f) as fh:
+            names.update(r["Counter_Name"] for r in csv.DictReader(fh))
+    per = {n: counter_per_dispatch(a.dir, n) for n in sorted(names)}
+    kernels = sorted({k for v in per.values() for k in v})
+    if a.kernel:
+        kernels = [k for k in kernels if k in a.kernel]
+    print("| kernel | dispatches | " + " | ".join(sorted(names)) + " |")
+    print("|---|---:|" + "---:|" * len(names))
+    for k in kernels:
+        disp = max(per[n][k][1] for n in per if k in per[n])
+        vals = [f"{per[n][k][0]:.4g}" if k in per[n] else "-" for n in sorted(names)]
+        print(f"| `{k}` | {disp} | " + " | ".join(vals) + " |")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(prog="python -m block_sparse_long_score_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -149,8 +170,11 @@ def main(argv=None) -> int:
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--kernel", nargs="*")
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
     return 0
 
 

@@ -105,6 +105,24 @@ int prefill_chunk_fitting(const Dims& d, size_t bytes) {
   }
   return lo;
 }
+// Calls fn(c, row, kv_off) for each query chunk of at most cq queries of each
+// sequence of d: c is the chunk's dims (one sequence, its queries at
+// pos0 + t0 ..), row its first (sequence, query) row, kv_off the element
+// offset of its sequence's K/V.  Stops at the first error.
+template <class F>
+msa_status for_query_chunks(const Dims& d, int cq, F fn) {
+  for (int b = 0; b < d.batch; ++b) {
+    for (int t0 = 0; t0 < d.n_q; t0 += cq) {
+      Dims c = d;
+      c.batch = 1;
+      c.n_q = std::min(cq, d.n_q - t0);
+      c.pos0 = d.pos0 + t0;
+      const msa_status st = fn(c, (int64_t)b * d.n_q + t0, (int64_t)b * d.n_kv * d.h_kv * d.d);
+      if (st != MSA_OK) return st;
+    }
+  }
+  return MSA_OK;
+}
 size_t decode_ws_bytes(const Dims& d) { return sel_bytes(d) + msa::sparse_decode_ws_layout(blocks128(d)).total; }
 
 hipError_t run_index_topk(const Dims& d, const uint16_t* q_idx, const uint16_t* k_idx, int32_t* blk, void* ws,
@@ -296,21 +314,11 @@ msa_status msa_sparse_prefill(const msa_dims* dims, const uint16_t* q, const uin
   const int cq = prefill_chunk_fitting(d, workspace_bytes);
   if (cq < 1) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
-  for (int b = 0; b < d.batch; ++b) {
-    for (int t0 = 0; t0 < d.n_q; t0 += cq) {
-      Dims c = d;
-      c.batch = 1;
-      c.n_q = std::min(cq, d.n_q - t0);
-      c.pos0 = d.pos0 + t0;
-      const int64_t row = (int64_t)b * d.n_q + t0;      // first (sequence, query) row of the chunk
-      const int64_t kv_off = (int64_t)b * d.n_kv * d.h_kv * d.d;
-      st = hip_status(run_sparse(c, false, q + row * d.h_q * d.d, k + kv_off, v + kv_off,
+  return for_query_chunks(d, cq, [&](const Dims& c, int64_t row, int64_t kv_off) {
+    return hip_status(run_sparse(c, false, q + row * d.h_q * d.d, k + kv_off, v + kv_off,
                                  blk_idx + row * d.h_kv * d.topk, sc, out + row * d.h_q * d.d,
                                  lse ? lse + row * d.h_q : nullptr, workspace, s));
-      if (st != MSA_OK) return st;
-    }
-  }
-  return MSA_OK;
+  });
 }
 
 msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -326,12 +334,25 @@ msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, co
       misaligned(out) || misaligned(target) || misaligned(kl) || (lse && misaligned(lse)))
     return MSA_ERR_ALIGN;
   const Dims d = to_dims(*dims);
-  const size_t need = msa::prefill_ws_layout(d).total;
-  if (!workspace || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  if (!workspace) return MSA_ERR_WORKSPACE;
+  const float sc = resolve_scale(scale, d.d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (workspace_bytes >= prefill_ws_bytes(d)) {      // 128-token blocks: the sparse prefill's own layout
+    if (misaligned(workspace)) return MSA_ERR_ALIGN;
+    return hip_status(msa::launch_sparse_prefill_target(d, q, k, v, blk_idx, sc, bscore, idx_scale, out, lse,
+                                                        target, kl, workspace, s));
+  }
+  // A smaller workspace: query chunks, as msa_sparse_prefill (every row's
+  // target and KL depend only on its own partial results and pooled scores).
+  const int cq = prefill_chunk_fitting(d, workspace_bytes);
+  if (cq < 1) return MSA_ERR_WORKSPACE;
   if (misaligned(workspace)) return MSA_ERR_ALIGN;
-  return hip_status(msa::launch_sparse_prefill_target(d, q, k, v, blk_idx, resolve_scale(scale, d.d), bscore,
-                                                      idx_scale, out, lse, target, kl, workspace,
-                                                      static_cast<hipStream_t>(stream)));
+  return for_query_chunks(d, cq, [&](const Dims& c, int64_t row, int64_t kv_off) {
+    return hip_status(msa::launch_sparse_prefill_target(
+        c, q + row * d.h_q * d.d, k + kv_off, v + kv_off, blk_idx + row * d.h_kv * d.topk, sc,
+        bscore + row * d.h_kv * d.nblk(), idx_scale, out + row * d.h_q * d.d, lse ? lse + row * d.h_q : nullptr,
+        target + row * d.h_kv * d.topk, kl + row * d.h_kv, workspace, s));
+  });
 }
 
 msa_status msa_sparse_prefill_backward(const msa_dims* dims, const uint16_t* q, const uint16_t* k,

@@ -237,7 +237,9 @@ msa_status msa_sparse_prefill(const msa_dims* dims, const uint16_t* q, const uin
  *   idx_scale finite temperature of the index softmax (MSA_ERR_SHAPE if not
  *            finite; the pages name none).
  *   target   [batch][n_q][h_kv][topk] fp32, kl [batch][n_q][h_kv] fp32, outputs.
- * Workspace: msa_workspace_size(MSA_OP_SPARSE_PREFILL, dims). */
+ * Workspace: msa_workspace_size(MSA_OP_SPARSE_PREFILL, dims) for one pass; as for
+ * msa_sparse_prefill, anything down to one query's workspace runs the call in
+ * query chunks with the same outputs. */
 msa_status msa_sparse_prefill_target(const msa_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const int32_t* blk_idx, const float* bscore, float idx_scale, float scale,
                                      uint16_t* out, float* lse, float* target, float* kl, void* workspace,

@@ -246,8 +246,10 @@ def test_target_argument_checks():
     assert call(d, idx_scale=float("nan")) == SHAPE
     assert call(d, idx_scale=float("inf")) == SHAPE
     assert call(dims(h_q=6, h_kv=2)) == UNSUP
-    need = lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(d))
-    assert call(d, wsb=need - 1) == WS
+    # as msa_sparse_prefill: down to one query's workspace, the call runs in query chunks
+    one = lib.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, ctypes.byref(dims(batch=1, n_q=1)))
+    assert call(d, wsb=one - 1) == WS
+    assert call(d, ws=None) == WS
     assert call(dims(n_q=0), bscore=None, target=None, kl=None, ws=None) == OK
 
 

@@ -55,3 +55,35 @@ def test_small_workspace_gives_the_same_outputs(name):
         assert small < full
         o1, l1 = run(small)
         assert torch.equal(bits(o0), bits(o1)) and torch.equal(bits(l0), bits(l1)), f"{name}: chunks of {n} differ"
+
+
+@pytest.mark.parametrize("name", ["chunk_ragged_g4", "batch2_g16_d64"])
+def test_target_small_workspace_gives_the_same_outputs(name):
+    """msa_sparse_prefill_target with a smaller workspace: the same query chunks,
+    each followed by its rows' target and KL."""
+    cfg, s = CASES[name]
+    print(f"[small-ws target] {name} {s}", flush=True)
+    inp = make_inputs(s, cfg, device="cuda")
+    blk = torch.empty((s.batch, s.n_q, s.h_kv, s.topk), dtype=torch.int32, device="cuda")
+    M.msa_index_topk(s, inp["q_idx"], inp["k_idx"], blk, M.alloc_workspace(M.MSA_OP_INDEX_TOPK, s))
+    bscore = torch.empty((s.batch, s.n_q, s.h_kv, s.nblk), dtype=torch.float32, device="cuda")
+    M.msa_index_scores(s, inp["q_idx"], inp["k_idx"], bscore)
+
+    def run(ws_bytes):
+        out = torch.full((s.batch, s.n_q, s.h_q, s.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((s.batch, s.n_q, s.h_q), float("nan"), dtype=torch.float32, device="cuda")
+        target = torch.full((s.batch, s.n_q, s.h_kv, s.topk), float("nan"), dtype=torch.float32, device="cuda")
+        kl = torch.full((s.batch, s.n_q, s.h_kv), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        M.msa_sparse_prefill_target(s, inp["q"], inp["k"], inp["v"], blk, bscore, target, kl, out, lse, ws,
+                                    idx_scale=0.1)
+        torch.cuda.synchronize()
+        return out, lse, target, kl
+
+    full = M.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, s)
+    ref = run(full)
+    assert not bool(torch.isnan(ref[0]).any()) and not bool(torch.isnan(ref[3]).any())
+    for n in (1, 37):
+        got = run(M.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, s.replace(batch=1, n_q=n)))
+        for a, b, what in zip(ref, got, ("out", "lse", "target", "kl")):
+            assert torch.equal(bits(a), bits(b)), f"{name}: {what} differs with chunks of {n}"

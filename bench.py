@@ -58,6 +58,8 @@ def parse():
                     help="skip the whole 1M-token chunked prefill leg")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-topk-compare", action="store_true")
+    ap.add_argument("--no-small-workspace", action="store_true",
+                    help="skip the sparse prefill with an eighth of its workspace (query chunks)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other configurations' legs (32K prefill, the 1M prefill chunk, 256K x 64 decode)")
     ap.add_argument("--no-topk-full", action="store_true",
@@ -585,7 +587,7 @@ def main():
             f"(msa_index_topk {ms_it:.3f} ms), same selection: {same}")
         del ublk
 
-    if s.n_q > 1:
+    if s.n_q > 1 and not args.no_small_workspace:
         # msa_sparse_prefill with an eighth of its one-pass workspace: the call
         # takes the queries in chunks whose workspace fits.
         small = max(M.msa_workspace_size(M.MSA_OP_SPARSE_PREFILL, s.replace(batch=1, n_q=1)),

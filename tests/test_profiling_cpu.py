@@ -48,3 +48,25 @@ def test_profile_end_rejects_null_count():
     assert lib.msa_profile_end(None, 0, None) == 1          # MSA_ERR_NULL
     n = ctypes.c_int32(-1)
     assert lib.msa_profile_end(None, 0, ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_counters_table_lists_each_kernel_and_counter(tmp_path, capsys):
+    d = tmp_path / "run" / "host"
+    d.mkdir(parents=True)
+    rows = [
+        ("1", "void msa::(anonymous namespace)::dense_prefill<128, 3>(int)", "SQ_INSTS_MFMA", "100"),
+        ("1", "void msa::(anonymous namespace)::dense_prefill<128, 3>(int)", "SQ_INSTS_MFMA", "50"),
+        ("1", "void msa::(anonymous namespace)::dense_prefill<128, 3>(int)", "SQ_INSTS_VALU", "600"),
+        ("2", "void msa::(anonymous namespace)::dense_prefill<128, 3>(int)", "SQ_INSTS_MFMA", "250"),
+        ("2", "void msa::(anonymous namespace)::dense_prefill<128, 3>(int)", "SQ_INSTS_VALU", "800"),
+        ("3", "__amd_rocclr_copyBuffer", "SQ_INSTS_VALU", "4"),
+    ]
+    with open(d / "x_counter_collection.csv", "w") as fh:
+        fh.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for r in rows:
+            fh.write(",".join(f'"{x}"' for x in r) + "\n")
+    P.main(["counters", str(tmp_path / "run"), "--kernel", "dense_prefill"])
+    out = capsys.readouterr().out.strip().splitlines()
+    assert out[0] == "| kernel | dispatches | SQ_INSTS_MFMA | SQ_INSTS_VALU |"
+    assert len(out) == 3                                  # header, rule, one kernel (the copy is filtered out)
+    assert out[2] == "| `dense_prefill` | 2 | 200 | 700 |"
